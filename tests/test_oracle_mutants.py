@@ -1,0 +1,109 @@
+"""The pins have teeth: plant a plausible mistake in a copy of the oracle, on
+the CPU, and check that at least one pin of test_oracle_pins rejects it.
+
+Each mutant is one textual change of oracle/gsa_oracle.c, compiled with the
+same flags into a temporary library that the pins then run against.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import _util as U
+from tests import test_oracle_pins as P
+from long_context_sparse_gist_amd import inputs as gi
+
+MUTANTS = {
+    "scale_dropped": ("z[j] = tau * dot_q(", "z[j] = dot_q("),
+    "ties_to_higher_index": ("return (a->id < b->id) ? -1 : (a->id > b->id);",
+                             "return (a->id > b->id) ? -1 : (a->id < b->id);"),
+    "keys_ascending": ("if (a->s > b->s) return -1;\n        if (a->s < b->s) return 1;",
+                       "if (a->s < b->s) return -1;\n        if (a->s > b->s) return 1;"),
+    "gist_slot_off_by_one": (" rows[m] = slot_base(&sv, (long)m * (C + 1) + C);\n        ids[m] = m;",
+                             " rows[m] = slot_base(&sv, (long)m * (C + 1) + C - 1);\n        ids[m] = m;"),
+    "head_to_group_transposed": ("dot_q(c, q, b, g * G + j, kv, kb)",
+                                 "dot_q(c, q, b, j * c->num_kv_heads + g, kv, kb)"),
+    "raw_tail_dropped": ("for (int r = 0; r < tail; r++) { T[nT].arr_k = kc; T[nT].arr_v = vc; "
+                         "T[nT].row = slot_base(&sv, (long)n * (C + 1) + r); nT++; }\n    /* O4 */",
+                         "for (int r = 0; r < 0; r++) { T[nT].arr_k = kc; T[nT].arr_v = vc; "
+                         "T[nT].row = slot_base(&sv, (long)n * (C + 1) + r); nT++; }\n    /* O4 */"),
+    "first_raw_token_dropped": (
+        "long s0 = (long)m * (C + 1);\n        if (is_sel[m])\n            for (int r = 0; r < C; r++)"
+        " { T[nT].arr_k = kc; T[nT].arr_v = vc; T[nT].row = slot_base(&sv, s0 + r); nT++; }\n"
+        "        if (is_sel[m] || all_gists)",
+        "long s0 = (long)m * (C + 1);\n        if (is_sel[m])\n            for (int r = 1; r < C; r++)"
+        " { T[nT].arr_k = kc; T[nT].arr_v = vc; T[nT].row = slot_base(&sv, s0 + r); nT++; }\n"
+        "        if (is_sel[m] || all_gists)"),
+    "v_read_from_k": ("o[i] += p * ld(T[t].arr_v, T[t].row + i, c->dtype);",
+                      "o[i] += p * ld(T[t].arr_k, T[t].row + i, c->dtype);"),
+    "softmax_not_normalised": ("for (int i = 0; i < d; i++) o[i] /= lam;",
+                               "for (int i = 0; i < d; i++) o[i] /= 1.0;"),
+    "page_layout_heads_outer": (
+        "return (((size_t)phys * c->num_kv_heads + sv->g) * spp + off) * c->head_dim;",
+        "return (((size_t)sv->g * c->num_pages + phys) * spp + off) * c->head_dim;"),
+    "bf16_widened_wrong": ("(uint32_t)((const uint16_t *)p)[i] << 16;",
+                           "(uint32_t)((const uint16_t *)p)[i] << 15;"),
+    "candidates_wrong_group": ("cids[nc++] = sel1[i] * R + j;", "cids[nc++] = sel1[i] + j * nm;"),
+    "tail_gists_not_candidates": ("for (int m = nm * R; m < n; m++) cids[nc++] = m;",
+                                  "for (int m = nm * R; m < nm * R; m++) cids[nc++] = m;"),
+    "meta_gists_not_attended": ("for (int r = 0; r < nm; r++) { T[nT].arr_k = km;",
+                                "for (int r = 0; r < 0; r++) { T[nT].arr_k = km;"),
+}
+
+
+def pin_battery():
+    """Every pin, as (name, thunk)."""
+    out = []
+    for wl in (P.SMALL_BF16, P.SMALL_F32, P.SMALL_D128):
+        for lens in ("full", "ragged"):
+            out.append((f"keys_topk/{wl.name}/{lens}",
+                        lambda wl=wl, lens=lens: P.test_keys_and_topk_match_brute_force(wl, lens)))
+        out.append((f"pa/{wl.name}", lambda wl=wl: P.test_pa_all_chunks_is_dense_attention(wl)))
+        for fl in (0, oracle.SET_SELECTED_GISTS):
+            out.append((f"pc/{wl.name}/{fl}",
+                        lambda wl=wl, fl=fl: P.test_pc_masked_dense_invariant(wl, fl)))
+    out += [("pb", P.test_pb_planted_selection_tiny_f32), ("pd", P.test_pd_k0_gists_only),
+            ("pe", P.test_pe_ties_go_to_lower_index), ("pf", P.test_pf_page_permutation_and_sharing),
+            ("pg", P.test_pg_group_collapse), ("ph", P.test_ph_hierarchy_reduces_to_flat_topk),
+            ("pa_h", P.test_pa_hierarchy_all_kept_is_dense_over_meta_and_sequence),
+            ("h_full", lambda: P.test_hgsa_matches_brute_force("full")),
+            ("h_ragged", lambda: P.test_hgsa_matches_brute_force("ragged")),
+            ("sum_probs", P.test_sum_of_probs_keys)]
+    for wl in (P.SMALL_BF16, P.SMALL_F32):
+        out.append((f"pi/{wl.name}", lambda wl=wl: P.test_pi_convex_hull(wl)))
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    find, repl = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(find) == 1, f"mutation site of {name} not unique"
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(find, repl))
+    lib = oracle.load(oracle.compile_source(path, os.path.join(tmp_path, "libmutant.so")))
+    caught = []
+    saved = U.ORACLE_LIB
+    U.ORACLE_LIB = lib
+    try:
+        for pin, fn in pin_battery():
+            try:
+                fn()
+            except (AssertionError, ValueError):
+                caught.append(pin)
+                break
+    finally:
+        U.ORACLE_LIB = saved
+    assert caught, f"no pin catches the mutant {name}"
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    lib = oracle.load(oracle.compile_source(oracle._SRC, os.path.join(tmp_path, "libcopy.so")))
+    saved = U.ORACLE_LIB
+    U.ORACLE_LIB = lib
+    try:
+        for _, fn in pin_battery():
+            fn()
+    finally:
+        U.ORACLE_LIB = saved

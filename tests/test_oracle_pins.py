@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the pin it implements:
+  P-a  closed form: k = every chunk turns the set into the whole interleaved
+       sequence, so the output is dense softmax attention (numpy fp64).
+  P-b  the hand-computable planted selection of the tiny fp32 workload.
+  P-c  invariant: output == fp64 dense attention with the tokens outside the
+       set masked out (default set, selected-gists set, ragged lengths).
+  P-d  special case k = 0: attention over the gists (and raw tail) only.
+  P-e  ties go to the lower chunk index.
+  P-f  page order and page sharing do not change any result (bitwise).
+  P-g  group collapse: the group key is the key of the summed query; G equal
+       heads give G times the single-head key.
+  P-h  hierarchy reduction: keeping every meta-group makes the two-level
+       selection equal to flat top-k (bitwise).
+  P-i  each output coordinate lies in the [min, max] of V over the set.
+The routing keys (O1) and the top-k (O2) are also checked against numpy
+brute force on random inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_gist_amd import inputs as gi
+from tests import _util as U
+
+import oracle
+
+SMALL_BF16 = gi.Workload("small-bf16", gi.BF16, 2, 8, 2, 64, 8, 40, 6, 4,
+                         plant="align", plant_count=3)
+SMALL_F32 = gi.Workload("small-f32", gi.F32, 2, 6, 2, 64, 4, 50, 7, 8,
+                        plant="align", plant_count=2)
+SMALL_D128 = gi.Workload("small-d128", gi.BF16, 1, 7, 1, 128, 16, 24, 5, 3)
+SMALL_H = gi.Workload("small-hgsa", gi.BF16, 2, 4, 2, 64, 4, 64, 6, 8,
+                      plant="align_meta", plant_count=2, gists_per_meta=4, top_k_meta=3)
+
+
+def ragged(wl, rng_seed=0):
+    rng = np.random.default_rng(rng_seed)
+    M, C = wl.num_chunks, wl.chunk_size
+    return [int(x) for x in rng.integers(C, M * C + C - 1, size=wl.batch)]
+
+
+@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32, SMALL_D128], ids=lambda w: w.name)
+@pytest.mark.parametrize("lens", ["full", "ragged"])
+def test_keys_and_topk_match_brute_force(wl, lens):
+    inp = gi.make_inputs(wl, 7, seq_lens=None if lens == "full" else ragged(wl))
+    out, sel, sc = U.run_oracle(inp)
+    keys = U.np_keys(inp)
+    n, _ = U.shapes(inp)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            S = keys[b][g]
+            assert np.allclose(sc[b, g, :n[b]], S, rtol=2e-6, atol=2e-6)
+            assert np.all(np.isneginf(sc[b, g, n[b]:]))
+            # O2 on the oracle's own float keys
+            want = U.np_topk(sc[b, g, :n[b]], wl.top_k)
+            got = sel[b, g][sel[b, g] >= 0]
+            assert np.array_equal(got, want)
+            assert np.all(sel[b, g, len(want):] == -1)
+
+
+@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32, SMALL_D128], ids=lambda w: w.name)
+def test_pa_all_chunks_is_dense_attention(wl):
+    inp = gi.make_inputs(wl, 11, seq_lens=ragged(wl, 3))
+    out, sel, _ = U.run_oracle(inp, top_k=wl.num_chunks)
+    q = U.f64(inp.q)
+    K, V = U.logical(inp, "k"), U.logical(inp, "v")
+    n, tail = U.shapes(inp)
+    tau = U.tau_of(wl.head_dim)
+    G = wl.group
+    for b in range(wl.batch):
+        L = n[b] * (wl.chunk_size + 1) + tail[b]
+        for h in range(wl.num_q_heads):
+            g = h // G
+            ref = U.np_attend(q[b, h], K[b, g, :L], V[b, g, :L], tau)
+            assert np.allclose(out[b, h], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_pb_planted_selection_tiny_f32():
+    wl = gi.TINY_F32
+    inp = gi.make_inputs(wl, gi.seed_of(0))
+    out, sel, sc = U.run_oracle(inp)
+    planted = set(inp.planted[0, 0].tolist())
+    assert len(planted) == 4
+    chosen = set(sel[0, 0].tolist())
+    assert planted <= chosen
+    # planted keys ~ 2*||q|| = 16, far above the unplanted N(0, ~1) maximum
+    q = U.f64(inp.q)[0, 0]
+    for m in planted:
+        assert abs(sc[0, 0, m] - 2 * np.linalg.norm(q)) < 1.0
+    # the other 4 are the largest unplanted keys, by brute force
+    S = U.np_keys(inp)[0][0].astype(np.float64)
+    rest = [m for m in np.argsort(-S, kind="stable") if m not in planted][:4]
+    assert chosen - planted == set(int(m) for m in rest)
+
+
+@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32, SMALL_D128], ids=lambda w: w.name)
+@pytest.mark.parametrize("flags", [0, oracle.SET_SELECTED_GISTS])
+def test_pc_masked_dense_invariant(wl, flags):
+    inp = gi.make_inputs(wl, 21, seq_lens=ragged(wl, 5))
+    out, sel, _ = U.run_oracle(inp, flags=flags)
+    ref = U.np_gsa_out(inp, sel, all_gists=not flags)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_pd_k0_gists_only():
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 4, seq_lens=ragged(wl, 9))
+    out, sel, _ = U.run_oracle(inp, top_k=0)
+    assert sel.shape[2] == 0
+    empty = [[[] for _ in range(wl.num_kv_heads)] for _ in range(wl.batch)]
+    ref = U.np_gsa_out(inp, empty)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+    # selected-gists set with k = 0 keeps only the raw tail; no tail -> zeros
+    inp2 = gi.make_inputs(wl, 4)
+    out2, _, _ = U.run_oracle(inp2, top_k=0, flags=oracle.SET_SELECTED_GISTS)
+    assert np.all(out2 == 0.0)
+
+
+def test_pe_ties_go_to_lower_index():
+    wl = SMALL_F32.replace(plant="none", batch=1, num_kv_heads=1, num_q_heads=3)
+    inp = gi.make_inputs(wl, 5)
+    _, _, sc = U.run_oracle(inp)
+    order = np.argsort(-sc[0, 0], kind="stable")
+    k = wl.top_k
+    # copy the gist key of the k-th ranked chunk onto a higher-index and a
+    # lower-index unselected chunk: exact ties straddling the boundary
+    src = int(order[k - 1])
+    K = inp.k_cache
+    C, spp = wl.chunk_size, wl.slots_per_page
+
+    def gist_row(m):
+        s = m * (C + 1) + C
+        return int(inp.block_table[0, s // spp]), s % spp
+
+    outside = [int(m) for m in order[k:]]
+    lower = [m for m in outside if m < src]
+    higher = [m for m in outside if m > src]
+    targets = ([lower[0]] if lower else []) + ([higher[0]] if higher else [])
+    assert targets
+    for m in targets:
+        p, o = gist_row(m)
+        ps, os_ = gist_row(src)
+        K[p, 0, o] = K[ps, 0, os_]
+    _, sel, sc2 = U.run_oracle(inp)
+    tied = sorted([src] + targets)
+    assert len({float(sc2[0, 0, m]) for m in tied}) == 1
+    chosen = set(sel[0, 0].tolist())
+    # exactly one slot is left for the tied keys: the lowest index wins
+    assert tied[0] in chosen and all(m not in chosen for m in tied[1:])
+
+
+def test_pf_page_permutation_and_sharing():
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 13, seq_lens=ragged(wl, 2), spare_pages=3)
+    base = U.run_oracle(inp)
+    # permute physical pages and remap the block table
+    perm = torch.randperm(inp.num_pages, generator=torch.Generator().manual_seed(1))
+    inv = torch.argsort(perm)
+    k2 = inp.k_cache[perm].contiguous()
+    v2 = inp.v_cache[perm].contiguous()
+    bt2 = inv[inp.block_table.long()].to(torch.int32)
+    import dataclasses
+    inp2 = dataclasses.replace(inp, k_cache=k2, v_cache=v2, block_table=bt2)
+    got = U.run_oracle(inp2)
+    for x, y in zip(base, got):
+        assert np.array_equal(x, y)
+    # sharing: sequence 1 maps sequence 0's pages with the same query
+    q3 = inp.q.clone()
+    q3[1] = q3[0]
+    sl3 = inp.seq_lens.clone()
+    sl3[1] = sl3[0]
+    inp3 = dataclasses.replace(gi.share_pages(inp, 0, 1), q=q3, seq_lens=sl3)
+    out3, sel3, sc3 = U.run_oracle(inp3)
+    assert np.array_equal(out3[0], out3[1]) and np.array_equal(sel3[0], sel3[1])
+    assert np.array_equal(out3[0], base[0][0])
+
+
+def test_pg_group_collapse():
+    wl = SMALL_F32.replace(num_q_heads=4, num_kv_heads=1, batch=1, plant="none")
+    inp = gi.make_inputs(wl, 17)
+    q = inp.q.clone()
+    q[0, 1:] = q[0, 0]                   # four identical heads
+    import dataclasses
+    inp4 = dataclasses.replace(inp, q=q)
+    _, _, s4 = U.run_oracle(inp4)
+    wl1 = wl.replace(num_q_heads=1)
+    inp1 = dataclasses.replace(inp, wl=wl1, q=q[:, :1].contiguous())
+    _, _, s1 = U.run_oracle(inp1)
+    assert np.allclose(s4, 4 * s1.astype(np.float64), rtol=1e-6, atol=1e-6)
+    # key of the summed query (four distinct heads)
+    tau = U.tau_of(wl.head_dim)
+    K = U.logical(inp, "k")[0, 0, U.gist_slots(wl.num_chunks, wl.chunk_size)]
+    qs = U.f64(inp.q)[0].sum(0)
+    _, _, s_orig = U.run_oracle(inp)
+    assert np.allclose(s_orig[0, 0], tau * K @ qs, rtol=1e-5, atol=1e-5)
+
+
+def test_ph_hierarchy_reduces_to_flat_topk():
+    wl = SMALL_H
+    inp = gi.make_inputs(wl, 31)
+    nm = wl.num_chunks // wl.gists_per_meta
+    out_h, s1, s2, ms, gs = U.run_oracle_h(inp, top_k_meta=nm)
+    _, sel_flat, _ = U.run_oracle(inp)
+    assert np.array_equal(s2, sel_flat)
+    assert np.all(np.sort(s1, axis=-1) == np.arange(nm))
+
+
+def test_pa_hierarchy_all_kept_is_dense_over_meta_and_sequence():
+    wl = SMALL_H
+    inp = gi.make_inputs(wl, 33)
+    nm = wl.num_chunks // wl.gists_per_meta
+    out, *_ = U.run_oracle_h(inp, top_k_meta=nm, top_k=wl.num_chunks)
+    q = U.f64(inp.q)
+    K, V = U.logical(inp, "k"), U.logical(inp, "v")
+    km, vm = U.f64(inp.k_meta), U.f64(inp.v_meta)
+    L = wl.num_chunks * (wl.chunk_size + 1)
+    tau = U.tau_of(wl.head_dim)
+    for b in range(wl.batch):
+        for h in range(wl.num_q_heads):
+            g = h // wl.group
+            Kall = np.concatenate([km[b, g, :nm], K[b, g, :L]])
+            Vall = np.concatenate([vm[b, g, :nm], V[b, g, :L]])
+            assert np.allclose(out[b, h], U.np_attend(q[b, h], Kall, Vall, tau),
+                               rtol=1e-10, atol=1e-12)
+
+
+def _np_hgsa(inp, k1, k2):
+    """Two-level selection and attention, numpy brute force."""
+    wl = inp.wl
+    R, C, G = wl.gists_per_meta, wl.chunk_size, wl.group
+    tau = U.tau_of(wl.head_dim)
+    q = U.f64(inp.q)
+    K, V = U.logical(inp, "k"), U.logical(inp, "v")
+    km, vm = U.f64(inp.k_meta), U.f64(inp.v_meta)
+    n, tail = U.shapes(inp)
+    out = np.zeros(q.shape)
+    sels = []
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            nm = n[b] // R
+            qg = q[b, g * G:(g + 1) * G]
+            SM = (tau * km[b, g, :nm] @ qg.T).sum(1).astype(np.float32)
+            s1 = U.np_topk(SM, k1)
+            cand = np.concatenate([np.arange(r * R, r * R + R) for r in s1] +
+                                  [np.arange(nm * R, n[b])]).astype(np.int64)
+            SC = (tau * K[b, g, cand * (C + 1) + C] @ qg.T).sum(1).astype(np.float32)
+            s2 = U.np_topk(SC, k2, ids=cand)
+            m = U.gsa_mask(n[b], tail[b], C, s2, K.shape[2], all_gists=False)
+            m[np.arange(nm * R, n[b]) * (C + 1) + C] = True
+            Kall = np.concatenate([km[b, g, :nm], K[b, g][m]])
+            Vall = np.concatenate([vm[b, g, :nm], V[b, g][m]])
+            for j in range(G):
+                out[b, g * G + j] = U.np_attend(q[b, g * G + j], Kall, Vall, tau)
+            sels.append((s1, s2))
+    return out, sels
+
+
+@pytest.mark.parametrize("lens", ["full", "ragged"])
+def test_hgsa_matches_brute_force(lens):
+    wl = SMALL_H
+    inp = gi.make_inputs(wl, 41, seq_lens=None if lens == "full" else [201, 150])
+    out, s1, s2, ms, gs = U.run_oracle_h(inp)
+    ref, sels = _np_hgsa(inp, wl.top_k_meta, wl.top_k)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+    i = 0
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            a1, a2 = sels[i]
+            i += 1
+            assert np.array_equal(s1[b, g][s1[b, g] >= 0], a1)
+            assert np.array_equal(s2[b, g][s2[b, g] >= 0], a2)
+
+
+@pytest.mark.parametrize("wl", [SMALL_BF16, SMALL_F32], ids=lambda w: w.name)
+def test_pi_convex_hull(wl):
+    inp = gi.make_inputs(wl, 3, seq_lens=ragged(wl, 1))
+    out, sel, _ = U.run_oracle(inp)
+    V = U.logical(inp, "v")
+    n, tail = U.shapes(inp)
+    for b in range(wl.batch):
+        for h in range(wl.num_q_heads):
+            g = h // wl.group
+            m = U.gsa_mask(n[b], tail[b], wl.chunk_size, sel[b, g], V.shape[2])
+            Vs = V[b, g][m]
+            assert np.all(out[b, h] >= Vs.min(0) - 1e-12)
+            assert np.all(out[b, h] <= Vs.max(0) + 1e-12)
+
+
+def test_sum_of_probs_keys():
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 8, seq_lens=ragged(wl, 4))
+    _, sel, sc = U.run_oracle(inp, flags=oracle.SCORE_SUM_PROBS)
+    keys = U.np_keys(inp, probs=True)
+    n, _ = U.shapes(inp)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            assert np.allclose(sc[b, g, :n[b]], keys[b][g], rtol=1e-5, atol=1e-7)
+            assert abs(float(np.sum(keys[b][g], dtype=np.float64)) - wl.group) < 1e-4
+    # a single head: probabilities are monotone in the logit, same selection
+    wl1 = SMALL_F32.replace(num_q_heads=2, num_kv_heads=2)
+    inp1 = gi.make_inputs(wl1, 9)
+    _, a, _ = U.run_oracle(inp1)
+    _, b_, _ = U.run_oracle(inp1, flags=oracle.SCORE_SUM_PROBS)
+    assert np.array_equal(a, b_)
+
+
+def test_external_selection_reproduces_own():
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 12, seq_lens=ragged(wl, 6))
+    out, sel, _ = U.run_oracle(inp)
+    out2, sel2, _ = U.run_oracle(inp, ext_sel=sel)
+    assert np.array_equal(out, out2) and np.array_equal(sel, sel2)
+
+
+def test_oracle_rejects_bad_config():
+    inp = gi.make_inputs(SMALL_BF16, 1)
+    c = U.cfg_of(inp)
+    for key, val in [("num_q_heads", 7), ("chunk_size", 0), ("top_k", -1), ("dtype", 5),
+                     ("flags", 0x40), ("max_pages", 1)]:
+        bad = dict(c, **{key: val})
+        with pytest.raises(ValueError):
+            oracle.gsa_decode(bad, U.np_raw(inp.q), U.np_raw(inp.k_cache),
+                              U.np_raw(inp.v_cache), U.np_raw(inp.block_table),
+                              U.np_raw(inp.seq_lens))
