@@ -1,0 +1,182 @@
+"""GSA decode benchmark on one MI355X.
+
+One step = one gsa_decode call (gist scoring, top-k select, unfolded
+attention, merge) over one batch of the workload, with the caches already
+resident in HBM.  Several copies of the caches are rotated so that no call
+finds the previous call's bytes in the 256 MB Infinity Cache (the copies
+together are far larger than it).
+
+Prints one JSON line: queries/s (batch x q-heads per second), algorithmic
+HBM GB/s against the 8 TB/s peak, and the CPU oracle on the host cores as a
+reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+import long_context_sparse_gist_amd as gsa
+from long_context_sparse_gist_amd import inputs as gi
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def alg_bytes(wl: gi.Workload) -> int:
+    """Bytes the method must read per call: every attended gist K/V, the
+    selected chunks' raw K/V (H-GSA: meta K/V, candidate gist K, selected gist
+    V) plus q and the output."""
+    e, d, G = wl.elem_bytes, wl.head_dim, wl.group
+    units = wl.batch * wl.num_kv_heads
+    M, C, k = wl.num_chunks, wl.chunk_size, wl.top_k
+    if wl.hgsa:
+        Mm, R, k1 = wl.num_meta, wl.gists_per_meta, wl.top_k_meta
+        per = e * d * (2 * Mm + k1 * R + k + 2 * k * C) + 2 * G * d * e
+    else:
+        per = e * d * (2 * M + 2 * k * C) + 2 * G * d * e
+    return units * per
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=gi.QWEN7B_128K.name, choices=sorted(gi.BY_NAME))
+    ap.add_argument("--copies", type=int, default=6,
+                    help="cache copies rotated between calls (defeats the Infinity Cache)")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle, as it stands, on the host cores: the whole batch, repeated
+    until `seconds` of wall time (at least one run)."""
+    import oracle
+    from tests import _util as U  # oracle glue (storage formats only)
+    wl = inp.wl
+    q = U.np_raw(inp.q)
+    kc = U.np_raw(inp.k_cache)
+    vc = U.np_raw(inp.v_cache)
+    bt = U.np_raw(inp.block_table)
+    sl = U.np_raw(inp.seq_lens)
+    cfg = U.cfg_of(inp)
+    threads = oracle.max_threads()
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        if wl.hgsa:
+            oracle.hgsa_decode(cfg, q, kc, vc, bt, sl, U.np_raw(inp.k_meta), U.np_raw(inp.v_meta))
+        else:
+            oracle.gsa_decode(cfg, q, kc, vc, bt, sl)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 50:
+            break
+    t = statistics.median(times)
+    queries = wl.batch * wl.num_q_heads
+    return {"value": queries / t, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole batch of the workload ({queries} queries), median of "
+                      f"{len(times)} runs, OpenMP over (batch, kv-head) units"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has "
+              f"no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    wl = gi.BY_NAME[args.workload]
+    idx = gi.WORKLOADS.index(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gsa.lib()
+
+    inp = gi.make_inputs(wl, gi.seed_of(idx), device=dev)
+    copies = [inp]
+    for _ in range(max(1, args.copies) - 1):
+        copies.append(gi.GsaInputs(wl, inp.q, inp.k_cache.clone(), inp.v_cache.clone(),
+                                   inp.block_table, inp.seq_lens, inp.planted,
+                                   None if inp.k_meta is None else inp.k_meta.clone(),
+                                   None if inp.v_meta is None else inp.v_meta.clone()))
+    out = torch.empty_like(inp.q)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(c):
+        if wl.hgsa:
+            gsa.hgsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.k_meta,
+                            c.v_meta, num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                            page_chunks=wl.page_chunks, gists_per_meta=wl.gists_per_meta,
+                            top_k_meta=wl.top_k_meta, top_k=wl.top_k, out=out, stream=stream)
+        else:
+            gsa.gsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                           num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                           page_chunks=wl.page_chunks, top_k=wl.top_k, out=out, stream=stream)
+
+    for i in range(args.warmup):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` calls; HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(copies[i % len(copies)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    mean_call_s = statistics.fmean(call_ms) / 1e3
+
+    queries = wl.batch * wl.num_q_heads
+    nbytes = alg_bytes(wl)
+    ms_per_step = wall / args.steps * 1e3
+    value = queries * args.steps / wall
+    achieved = nbytes / mean_call_s / 1e9
+    res = {
+        "metric": "GSA decode queries/sec (batch x q-heads) and achieved HBM GB/s vs peak "
+                  "at 128K ctx",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == gi.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "context_tokens": wl.raw_tokens, "chunk_size": wl.chunk_size,
+                   "top_k": wl.top_k, "page_chunks": wl.page_chunks,
+                   "cache_copies": len(copies)},
+        "hbm_gbps_alg": achieved,
+        "call_us": {"mean": statistics.fmean(call_ms) * 1e3,
+                    "median": statistics.median(call_ms) * 1e3,
+                    "p10": float(np.percentile(call_ms, 10)) * 1e3,
+                    "p90": float(np.percentile(call_ms, 90)) * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "gsa_decode call", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "alg_bytes_per_call": nbytes},
+    }
+    if args.cpu_baseline:
+        del copies
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * gsa.h -- C ABI of the gist sparse attention (GSA) decode library for
+ * MI355X (gfx950).
+ *
+ * One decode step of "Forget, Then Recall: Learnable Compression and
+ * Selective Unfolding via Gist Sparse Attention", as described on the
+ * gist.science technical summaries of that paper (ja / ko / nl pages):
+ *
+ *   1. score every gist of the cached context against the current query,
+ *      s_{t,m} = q_t . k_{g_m}  (nl page, Methodologie, "Het Proces",
+ *      Scoring; ja page, section 2.1 item 2);
+ *   2. keep the top-k chunks (ja page 2.1 item 3; nl page, "Selectie");
+ *   3. unfold the raw tokens of those chunks (nl page, "Selectieve
+ *      Ontvouwing");
+ *   4. attend over the gist tokens plus the unfolded raw tokens (ja page 2.1
+ *      item 4, "hybrid attention"; ko page, methodology, hybrid attention).
+ * hgsa_decode adds the coarse-to-fine gist-of-gist level (ja page 2.2; nl
+ * page, "Hierarchische Uitbreiding").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are caller-owned device memory (HIP device pointers), dense
+ *    row-major with the shapes given below.  The library allocates nothing,
+ *    keeps no pointer after a call returns and has no global mutable state.
+ *  - Every host-side argument is validated before anything is enqueued.  On
+ *    an error nothing is launched, no output is touched and the status is
+ *    returned; nothing aborts or throws across this ABI.
+ *  - GSA_OK means the work has been enqueued on `stream` (a hipStream_t;
+ *    NULL is the null stream); results are ready after the caller
+ *    synchronises with that stream.  Device faults surface there.
+ *  - Sequence lengths and block tables are device arrays read by the
+ *    kernels; their contents must satisfy the constraints stated below (the
+ *    host cannot check device memory without a synchronisation).  Lengths
+ *    outside [0, num_chunks*C + C-1] are clamped into that range.
+ *  - Two calls that share one workspace must not overlap in time.
+ */
+#ifndef GSA_H_
+#define GSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GSA_OK = 0,
+    GSA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
+    GSA_ERR_BAD_SHAPE = 2,  /* a size or count is out of range */
+    GSA_ERR_BAD_DTYPE = 3,  /* dtype not GSA_F32 / GSA_BF16 */
+    GSA_ERR_BAD_FLAGS = 4,  /* unknown or unsupported flag bits */
+    GSA_ERR_WORKSPACE = 5,  /* workspace NULL, too small or misaligned */
+    GSA_ERR_DEVICE = 6,     /* no usable HIP device / not a gfx950 device */
+    GSA_ERR_LAUNCH = 7      /* a kernel launch failed */
+} gsa_status_t;
+
+typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype_t;
+
+/* Routing key shared by the query heads of one GQA group (one selection per
+ * (batch, kv-head)).  Default: the sum over the group of the scaled logits
+ * sm_scale * q_h . k_gist.  SUM_PROBS: the sum over the group of each head's
+ * softmax probability of the gist, the softmax taken over the gists. */
+#define GSA_SCORE_SUM_LOGITS 0x0u
+#define GSA_SCORE_SUM_PROBS 0x1u
+/* Attention set.  Default: every gist plus the raw tokens of the selected
+ * chunks.  SELECTED_GISTS: only the selected chunks' gists plus their raw
+ * tokens (the "SG+SR" rule of the ja page's ablation, section 4). */
+#define GSA_SET_ALL_GISTS 0x0u
+#define GSA_SET_SELECTED_GISTS 0x2u
+/* Run the portable fp32-VALU kernels instead of the MFMA kernels (the fp32
+ * dtype always uses them); a cross-check of the bf16 MFMA path. */
+#define GSA_PATH_PORTABLE 0x100u
+
+typedef struct {
+    int32_t batch;         /* B >= 1 */
+    int32_t num_q_heads;   /* Hq >= 1, a multiple of num_kv_heads */
+    int32_t num_kv_heads;  /* Hkv >= 1; query head h reads kv-head h / (Hq/Hkv) */
+    int32_t head_dim;      /* d: 64 or 128 */
+    int32_t top_k;         /* chunks unfolded per (batch, kv-head), >= 0; clamped
+                              per sequence to its gist count; 0 = gists only.
+                              For hgsa_decode: k2, the gist-level top-k. */
+    float sm_scale;        /* softmax scale tau; <= 0 selects 1/sqrt(d) */
+    int32_t dtype;         /* gsa_dtype_t of q, caches, meta caches and out */
+    uint32_t flags;        /* GSA_SCORE_* | GSA_SET_* */
+} gsa_params_t;
+
+/* Paged interleaved raw+gist KV cache.
+ *   k_cache, v_cache : [num_pages][num_kv_heads][page_chunks*(chunk_size+1)][head_dim]
+ * Logical slot s of a sequence holds raw token c of chunk m at
+ * s = m*(C+1) + c (c < C) and the gist of chunk m at s = m*(C+1) + C, i.e. one
+ * gist token after every chunk of C raw tokens (ja page 2.1 item 1).  Logical
+ * page p = s / (page_chunks*(C+1)) of sequence b is physical page
+ * block_table[b*max_pages + p]; pages may be shared between sequences.
+ *   block_table : int32 [batch][max_pages], entries in [0, num_pages)
+ *   seq_lens    : int32 [batch] raw tokens per sequence, or NULL meaning
+ *                 num_chunks*chunk_size for all.  A sequence of L raw tokens
+ *                 has L/C complete chunks (each with its gist) and L%C raw
+ *                 tokens after its last gist, which are always attended.
+ *                 Its block-table row must map every page those
+ *                 (L/C)*(C+1) + L%C slots touch. */
+typedef struct {
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t num_chunks;    /* capacity in chunks (>= L/C of every sequence) */
+    int32_t chunk_size;    /* C >= 1 */
+    int32_t page_chunks;   /* chunks per page >= 1 */
+    int32_t num_pages;     /* physical pages in the caches >= 1 */
+    int32_t max_pages;     /* block-table row length >= 1 */
+} gsa_kv_t;
+
+/* Meta-gists for hgsa_decode.  Meta-gist r of a sequence summarises gists
+ * [r*R, r*R + R) and exists once all R of them exist; gists after the last
+ * complete group are always attended and are always candidates.
+ *   k_meta, v_meta : [batch][num_kv_heads][max_meta][head_dim]  */
+typedef struct {
+    const void* k_meta;
+    const void* v_meta;
+    int32_t max_meta;        /* >= num_chunks / gists_per_meta */
+    int32_t gists_per_meta;  /* R >= 1 */
+    int32_t top_k_meta;      /* k1 >= 0 meta-gists kept per (batch, kv-head) */
+} hgsa_meta_t;
+
+/* Bytes of device workspace gsa_decode needs for these shapes (0 if the
+ * shapes are invalid).  The workspace must be 256-byte aligned and
+ * zero-filled before its first use; every call that completes leaves it
+ * zero-filled again, so one zeroed allocation serves any number of
+ * sequential calls with shapes that fit it. */
+size_t gsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv);
+
+/* As gsa_workspace_size, for hgsa_decode. */
+size_t hgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv,
+                           const hgsa_meta_t* meta);
+
+/* One GSA decode step for every (batch, query head).
+ *   q       : [batch][num_q_heads][head_dim], dtype
+ *   out     : [batch][num_q_heads][head_dim], dtype (rounded to nearest even
+ *             from the fp32 result for bf16)
+ *   sel_idx : NULL, or int32 [batch][num_kv_heads][top_k]: selected chunk
+ *             ids in ascending order, -1 in unused slots
+ *   scores  : NULL, or float [batch][num_kv_heads][num_chunks]: routing key
+ *             of every gist, -inf past each sequence's gists
+ * Selection: the top_k largest keys, ties to the lower chunk index, NaN keys
+ * last. */
+gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q,
+                        void* out, int32_t* sel_idx, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* One H-GSA decode step: keep the top_k_meta meta-gists by routing key, score
+ * the gists of the kept groups (plus the gists after the last complete
+ * group), keep the top_k of those, and attend over every meta-gist, the kept
+ * gists, the gists after the last complete group, the raw tokens of the kept
+ * chunks and the raw tokens after the last gist.  flags: GSA_SCORE_* only.
+ *   sel_meta : NULL, or int32 [batch][num_kv_heads][top_k_meta] ascending, -1 padded
+ *   sel_idx  : NULL, or int32 [batch][num_kv_heads][top_k] ascending, -1 padded */
+gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv,
+                         const hgsa_meta_t* meta, const void* q, void* out,
+                         int32_t* sel_meta, int32_t* sel_idx, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gsa_status_string(gsa_status_t s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GSA_H_ */

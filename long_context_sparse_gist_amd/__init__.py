@@ -1,0 +1,223 @@
+"""Python binding of libgsa.so, the MI355X gist sparse attention decode library.
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  The library
+is loaded on first use and a missing or unloadable library raises; there is no
+fallback path.
+
+Names mirror the C ABI in include/gsa.h: gsa_decode, hgsa_decode,
+gsa_workspace_size, hgsa_workspace_size, gsa_status_string, gsa_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgsa.so")
+
+GSA_F32 = 0
+GSA_BF16 = 1
+GSA_SCORE_SUM_LOGITS = 0x0
+GSA_SCORE_SUM_PROBS = 0x1
+GSA_SET_ALL_GISTS = 0x0
+GSA_SET_SELECTED_GISTS = 0x2
+GSA_PATH_PORTABLE = 0x100
+
+STATUS = {0: "GSA_OK", 1: "GSA_ERR_NULL_ARG", 2: "GSA_ERR_BAD_SHAPE", 3: "GSA_ERR_BAD_DTYPE",
+          4: "GSA_ERR_BAD_FLAGS", 5: "GSA_ERR_WORKSPACE", 6: "GSA_ERR_DEVICE",
+          7: "GSA_ERR_LAUNCH"}
+
+
+class GsaParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class GsaKV(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("num_chunks", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("page_chunks", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
+
+
+class HgsaMeta(ctypes.Structure):
+    _fields_ = [("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
+                ("max_meta", ctypes.c_int32), ("gists_per_meta", ctypes.c_int32),
+                ("top_k_meta", ctypes.c_int32)]
+
+
+class GsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({gsa_status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_sparse_gist_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.gsa_workspace_size.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV)]
+        L.gsa_workspace_size.restype = ctypes.c_size_t
+        L.hgsa_workspace_size.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
+                                          ctypes.POINTER(HgsaMeta)]
+        L.hgsa_workspace_size.restype = ctypes.c_size_t
+        L.gsa_decode.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV), P, P, P, P,
+                                 P, ctypes.c_size_t, P]
+        L.gsa_decode.restype = ctypes.c_int
+        L.hgsa_decode.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
+                                  ctypes.POINTER(HgsaMeta), P, P, P, P, P, ctypes.c_size_t, P]
+        L.hgsa_decode.restype = ctypes.c_int
+        L.gsa_status_string.argtypes = [ctypes.c_int]
+        L.gsa_status_string.restype = ctypes.c_char_p
+        L.gsa_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def gsa_status_string(status: int) -> str:
+    return lib().gsa_status_string(status).decode()
+
+
+def gsa_version() -> int:
+    return lib().gsa_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GSA_F32
+    if t.dtype == torch.bfloat16:
+        return GSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_params(q: torch.Tensor, num_kv_heads: int, top_k: int, sm_scale: float = 0.0,
+                flags: int = 0) -> GsaParams:
+    B, Hq, d = q.shape
+    return GsaParams(B, Hq, num_kv_heads, d, top_k, sm_scale, _dtype_code(q), flags)
+
+
+def make_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+            seq_lens: Optional[torch.Tensor], num_chunks: int, chunk_size: int,
+            page_chunks: int) -> GsaKV:
+    return GsaKV(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), num_chunks,
+                 chunk_size, page_chunks, k_cache.shape[0], block_table.shape[1])
+
+
+def make_meta(k_meta: torch.Tensor, v_meta: torch.Tensor, gists_per_meta: int,
+              top_k_meta: int) -> HgsaMeta:
+    return HgsaMeta(_ptr(k_meta), _ptr(v_meta), k_meta.shape[2], gists_per_meta, top_k_meta)
+
+
+def gsa_workspace_size(params: GsaParams, kv: GsaKV) -> int:
+    return lib().gsa_workspace_size(ctypes.byref(params), ctypes.byref(kv))
+
+
+def hgsa_workspace_size(params: GsaParams, kv: GsaKV, meta: HgsaMeta) -> int:
+    return lib().hgsa_workspace_size(ctypes.byref(params), ctypes.byref(kv), ctypes.byref(meta))
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes on `device`, reused across
+    calls (calls on one device must not overlap when they share it)."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index)
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = t
+    return t
+
+
+def _check(q, k_cache, v_cache, block_table, seq_lens):
+    for t in (q, k_cache, v_cache, block_table):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, caches and block_table must be contiguous device tensors")
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_cuda):
+        raise TypeError("seq_lens must be an int32 device tensor")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
+               chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
+               flags: int = 0, out=None, sel_idx=None, scores=None, ws=None, stream=None):
+    """One GSA decode step (see gsa_decode in include/gsa.h).
+
+    q [B][Hq][d]; k_cache, v_cache [num_pages][Hkv][page_chunks*(C+1)][d];
+    block_table int32 [B][max_pages]; seq_lens int32 [B] or None.
+    Returns out [B][Hq][d] (allocated if not given)."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    Hkv = k_cache.shape[1]
+    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = gsa_workspace_size(p, kv)
+    if nbytes == 0:
+        raise GsaError(2, "gsa_workspace_size")
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    st = lib().gsa_decode(ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(sel_idx),
+                          _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream_ptr(stream, q.device))
+    if st != 0:
+        raise GsaError(st, "gsa_decode")
+    return out
+
+
+def hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_meta, *, num_chunks: int,
+                chunk_size: int, page_chunks: int, gists_per_meta: int, top_k_meta: int,
+                top_k: int, sm_scale: float = 0.0, flags: int = 0, out=None, sel_meta=None,
+                sel_idx=None, ws=None, stream=None):
+    """One H-GSA decode step (see hgsa_decode in include/gsa.h).
+    k_meta, v_meta [B][Hkv][max_meta][d]."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    for t in (k_meta, v_meta):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("meta caches must be contiguous device tensors of q's dtype")
+    Hkv = k_cache.shape[1]
+    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    m = make_meta(k_meta, v_meta, gists_per_meta, top_k_meta)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = hgsa_workspace_size(p, kv, m)
+    if nbytes == 0:
+        raise GsaError(2, "hgsa_workspace_size")
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    st = lib().hgsa_decode(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(m), _ptr(q), _ptr(out),
+                           _ptr(sel_meta), _ptr(sel_idx), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream_ptr(stream, q.device))
+    if st != 0:
+        raise GsaError(st, "hgsa_decode")
+    return out

@@ -1,0 +1,103 @@
+// Internal declarations of the GSA decode library: kernel argument block,
+// device helpers and the host launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gsa {
+
+constexpr unsigned kFlagSumProbs = 0x1u;
+constexpr unsigned kFlagSelectedGists = 0x2u;
+constexpr unsigned kFlagPortable = 0x100u;
+
+// Everything a kernel needs to walk one decode call.  Built once on the host,
+// passed by value.
+struct Args {
+    // shapes
+    int B, Hq, Hkv, G, D, C;
+    int num_chunks, page_chunks, num_pages, max_pages, spp;  // spp: slots per page
+    int top_k;
+    float tau;        // softmax scale
+    float tau_log2e;  // tau * log2(e): logits in the exp2 domain
+    unsigned flags;
+    int dtype;        // 0 f32, 1 bf16
+    // inputs
+    const void* q;
+    const void* kc;
+    const void* vc;
+    const int32_t* bt;
+    const int32_t* seq_lens;
+    // H-GSA inputs (null for flat GSA)
+    const void* km;
+    const void* vm;
+    int R, top_k_meta, max_meta;
+    // work buffers
+    float* keys;      // [units][key_stride] routing keys
+    int key_stride;
+    int32_t* sel;     // [units][top_k] selected chunk ids, ascending, -1 padded
+    int32_t* sel_meta;   // [units][top_k_meta] (H-GSA)
+    float* mkeys;     // [units][max_meta] meta routing keys (H-GSA)
+    float* ckeys;     // [units][cand_stride] candidate routing keys (H-GSA)
+    int32_t* cand;    // [units][cand_stride] candidate chunk ids (H-GSA)
+    int cand_stride;
+    float2* part_ml;  // [units][NS][G] (max in exp2 domain, sum)
+    float* part_acc;  // [units][NS][G][D]
+    int NS;           // partial slots per unit
+    int S1;           // token-list splits of the "all gists" / meta list
+    int SL;           // tokens per split of that list
+    int SR;           // tokens per split of the unfolded list
+    void* out;        // [B][Hq][D]
+};
+
+// Length of sequence b in chunks and raw tail, clamped so that nothing past
+// the block-table row is ever read.
+__device__ inline void seq_shape(const Args& a, int b, int& n, int& tail) {
+    long L = a.seq_lens ? (long)a.seq_lens[b] : (long)a.num_chunks * a.C;
+    long maxL = (long)a.num_chunks * a.C + a.C - 1;
+    L = L < 0 ? 0 : (L > maxL ? maxL : L);
+    n = (int)(L / a.C);
+    tail = (int)(L - (long)n * a.C);
+    if (n > a.num_chunks) { n = a.num_chunks; tail = 0; }
+    long cap = (long)a.max_pages * a.spp - (long)n * (a.C + 1);
+    if (tail > cap) tail = (int)cap;
+}
+
+// Element offset of logical slot s of sequence b, kv-head g in the paged cache.
+__device__ inline size_t slot_offset(const Args& a, int b, int g, int s) {
+    int lp = s / a.spp;
+    int off = s - lp * a.spp;
+    int phys = a.bt[(size_t)b * a.max_pages + lp];
+    return (((size_t)phys * a.Hkv + g) * a.spp + off) * (size_t)a.D;
+}
+
+// Order-preserving 32-bit key of a float: larger float -> larger key; -0 and
+// +0 map to one key; NaN maps to the smallest key.
+__device__ inline uint32_t order_key(float f) {
+    if (f != f) return 0u;
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of unfolded (non-"all gists") list tokens of a sequence with `ns`
+// selected chunks and `tail` raw tokens after its last gist.
+__device__ inline int unfolded_len(const Args& a, int ns, int tail) {
+    return ns * a.C + tail + ((a.flags & kFlagSelectedGists) ? ns : 0);
+}
+
+// ---- host launchers (one per kernel family) ----
+enum ListKind { kListGists = 0, kListUnfolded = 1, kListMeta = 2, kListCand = 3 };
+
+hipError_t launch_attn_mfma(const Args& a, int kind, int splits, hipStream_t st);
+hipError_t launch_attn_portable(const Args& a, int kind, int splits, hipStream_t st);
+int mfma_tokens_per_block(int D);
+int portable_tokens_per_block();
+
+enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
+hipError_t launch_select(const Args& a, int mode, hipStream_t st);
+hipError_t launch_merge(const Args& a, int hier, hipStream_t st);
+hipError_t launch_cand_keys(const Args& a, hipStream_t st);
+
+}  // namespace gsa

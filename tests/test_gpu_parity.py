@@ -1,0 +1,200 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases cover every unit and span several splits with ragged tails; the
+full-size workloads, in the launch configuration the benchmark times, are
+checked on a seeded sample of (batch, kv-head) units.  Selections follow the
+gap rule, outputs the dtype's tolerance (bf16: 2e-2 abs / 1e-2 rel; fp32:
+1e-4 / 1e-4), keys 1e-3 abs / 1e-4 rel.
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_gist_amd as gsa
+from long_context_sparse_gist_amd import inputs as gi
+from tests import gpu_util as GU
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+SMALL = {
+    "b3-g4-d64-c8": gi.Workload("b3-g4-d64-c8", gi.BF16, 3, 8, 2, 64, 8, 300, 20, 16,
+                                plant="align", plant_count=4),
+    "b2-g7-d128-c16": gi.Workload("b2-g7-d128-c16", gi.BF16, 2, 14, 2, 128, 16, 333, 37, 8,
+                                  plant="align", plant_count=5),
+    "b2-g4-d128-c32": gi.Workload("b2-g4-d128-c32", gi.BF16, 2, 8, 2, 128, 32, 150, 9, 4,
+                                  plant="doc_bias", n_docs=5),
+    "b1-g1-d128-c16": gi.Workload("b1-g1-d128-c16", gi.BF16, 1, 3, 3, 128, 16, 260, 11, 16),
+    "b2-g16-d64-c4": gi.Workload("b2-g16-d64-c4", gi.BF16, 2, 16, 1, 64, 4, 700, 50, 64),
+    "f32-b2-g3-d64": gi.Workload("f32-b2-g3-d64", gi.F32, 2, 6, 2, 64, 16, 200, 12, 16,
+                                 plant="align", plant_count=3),
+}
+
+
+def lens_for(wl, kind, seed=0):
+    M, C = wl.num_chunks, wl.chunk_size
+    if kind == "full":
+        return None
+    rng = np.random.default_rng(seed)
+    L = [int(x) for x in rng.integers(1, M * C + C - 1, size=wl.batch)]
+    if kind == "edge":
+        L[0] = 0                     # empty sequence
+        if wl.batch > 1:
+            L[1] = C - 1             # no gist yet, raw tail only
+        if wl.batch > 2:
+            L[2] = 3 * C             # fewer chunks than top_k
+    return L
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("lens", ["full", "ragged", "edge"])
+def test_small_all_units(gpu, name, lens):
+    wl = SMALL[name]
+    say(f"[parity] {name} lens={lens}")
+    inp = gi.make_inputs(wl, 100 + len(name), seq_lens=lens_for(wl, lens, 3), spare_pages=2)
+    g_inp = GU.to(inp, gpu)
+    res = GU.run_gpu(g_inp)
+    GU.check_gsa(inp, res)
+
+
+@pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16"])
+@pytest.mark.parametrize("top_k", [0, 1, 10 ** 6])
+def test_small_topk_extremes(gpu, name, top_k):
+    wl = SMALL[name]
+    say(f"[parity] {name} top_k={top_k}")
+    inp = gi.make_inputs(wl, 7, seq_lens=lens_for(wl, "ragged", 1))
+    res = GU.run_gpu(GU.to(inp, gpu), top_k=top_k)
+    GU.check_gsa(inp, res, top_k=top_k)
+
+
+@pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16", "f32-b2-g3-d64"])
+def test_small_selected_gists_set(gpu, name):
+    wl = SMALL[name]
+    say(f"[parity] {name} selected-gists set")
+    inp = gi.make_inputs(wl, 9, seq_lens=lens_for(wl, "edge", 2))
+    flags = gsa.GSA_SET_SELECTED_GISTS
+    res = GU.run_gpu(GU.to(inp, gpu), flags=flags)
+    GU.check_gsa(inp, res, flags=flags)
+
+
+@pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16"])
+def test_portable_path_on_bf16(gpu, name):
+    wl = SMALL[name]
+    say(f"[parity] {name} portable kernels")
+    inp = gi.make_inputs(wl, 5, seq_lens=lens_for(wl, "ragged", 4))
+    res = GU.run_gpu(GU.to(inp, gpu), flags=gsa.GSA_PATH_PORTABLE)
+    GU.check_gsa(inp, res)
+
+
+def test_custom_scale(gpu):
+    wl = SMALL["b2-g7-d128-c16"]
+    say("[parity] sm_scale=0.05")
+    inp = gi.make_inputs(wl, 15)
+    res = GU.run_gpu(GU.to(inp, gpu), sm_scale=0.05)
+    GU.check_gsa(inp, res, sm_scale=0.05)
+
+
+def test_shared_and_shuffled_pages(gpu):
+    wl = SMALL["b3-g4-d64-c8"]
+    say("[parity] shared pages")
+    inp = gi.make_inputs(wl, 21, seq_lens=[2000, 1500, 2400])
+    inp = gi.share_pages(inp, 0, 2)
+    res = GU.run_gpu(GU.to(inp, gpu))
+    GU.check_gsa(inp, res)
+    inp2 = gi.make_inputs(wl, 21, seq_lens=[2000, 1500, 2400], shuffle_pages=False)
+    res2 = GU.run_gpu(GU.to(inp2, gpu))
+    GU.check_gsa(inp2, res2)
+
+
+def test_tiny_f32_workload(gpu):
+    wl = gi.TINY_F32
+    say(f"[parity] {wl.name}")
+    inp = gi.make_inputs(wl, gi.seed_of(0))
+    res = GU.run_gpu(GU.to(inp, gpu))
+    assert GU.check_gsa(inp, res) == 0
+    assert set(inp.planted[0, 0].tolist()) <= set(res[1][0, 0].tolist())
+
+
+def test_deterministic(gpu):
+    wl = SMALL["b2-g7-d128-c16"]
+    say("[parity] determinism")
+    g_inp = GU.to(gi.make_inputs(wl, 3, seq_lens=lens_for(wl, "ragged", 7)), gpu)
+    first = GU.run_gpu(g_inp)
+    for _ in range(5):
+        again = GU.run_gpu(g_inp)
+        for x, y in zip(first, again):
+            assert np.array_equal(x, y)
+
+
+FULL = [gi.LLAMA1B_32K, gi.QWEN7B_128K, gi.MULTIDOC_120K]
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_full_workload_sampled_units(gpu, idx):
+    wl = gi.WORKLOADS[idx]
+    say(f"[parity] full {wl.name}")
+    inp = gi.make_inputs(wl, gi.seed_of(idx), device=gpu)
+    res = GU.run_gpu(inp)
+    rng = random.Random(idx)
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    sample = rng.sample(units, 6)
+    GU.check_gsa(inp, res, units=sample)
+    # planted chunks are routed to (align planting: every planted chunk kept)
+    if wl.plant == "align":
+        sel = res[1]
+        for b, g in sample:
+            assert set(inp.planted[b, g].tolist()) <= set(sel[b, g].tolist())
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ---------------- H-GSA ----------------
+
+SMALL_H = {
+    "h-b2-g4-d64-r4": gi.Workload("h-b2-g4-d64-r4", gi.BF16, 2, 8, 2, 64, 8, 400, 12, 16,
+                                  plant="align_meta", plant_count=3, gists_per_meta=4,
+                                  top_k_meta=6),
+    "h-b1-g7-d128-r16": gi.Workload("h-b1-g7-d128-r16", gi.BF16, 1, 7, 1, 128, 16, 600, 20, 16,
+                                    plant="align_meta", plant_count=2, gists_per_meta=16,
+                                    top_k_meta=5),
+    "h-f32-b2-g2-r8": gi.Workload("h-f32-b2-g2-r8", gi.F32, 2, 4, 2, 64, 4, 256, 10, 16,
+                                  plant="align_meta", plant_count=2, gists_per_meta=8,
+                                  top_k_meta=3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_H))
+@pytest.mark.parametrize("lens", ["full", "ragged", "edge"])
+def test_hgsa_small(gpu, name, lens):
+    wl = SMALL_H[name]
+    say(f"[parity] {name} lens={lens}")
+    inp = gi.make_inputs(wl, 200 + len(name), seq_lens=lens_for(wl, lens, 5))
+    res = GU.run_gpu_h(GU.to(inp, gpu))
+    GU.check_hgsa(inp, res)
+
+
+@pytest.mark.parametrize("k1,k2", [(0, 5), (2, 0), (10 ** 5, 10 ** 5)])
+def test_hgsa_extremes(gpu, k1, k2):
+    wl = SMALL_H["h-b2-g4-d64-r4"]
+    say(f"[parity] hgsa k1={k1} k2={k2}")
+    inp = gi.make_inputs(wl, 17, seq_lens=lens_for(wl, "ragged", 8))
+    res = GU.run_gpu_h(GU.to(inp, gpu), top_k=k2, top_k_meta=k1)
+    GU.check_hgsa(inp, res, top_k=k2, top_k_meta=k1)
+
+
+def test_hgsa_full_workload_sampled_units(gpu):
+    wl = gi.HGSA_1M
+    say(f"[parity] full {wl.name}")
+    inp = gi.make_inputs(wl, gi.seed_of(4), device=gpu)
+    res = GU.run_gpu_h(inp)
+    rng = random.Random(4)
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    GU.check_hgsa(inp, res, units=rng.sample(units, 4))
+    del inp
+    torch.cuda.empty_cache()
