@@ -124,10 +124,11 @@ typedef struct {
 } hgsa_meta_t;
 
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the
- * shapes are invalid).  The workspace must be 256-byte aligned and
- * zero-filled before its first use; every call that completes leaves it
- * zero-filled again, so one zeroed allocation serves any number of
- * sequential calls with shapes that fit it. */
+ * shapes are invalid).  The workspace must be 256-byte aligned and its first
+ * 16 KiB (a control block of work-queue counters) must be zero before its
+ * first use; every call that completes leaves that block zero again and uses
+ * the rest as scratch, so one zero-filled allocation serves any number of
+ * sequential calls, of any shapes that fit it. */
 size_t gsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv);
 
 /* As gsa_workspace_size, for hgsa_decode. */

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgsa.so")
-SOURCES = ["api.hip", "attn_mfma.hip", "attn_portable.hip", "select.hip", "merge.hip"]
+SOURCES = ["api.hip", "fused.hip", "attn_mfma.hip", "attn_portable.hip", "select.hip",
+           "merge.hip"]
 ARCH = "gfx950"
 
 

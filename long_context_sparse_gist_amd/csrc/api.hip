@@ -15,19 +15,27 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxGroup = 16;
 constexpr long kMaxTopK = 1L << 20;
 constexpr int kVersion = 100;  // 0.1.0
+// Control block at the start of every workspace layout: the single-launch
+// kernel's counters, zero between calls.  No layout writes scratch data below
+// this offset, so reusing one workspace across shapes keeps it zero.
+constexpr size_t kCtlWords = 4096;
+constexpr long kMaxFusedUnits = (long)(kCtlWords - 8) / 3;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
     Args a;
+    gsa::Sched sc;
     bool hier;
     bool mfma;
+    bool fused;        // single-launch work-queue kernel
     int TB;            // tokens per split of every list
     int S1;            // splits of the gist (flat) / meta (H-GSA) list
     int Sc;            // splits of the candidate list (H-GSA)
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
-    size_t off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc, total;
+    size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
+        total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -106,16 +114,30 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         long k2 = p->top_k < cc ? p->top_k : cc;
         cap2 = k2 * C + (C - 1) + k2 + (a.R - 1);
     }
-    pl.S1 = (int)((cap1 + pl.TB - 1) / pl.TB);
+    pl.fused = pl.mfma && !pl.hier && units <= kMaxFusedUnits;
+    const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
+    const int TB = pl.fused ? gsa::kFusedTB : pl.TB;
+    pl.S1 = (int)((cap1 + TA - 1) / TA);
     pl.Sc = (int)((pl.cand_cap + pl.TB - 1) / pl.TB);
-    pl.S2 = (int)((cap2 + pl.TB - 1) / pl.TB);
+    pl.S2 = (int)((cap2 + TB - 1) / TB);
+    if (pl.fused) {  // every unit owns at least one task of each kind
+        pl.S1 = pl.S1 > 0 ? pl.S1 : 1;
+        pl.S2 = pl.S2 > 0 ? pl.S2 : 1;
+    }
     a.S1 = pl.S1;
-    a.SL = pl.TB;
-    a.SR = pl.TB;
+    a.SL = TA;
+    a.SR = TB;
     a.NS = pl.S1 + pl.S2;
+    pl.sc.units = (int)units;
+    pl.sc.S1 = pl.S1;
+    pl.sc.S2 = pl.S2;
+    pl.sc.TA = TA;
+    pl.sc.TB = TB;
+    pl.sc.total = (int)(units * (pl.S1 + pl.S2));
     a.key_stride = kv->num_chunks;
     a.cand_stride = pl.cand_cap;
     size_t off = 0;
+    pl.off_ctl = off;   off += sizeof(unsigned) * kCtlWords;
     pl.off_keys = off;  off += align_up(sizeof(float) * units * (pl.hier ? 0 : M));
     pl.off_sel = off;   off += align_up(sizeof(int32_t) * units * p->top_k);
     pl.off_selm = off;  off += align_up(sizeof(int32_t) * units * (pl.hier ? m->top_k_meta : 0));
@@ -203,6 +225,15 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     a.out = out;
     hipStream_t st = (hipStream_t)stream;
 
+    if (pl.fused) {
+        unsigned* ctl = (unsigned*)(ws + pl.off_ctl);
+        pl.sc.err = ctl + 2;
+        pl.sc.cntA = ctl + 8;
+        pl.sc.cntB = ctl + 8 + pl.sc.units;
+        pl.sc.ready = ctl + 8 + 2 * pl.sc.units;
+        GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
+        return GSA_OK;
+    }
     if ((s = run_attn(pl, gsa::kListGists, pl.S1, st)) != GSA_OK) return s;
     GSA_LAUNCH(gsa::launch_select(a, gsa::kSelGists, st));
     if ((s = run_attn(pl, gsa::kListUnfolded, pl.S2, st)) != GSA_OK) return s;

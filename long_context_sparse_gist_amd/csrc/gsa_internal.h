@@ -95,6 +95,22 @@ hipError_t launch_attn_portable(const Args& a, int kind, int splits, hipStream_t
 int mfma_tokens_per_block(int D);
 int portable_tokens_per_block();
 
+// Work-queue state and geometry of the single-launch kernel.  The counters
+// live in the caller's workspace and are zero between calls.
+struct Sched {
+    unsigned* cntA;    // [units] finished gist-slice tasks
+    unsigned* cntB;    // [units] finished unfolded tasks
+    unsigned* ready;   // [units] selection published
+    unsigned* err;     // set if a wait gave up (never expected)
+    int units;
+    int S1, S2;        // task slots per unit (capacity)
+    int TA, TB;        // tokens per task
+    int total;         // tickets
+};
+hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
+constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
+constexpr int kFusedTB = 256;  // tokens per unfolded task
+
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
 hipError_t launch_merge(const Args& a, int hier, hipStream_t st);

@@ -83,10 +83,21 @@ __device__ inline int cand_gist(const Args& a, const ListCtx& c, int p) {
     return c.nm * a.R + (p - head);
 }
 
+// Selection entry i of unit u, clamped into [0, n).  `coherent`: read with a
+// device-scope load (written by another workgroup of the same kernel).
+__device__ inline int sel_at(const Args& a, const ListCtx& c, int i, bool coherent) {
+    const int32_t* p = a.sel + (size_t)c.u * a.top_k + i;
+    int v = coherent ? __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : *p;
+    return min(max(v, 0), max(c.n - 1, 0));
+}
+
 // Source rows of list position p (0 <= p < c.len): element offset of the row
 // in *kbase / *vbase.
 __device__ inline size_t list_row(const Args& a, int kind, const ListCtx& c, bool hier, int p,
-                                  const void** kbase, const void** vbase) {
+                                  const void** kbase, const void** vbase,
+                                  bool coherent = false) {
     const int C = a.C;
     if (kind == kListMeta) {
         *kbase = a.km;
@@ -101,18 +112,17 @@ __device__ inline size_t list_row(const Args& a, int kind, const ListCtx& c, boo
     } else if (kind == kListCand) {
         slot = cand_gist(a, c, p) * (C + 1) + C;
     } else {
-        const int32_t* sel = a.sel + (size_t)c.u * a.top_k;
         int raw = c.ns * C;
         if (p < raw) {
             int j = p / C;
-            slot = sel[j] * (C + 1) + (p - j * C);
+            slot = sel_at(a, c, j, coherent) * (C + 1) + (p - j * C);
         } else if (p < raw + c.tail) {
             slot = c.n * (C + 1) + (p - raw);
         } else {
             int q = p - raw - c.tail;
             int m;
-            if (!hier) m = sel[q];
-            else if (q < c.e1) m = sel[q];
+            if (!hier) m = sel_at(a, c, q, coherent);
+            else if (q < c.e1) m = sel_at(a, c, q, coherent);
             else m = c.nm * a.R + (q - c.e1);
             slot = m * (C + 1) + C;
         }

@@ -15,12 +15,19 @@
 
 namespace gsa {
 
-constexpr int kSelCache = 8192;  // keys kept in LDS; longer lists are re-read
+constexpr int kSelCache = 6144;   // general path: keys kept in LDS; longer lists are re-read
+constexpr int kSelFast = 8192;    // fast path: longest list
+
 
 template <int NT>
 struct SelectSmem {
-    uint32_t keys[kSelCache];
-    uint8_t flags[kSelCache];
+    union {
+        uint32_t keys[kSelCache];  // general path: order keys, then per-key flags
+        struct {
+            uint32_t selbits[kSelFast / 32];  // selected keys, one bit per index
+            uint32_t tiebits[kSelFast / 32];  // keys equal to the threshold
+        } f;
+    };
     int hist[2048];
     int wsum[NT / 64];
     int bstar, above, cnt;
@@ -57,23 +64,36 @@ __device__ inline int block_excl_scan(int x, int* total, int* wsum) {
     return base + incl - x;
 }
 
-// Top-k of keys[0..n) (ids[i] or i), written ascending to out[0..k) with -1
-// in unused slots.  Every thread of the block (NT threads) must call it.
-// Returns min(k, n).
+// General top-k: radix select over the whole key list, ordered output through
+// per-key flags.  Serves long lists and large k; block_topk below is the fast
+// path for the common shapes.
 template <int NT>
-__device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, int32_t* out,
-                          bool coherent, SelectSmem<NT>& sh) {
+__device__ int block_topk_general(const float* keys, const int32_t* ids, int n, int k, int32_t* out,
+                                  bool coherent, SelectSmem<NT>& sh) {
     const int tid = threadIdx.x;
     const int keff = min(k, n);
-    for (int i = keff + tid; i < k; i += NT) out[i] = -1;
+    auto put = [&](int i, int v) {
+        if (coherent) __hip_atomic_store(out + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else out[i] = v;
+    };
+    for (int i = keff + tid; i < k; i += NT) put(i, -1);
     if (keff == n) {
-        for (int i = tid; i < n; i += NT) out[i] = ids ? ids[i] : i;
+        for (int i = tid; i < n; i += NT) put(i, ids ? ids[i] : i);
         return keff;
     }
     if (keff == 0) return 0;
     const bool cached = n <= kSelCache;
-    if (cached)
-        for (int i = tid; i < n; i += NT) sh.keys[i] = order_key(load_key(keys + i, coherent));
+    if (cached) {
+        // eight loads in flight per thread
+        for (int i0 = tid; i0 < n; i0 += 8 * NT) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (i0 + j * NT < n) ? load_key(keys + i0 + j * NT, coherent) : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (i0 + j * NT < n) sh.keys[i0 + j * NT] = order_key(v[j]);
+        }
+    }
     __syncthreads();
     auto key_at = [&](int i) -> uint32_t {
         return cached ? sh.keys[i] : order_key(load_key(keys + i, coherent));
@@ -84,9 +104,8 @@ __device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, i
     int above = 0;         // keys above the current bucket range
     int fixed = 0;         // number of fixed high bits
     bool take_all = false;
-    const int widths[3] = {11, 11, 10};
     for (int pass = 0; pass < 3; ++pass) {
-        const int width = widths[pass];
+        const int width = pass < 2 ? 11 : 10;
         const int shift = 32 - fixed - width;
         const int nb = 1 << width;
         for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
@@ -141,14 +160,14 @@ __device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, i
     // flags: 1 = above the range, 2 = inside it
     auto flag_of = [&](uint32_t x) -> int { return x > hi ? 1 : (x >= lo ? 2 : 0); };
     if (cached) {
-        for (int i = tid; i < n; i += NT) sh.flags[i] = (uint8_t)flag_of(sh.keys[i]);
+        for (int i = tid; i < n; i += NT) sh.keys[i] = (uint32_t)flag_of(sh.keys[i]);
         __syncthreads();
     }
     const int per = (n + NT - 1) / NT;
     const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
     int c1 = 0, c2 = 0;
     for (int i = i0; i < i1; ++i) {
-        int f = cached ? sh.flags[i] : flag_of(key_at(i));
+        int f = cached ? (int)sh.keys[i] : flag_of(key_at(i));
         c1 += f == 1;
         c2 += f == 2;
     }
@@ -158,9 +177,170 @@ __device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, i
     int pos = block_excl_scan<NT>(c1 + take2, &tot, sh.wsum);
     int seen2 = 0;
     for (int i = i0; i < i1; ++i) {
-        int f = cached ? sh.flags[i] : flag_of(key_at(i));
+        int f = cached ? (int)sh.keys[i] : flag_of(key_at(i));
         bool s = f == 1 || (f == 2 && seen2++ < take2);
-        if (s) out[pos++] = ids ? ids[i] : i;
+        if (s) put(pos++, ids ? ids[i] : i);
+    }
+    __syncthreads();
+    return keff;
+}
+
+
+// Suffix scan of hist[0..nb) over the block: finds the bucket b* holding the
+// need-th largest key (need >= 1, at most the histogram total) and the count
+// of keys in buckets above it.  Results in sh.bstar / sh.above / sh.cnt.
+template <int NT>
+__device__ inline void find_bucket(int nb, int need, SelectSmem<NT>& sh) {
+    const int tid = threadIdx.x;
+    const int per = (nb + NT - 1) / NT;           // consecutive buckets per thread
+    int s = 0;
+    for (int j = 0; j < per; ++j) {
+        int bi = tid * per + j;
+        s += bi < nb ? sh.hist[bi] : 0;
+    }
+    // exclusive scan from the top: sum over higher threads
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_down(incl, off);
+        if (lane + off < 64) incl += y;
+    }
+    if (lane == 0) sh.wsum[w] = incl;  // wave total
+    __syncthreads();
+    int higher = incl - s;
+    for (int i = w + 1; i < NT / 64; ++i) higher += sh.wsum[i];
+    if (higher < need && higher + s >= need) {
+        int acc = higher;
+        for (int j = per - 1; j >= 0; --j) {
+            int bi = tid * per + j;
+            if (bi >= nb) continue;
+            int h = sh.hist[bi];
+            if (acc + h >= need) {
+                sh.bstar = bi;
+                sh.above = acc;
+                sh.cnt = h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    __syncthreads();
+}
+
+// Top-k of keys[0..n) (ids[i] or i), written ascending to out[0..k) with -1
+// in unused slots.  Every thread of the block (NT threads) must call it.
+// Returns min(k, n).  `coherent`: keys are read and out is written with
+// device-scope atomics (other workgroups of the kernel produce / consume them).
+//
+// Fast path (n <= kSelFast): radix select over keys held in registers (key
+// i = tid + j*NT in thread tid).  Passes histogram the digits [31:21],
+// [20:10], [9:0] of the keys that share the digits fixed so far and fix the
+// next digit of the k-th largest key T; a pass stops early when the keys above
+// a bucket boundary are exactly k.  Selected keys are marked in an LDS bitmap
+// (keys equal to T by their own bitmap, of which the lowest indices are
+// taken); a popcount scan of the bitmap then emits the selected ids in
+// ascending index order.  Longer lists use block_topk_general.
+template <int NT>
+__device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, int32_t* out,
+                          bool coherent, SelectSmem<NT>& sh) {
+    const int tid = threadIdx.x;
+    const int keff = min(k, n);
+    if (n > kSelFast || keff == n || keff == 0)
+        return block_topk_general<NT>(keys, ids, n, k, out, coherent, sh);
+    auto put = [&](int i, int v) {
+        if (coherent) __hip_atomic_store(out + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else out[i] = v;
+    };
+    for (int i = keff + tid; i < k; i += NT) put(i, -1);
+    constexpr int KPT = kSelFast / NT;
+    constexpr int WORDS = kSelFast / 32;
+    uint32_t kr[KPT];
+    {
+        float v[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            v[j] = (tid + j * NT < n) ? load_key(keys + tid + j * NT, coherent) : 0.f;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kr[j] = order_key(v[j]);
+    }
+    uint32_t prefix = 0;  // fixed high digits of T
+    int fixed = 0;        // number of fixed bits
+    int above = 0;        // keys above the current bucket range
+    bool take_all = false;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int width = pass < 2 ? 11 : 10;
+        const int shift = 32 - fixed - width;
+        const int nb = 1 << width;
+        for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool match = (tid + j * NT < n) &&
+                               (fixed == 0 || (kr[j] >> (32 - fixed)) == (prefix >> (32 - fixed)));
+            if (match) atomicAdd(&sh.hist[(kr[j] >> shift) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        find_bucket<NT>(nb, keff - above, sh);
+        above += sh.above;
+        prefix |= (uint32_t)sh.bstar << shift;
+        fixed += width;
+        const int cnt = sh.cnt;
+        __syncthreads();
+        if (above + cnt == keff) {
+            take_all = true;
+            break;
+        }
+    }
+    const uint32_t lo = prefix;
+    const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
+    const int need_eq = keff - above;  // keys to take from [lo, hi]
+
+    for (int i = tid; i < WORDS; i += NT) {
+        sh.f.selbits[i] = 0u;
+        sh.f.tiebits[i] = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = tid + j * NT;
+        if (i < n) {
+            const uint32_t x = kr[j];
+            if (x > hi || (take_all && x >= lo)) atomicOr(&sh.f.selbits[i >> 5], 1u << (i & 31));
+            else if (x >= lo) atomicOr(&sh.f.tiebits[i >> 5], 1u << (i & 31));
+        }
+    }
+    __syncthreads();
+    if (!take_all) {
+        // the need_eq lowest-index keys equal to T join the selection
+        const int wd = tid < WORDS ? tid : -1;
+        const uint32_t tb = wd >= 0 ? sh.f.tiebits[wd] : 0u;
+        int tot;
+        int before = block_excl_scan<NT>(__popc(tb), &tot, sh.wsum);
+        if (wd >= 0 && tb) {
+            uint32_t add = 0u, rest = tb;
+            while (rest && before < need_eq) {
+                const uint32_t bit = rest & (~rest + 1u);
+                add |= bit;
+                rest ^= bit;
+                ++before;
+            }
+            sh.f.selbits[wd] |= add;
+        }
+        __syncthreads();
+    }
+    // ascending output: popcount scan over the bitmap words
+    {
+        const int wd = tid < WORDS ? tid : -1;
+        uint32_t sb = wd >= 0 ? sh.f.selbits[wd] : 0u;
+        int tot;
+        int pos = block_excl_scan<NT>(__popc(sb), &tot, sh.wsum);
+        while (sb) {
+            const int bit = __ffs(sb) - 1;
+            sb &= sb - 1u;
+            const int i = wd * 32 + bit;
+            put(pos++, ids ? ids[i] : i);
+        }
     }
     __syncthreads();
     return keff;

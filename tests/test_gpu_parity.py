@@ -198,3 +198,24 @@ def test_hgsa_full_workload_sampled_units(gpu):
     GU.check_hgsa(inp, res, units=rng.sample(units, 4))
     del inp
     torch.cuda.empty_cache()
+
+
+def test_workspace_reuse_across_shapes(gpu):
+    """One zero-filled workspace shared by calls of different shapes and paths
+    (single-launch and multi-launch) in a row: the control block stays zero."""
+    say("[parity] workspace reuse across shapes")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=gpu)
+    cases = [("b2-g7-d128-c16", 0), ("b3-g4-d64-c8", gsa.GSA_PATH_PORTABLE),
+             ("b2-g16-d64-c4", 0), ("b3-g4-d64-c8", 0), ("b2-g7-d128-c16", 0)]
+    for i, (name, flags) in enumerate(cases):
+        wl = SMALL[name]
+        inp = gi.make_inputs(wl, 300 + i, seq_lens=lens_for(wl, "ragged", i))
+        g_inp = GU.to(inp, gpu)
+        k = wl.top_k
+        sel = torch.full((wl.batch, wl.num_kv_heads, k), -7, dtype=torch.int32, device=gpu)
+        out = gsa.gsa_decode(g_inp.q, g_inp.k_cache, g_inp.v_cache, g_inp.block_table,
+                             g_inp.seq_lens, num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                             page_chunks=wl.page_chunks, top_k=k, flags=flags, sel_idx=sel, ws=ws)
+        torch.cuda.synchronize()
+        GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None))
+        assert int(ws[:16384].count_nonzero()) == 0
