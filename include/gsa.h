@@ -123,9 +123,14 @@ typedef struct {
     int32_t top_k_meta;      /* k1 >= 0 meta-gists kept per (batch, kv-head) */
 } hgsa_meta_t;
 
+/* Size of the control block at the start of every workspace: work-queue
+ * counters and per-(batch, kv-head) routing-key histograms of the
+ * single-launch path. */
+#define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 8448)
+
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the
  * shapes are invalid).  The workspace must be 256-byte aligned and its first
- * 16 KiB (a control block of work-queue counters) must be zero before its
+ * GSA_WORKSPACE_CONTROL_BYTES (the control block) must be zero before its
  * first use; every call that completes leaves that block zero again and uses
  * the rest as scratch, so one zero-filled allocation serves any number of
  * sequential calls, of any shapes that fit it. */

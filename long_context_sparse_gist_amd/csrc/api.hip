@@ -16,10 +16,13 @@ constexpr int kMaxGroup = 16;
 constexpr long kMaxTopK = 1L << 20;
 constexpr int kVersion = 100;  // 0.1.0
 // Control block at the start of every workspace layout: the single-launch
-// kernel's counters, zero between calls.  No layout writes scratch data below
-// this offset, so reusing one workspace across shapes keeps it zero.
-constexpr size_t kCtlWords = 4096;
-constexpr long kMaxFusedUnits = (long)(kCtlWords - 8) / 3;
+// kernel's counters (first 16 KiB) and per-unit routing-key histograms, zero
+// between calls.  No layout writes scratch data below its end, so reusing one
+// workspace across shapes keeps it zero.
+constexpr size_t kCtlWords = GSA_WORKSPACE_CONTROL_BYTES / 4;
+constexpr size_t kHdrWords = 4096;  // header: error word
+constexpr long kMaxFusedUnits = 512;
+static_assert(kHdrWords + (size_t)kMaxFusedUnits * gsa::kUnitRec <= kCtlWords, "control block");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -35,7 +38,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        total;
+        off_spairs, off_rowoff, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -146,6 +149,10 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_cand = off;  off += align_up(sizeof(int32_t) * units * pl.cand_cap);
     pl.off_ml = off;    off += align_up(sizeof(float) * 2 * units * a.NS * a.G);
     pl.off_acc = off;   off += align_up(sizeof(float) * units * a.NS * a.G * a.D);
+    const size_t fslices = pl.fused ? (size_t)units * pl.S1 : 0;
+    pl.off_spairs = off; off += align_up(sizeof(uint64_t) * fslices * gsa::kFusedTA);
+    a.ro_stride = (int)(p->top_k < M ? p->top_k : M);
+    pl.off_rowoff = off; off += align_up(sizeof(int64_t) * (pl.fused ? units * a.ro_stride : 0));
     pl.total = off;
 }
 
@@ -228,9 +235,9 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     if (pl.fused) {
         unsigned* ctl = (unsigned*)(ws + pl.off_ctl);
         pl.sc.err = ctl + 2;
-        pl.sc.cntA = ctl + 8;
-        pl.sc.cntB = ctl + 8 + pl.sc.units;
-        pl.sc.ready = ctl + 8 + 2 * pl.sc.units;
+        a.urec = ctl + kHdrWords;
+        a.spairs = (uint64_t*)(ws + pl.off_spairs);
+        a.rowoff = (int64_t*)(ws + pl.off_rowoff);
         GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
         return GSA_OK;
     }

@@ -3,13 +3,15 @@
 // Workgroup t runs task t.  Tasks are numbered gist slices first (every unit,
 // unit-major), then unfolded-list tasks:
 //   gist slice (u, i)  scores gists [i*TA, (i+1)*TA) of unit u, writes their
-//                      routing keys and (all-gists set) one softmax partial.
-//                      The unit's last slice to finish runs its top-k select
-//                      and publishes the selection.
-//   unfolded (u, j)    waits for unit u's selection, attends tokens
+//                      routing keys, sorts them by the top 11 bits of their
+//                      order key (bucket) and publishes per-bucket suffix
+//                      counts, and (all-gists set) one softmax partial.  The
+//                      unit's last slice to finish runs the top-k select from
+//                      the slices' bucket counts and publishes the selection.
+//   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
+//                      select runs, waits for the selection, attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
-//                      the selected chunks, raw tail, selected gists), folds
-//                      gist-slice partials i = j, j+nB, ... into its own and
+//                      the selected chunks, raw tail, selected gists) and
 //                      writes one partial.  The unit's last one merges them
 //                      into the output and resets the unit's counters.
 // Only unfolded tasks wait, and only on gist-slice tasks, which have smaller
@@ -23,6 +25,17 @@
 // device-scope atomics (coherent across the XCDs' L2s); a producer waits for
 // its stores to complete before it bumps a counter or sets a flag, and the
 // unit's merging task returns the unit's counters to zero.
+//
+// Select.  A wavefront issues at most one instruction every few cycles, so a
+// single workgroup that touches every key of a unit several times is slow
+// (thousands of keys per wavefront).  The per-key work is done where the keys
+// are made instead: each slice (one key per thread) histograms its keys'
+// buckets, stores the inclusive suffix count of every bucket and scatters its
+// keys in descending bucket order.  The select then reads the suffix counts at
+// every 32nd bucket, then the 33 around the bucket holding the k-th largest
+// key, and gathers from each slice only the keys above that bucket (taken) and
+// inside it (candidates); two radix passes over the candidates' low 21 bits
+// fix the k-th largest key, ties go to the lower chunk index.
 #include "gsa_lists.h"
 #include "gsa_mfma_core.h"
 #include "gsa_select.h"
@@ -32,11 +45,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 24;
+constexpr int kFSelMaxSlices = 64;   // slices the bucketed select merges
+constexpr int kFSelMaxN = 16384;     // gists per unit the bucketed select handles
+constexpr int kFSelBt = 1024;        // block-table entries the select keeps in LDS
+constexpr int kFSelCand = 2048;      // largest boundary bucket (else the general select)
+constexpr int kFSelL = 32;           // keys per slice the select reads up front
 
 __device__ inline void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void st_dev(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int64_t* p, int64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline float ld_dev(const float* p) {
@@ -45,50 +72,98 @@ __device__ inline float ld_dev(const float* p) {
 __device__ inline unsigned ld_dev(const unsigned* p) {
     return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline int32_t ld_dev(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_dev(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int64_t ld_dev(const int64_t* p) {
+    return __hip_atomic_load(const_cast<int64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline unsigned add_dev(unsigned* p, unsigned v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // wait until this thread's memory operations have completed
 __device__ inline void drain() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Folding state of one partial: small per-head arrays (the G*D accumulator
-// lives in dynamic LDS next to it).
+// Thread 0 waits until *p >= target (bounded; giving up sets the error word).
+// The caller synchronises the block afterwards.  Polls are spaced out
+// (SLEEP * 64 cycles): hundreds of waiting workgroups polling a few counter
+// lines back to back load one memory channel enough to slow every other
+// access that maps to it.
+template <int SLEEP>
+__device__ inline void wait_at_least(const unsigned* p, unsigned target, unsigned* err) {
+    if (threadIdx.x != 0) return;
+    unsigned it = 0;
+    while (ld_dev(p) < target) {
+        __builtin_amdgcn_s_sleep(SLEEP);
+        if (++it >= kSpinLimit) {
+            st_dev(err, 1u);
+            break;
+        }
+    }
+}
+
+// Folding state of one partial: per-head running max (exp2 domain) and sum,
+// and the factors of the round being folded.
 constexpr int kFoldRound = 8;  // partials folded per round
 struct FoldHdr {
-    float m[16], l[16], f_self[16];
+    float m[16], l[16], f_self[16], fg[16], fb[16];
     float f[kFoldRound][16];
     float2 ml[kFoldRound][16];
 };
 
+// LDS of the top-k select (last gist slice of a unit).
+struct FSelSmem {
+    uint64_t selbits[kFSelMaxN / 64];  // selected chunk ids, one bit each
+    uint32_t tiebits[kFSelMaxN / 32];  // candidates equal to the k-th largest key
+    uint32_t ckey[kFSelCand];          // boundary-bucket candidates: order key, chunk id
+    int cidx[kFSelCand];
+    int hist[kBins];
+    int bt[kFSelBt];                   // the unit's block-table row
+    int need[kFSelMaxSlices];          // slice has boundary-bucket keys past its first kFSelL
+    int wsum[kThreads / 64];
+    int ncand, bstar, above, cnt;
+};
+
 // Dynamic LDS layout (bytes), uses separated in time:
-//   [0, vt)                          V transpose tiles (attention blocks)
-//   [0, red) [red, +acc) [.., +hdr)  wavefront combination, folding state
-//   [0, sel)                         top-k select (last gist slice of a unit)
+//   [0, vt)        V transpose tiles (attention blocks)
+//   [0, kBins*4+)  a slice's bucket histogram and staged keys
+//   [0, red)       wavefront combination
+//   [0, sel)       top-k select (last gist slice of a unit)
 struct Lds {
     static constexpr int vt(int D) { return 4 * (D * (32 + 4) * 2); }
     static constexpr int red(int G, int D) { return 4 * G * D * 4; }
-    static constexpr int acc_off(int G, int D) { return red(G, D); }
-    static constexpr int hdr_off(int G, int D) { return acc_off(G, D) + G * D * 4; }
-    static constexpr int sel() { return (int)sizeof(SelectSmem<kThreads>); }
     static int bytes(int G, int D) {
-        int a = vt(D), b = hdr_off(G, D) + (int)sizeof(FoldHdr), c = sel();
-        int m = a > b ? a : b;
-        return m > c ? m : c;
+        int m = vt(D);
+        m = m > red(G, D) ? m : red(G, D);
+        m = m > kBins * 4 + kFusedTA * 8 ? m : kBins * 4 + kFusedTA * 8;  // histogram, staged keys
+        m = m > (int)sizeof(FSelSmem) ? m : (int)sizeof(FSelSmem);
+        m = m > (int)sizeof(SelectSmem<kThreads>) ? m : (int)sizeof(SelectSmem<kThreads>);
+        return m;
     }
 };
 
-// Fold partial slots slot_of(0..ns) of unit u into (acc, hdr), eight per
-// round; within a round every load of a thread's element chunk is in flight
-// together.
-template <int D, typename SlotFn>
-__device__ void fold_slots(const Args& a, int u, SlotFn slot_of, int ns, float* acc, FoldHdr& fh) {
-    constexpr int EC = 4;  // elements per thread per chunk
-    const int G = a.G;
+// Fold partial slots slot_of(0..ns) of unit u into (acc, fh): acc[j] holds
+// element threadIdx.x + j*kThreads of the G x D accumulator.  Eight slots per
+// round, every load of a round in flight together.
+template <int EJ, typename SlotFn>
+__device__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&acc)[EJ], FoldHdr& fh) {
+    const int G = a.G, GD = a.G * a.D;
     const size_t base = (size_t)u * a.NS;
     for (int r0 = 0; r0 < ns; r0 += kFoldRound) {
         const int nr = min(kFoldRound, ns - r0);
-        for (int e = threadIdx.x; e < nr * G; e += kThreads) {
-            int i = e / G, h = e - i * G;
+        float v[EJ][kFoldRound];
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) {
+            const int e = threadIdx.x + j * kThreads;
+#pragma unroll
+            for (int i = 0; i < kFoldRound; ++i)
+                v[j][i] = (e < GD && i < nr) ? ld_dev(a.part_acc + (base + slot_of(r0 + i)) * GD + e) : 0.f;
+        }
+        if (threadIdx.x < (unsigned)(nr * G)) {
+            const int i = threadIdx.x / G, h = threadIdx.x - i * G;
             const float* p = (const float*)(a.part_ml + (base + slot_of(r0 + i)) * G + h);
             fh.ml[i][h] = make_float2(ld_dev(p), ld_dev(p + 1));
         }
@@ -97,10 +172,10 @@ __device__ void fold_slots(const Args& a, int u, SlotFn slot_of, int ns, float* 
             const int h = threadIdx.x;
             float M = fh.m[h];
             for (int i = 0; i < nr; ++i) M = fmaxf(M, fh.ml[i][h].x);
-            float fself = (fh.m[h] == -INFINITY) ? 0.f : exp2f(fh.m[h] - M);
+            const float fself = (fh.m[h] == -INFINITY) ? 0.f : exp2f(fh.m[h] - M);
             float L = fh.l[h] * fself;
             for (int i = 0; i < kFoldRound; ++i) {
-                float fi = (i >= nr || fh.ml[i][h].x == -INFINITY) ? 0.f : exp2f(fh.ml[i][h].x - M);
+                const float fi = (i >= nr || fh.ml[i][h].x == -INFINITY) ? 0.f : exp2f(fh.ml[i][h].x - M);
                 fh.f[i][h] = fi;
                 if (i < nr) L += fh.ml[i][h].y * fi;
             }
@@ -109,77 +184,290 @@ __device__ void fold_slots(const Args& a, int u, SlotFn slot_of, int ns, float* 
             fh.l[h] = L;
         }
         __syncthreads();
-        for (int e0 = threadIdx.x; e0 < G * D; e0 += EC * kThreads) {
-            float v[EC][kFoldRound];
 #pragma unroll
-            for (int j = 0; j < EC; ++j) {
-                const int e = e0 + j * kThreads;
+        for (int j = 0; j < EJ; ++j) {
+            const int e = threadIdx.x + j * kThreads;
+            if (e < GD) {
+                const int h = e / a.D;
+                float x = acc[j] * fh.f_self[h];
 #pragma unroll
-                for (int i = 0; i < kFoldRound; ++i)
-                    v[j][i] = (e < G * D && i < nr)
-                                  ? ld_dev(a.part_acc + (base + slot_of(r0 + i)) * G * D + e)
-                                  : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < EC; ++j) {
-                const int e = e0 + j * kThreads;
-                if (e < G * D) {
-                    const int h = e / D;
-                    float x = acc[e] * fh.f_self[h];
-#pragma unroll
-                    for (int i = 0; i < kFoldRound; ++i) x += v[j][i] * fh.f[i][h];
-                    acc[e] = x;
-                }
+                for (int i = 0; i < kFoldRound; ++i) x += v[j][i] * fh.f[i][h];
+                acc[j] = x;
             }
         }
         __syncthreads();
     }
 }
 
-__device__ inline void fold_init(float* acc, FoldHdr& fh, int G, int D) {
-    for (int e = threadIdx.x; e < G * D; e += kThreads) acc[e] = 0.f;
-    if (threadIdx.x < 16) {
-        fh.m[threadIdx.x] = -INFINITY;
-        fh.l[threadIdx.x] = 0.f;
+// Bucket sort of one slice's keys, one per thread: kv (the key) and pos (its
+// position in the slice, -1: none).  Adds the slice's bucket counts to the
+// unit's histogram and publishes its keys (order key | chunk id << 32) in
+// descending bucket order, staged in LDS and written as whole contiguous lines
+// (the stores write through to memory, and a partially written line costs the
+// memory a read-modify-write).
+__device__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
+                             unsigned char* smem, int* wsum) {
+    constexpr int PER = kBins / kThreads;  // consecutive buckets per thread
+    int* hist = (int*)smem;
+    uint64_t* pair_st = (uint64_t*)(smem + kBins * 4);  // kFusedTA pairs
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    const uint32_t ok = order_key(kv);
+    if (pos >= 0) atomicAdd(&hist[ok >> 21], 1);
+    __syncthreads();
+    int h[PER];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        h[i] = hist[PER * tid + i];
+        s += h[i];
     }
+    unsigned* H = unit_hist(a, u) + PER * tid;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (h[i]) __hip_atomic_fetch_add(H + i, (unsigned)h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int tot;
+    const int below = block_excl_scan<kThreads>(s, &tot, wsum);
+    int run = tot - below - s;  // keys in the buckets of higher threads
+    int cur[PER];
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+        cur[i] = run;  // keys in buckets above bucket PER*tid + i
+        run += h[i];
+    }
+    __syncthreads();  // histogram reads done
+#pragma unroll
+    for (int i = 0; i < PER; ++i) hist[PER * tid + i] = cur[i];
+    __syncthreads();
+    if (pos >= 0) {
+        const int at = atomicAdd(&hist[ok >> 21], 1);
+        pair_st[at] = (uint64_t)ok | ((uint64_t)(uint32_t)(p0 + pos) << 32);
+    }
+    __syncthreads();
+    static_assert(kFusedTA == kThreads, "one pair per thread");
+    if (tid < tot) st_dev(a.spairs + ((size_t)u * a.S1 + idx) * kFusedTA + tid, pair_st[tid]);
+    __syncthreads();
 }
 
-// One 32-token block per wavefront: wavefront w owns tokens [32w, 32w+32) of
-// the task.  off[t], ok[t]: element offset of this lane's K/V row (token
-// 16*t + lr) and whether that token is real.  Returns the scores through sc.
-template <int D>
-__device__ inline void wave_block(WaveAttn<D>& wa, const Args& a, const size_t* off, const bool* ok,
-                                  int nvalid, bool attn, int lr, int lg, __bf16* vt, f32x4_t sc[2]) {
-    constexpr int KK = WaveAttn<D>::KK;
-    // a token past the end reads q (valid memory); its score is masked out
-    const __bf16* kb[2];
-    const __bf16* vb[2];
+// Top-k of unit u (ascending chunk ids, -1 padded) and each selected chunk's
+// first-row offset.  nA: gist slices of the unit, keys: the routing keys.
+// Clears the unit's histogram.
+//
+// One round trip reads the histogram, the first kFSelL keys of every slice
+// (bucket-sorted, so they hold the slice's largest buckets) and the block-table
+// row.  The histogram gives the bucket b0 of the k-th largest key.  A slice
+// whose kFSelL-th key lies below b0 has all its keys of buckets >= b0 among
+// them; the rest of any other slice is read in a second round.  Keys above b0
+// are selected, keys in b0 are candidates for two radix passes over their low
+// 21 bits.
+__device__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
+                             unsigned char* smem) {
+    constexpr int PER = kBins / kThreads;
+    constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;  // up-front keys per thread
+    FSelSmem& sh = *(FSelSmem*)smem;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
+    int32_t* out = a.sel + (size_t)u * k;
+    int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
+    unsigned* H = unit_hist(a, u);
+    const uint64_t* pairs = a.spairs + (size_t)u * a.S1 * kFusedTA;
+    const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
+    const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
+    bool btl = fast && a.max_pages <= kFSelBt;
+    auto clear_hist = [&]() {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        kb[t] = ok[t] ? (const __bf16*)a.kc + off[t] : (const __bf16*)a.q;
-        vb[t] = ok[t] ? (const __bf16*)a.vc + off[t] : (const __bf16*)a.q;
+        for (int i = 0; i < PER; ++i) st_dev(H + PER * tid + i, 0u);
+    };
+    auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
+    // round trip 1
+    unsigned hv[PER];
+    uint64_t pv[KQ];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) hv[i] = ld_dev(H + PER * tid + i);
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+            pv[j] = (sl < nA && p < slice_n(sl)) ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
+        }
     }
-    bf16x8_t kA[2][KK], vA[2][KK];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(kb[t] + 32 * kk + 8 * lg);
-    if (attn) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) vA[t][kk] = *(const bf16x8_t*)(vb[t] + 32 * kk + 8 * lg);
+    if (btl)
+        for (int i = tid; i < a.max_pages; i += kThreads) sh.bt[i] = btrow[i];
+    auto row_of = [&](int m) -> int64_t {  // element offset of chunk m's first raw row
+        const int slot = m * (a.C + 1);
+        const int lp = slot / a.spp;
+        const int phys = btl ? sh.bt[lp] : btrow[lp];
+        return (((int64_t)phys * a.Hkv + c.g) * a.spp + (slot - lp * a.spp)) * a.D;
+    };
+    auto emit = [&](int pos, int m) {
+        st_dev(out + pos, (int32_t)m);
+        st_dev(ro + pos, row_of(m));
+    };
+    for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
+    if (!fast) clear_hist();
+    if (keff == 0) return;
+    if (keff == n) {
+        for (int i = tid; i < n; i += kThreads) emit(i, i);
+        return;
     }
-    wa.scores(kA, sc);
-    if (attn && nvalid > 0) {
-        bf16x8_t P = wa.softmax_stage(sc, vA, nvalid, a.tau_log2e, lr, lg, vt);
-        wa.pv_stage(P, lr, lg, vt);
+    bool general = !fast;
+    int b0 = 0, above0 = 0, cnt0 = 0;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sh.hist[PER * tid + i] = (int)hv[i];
+        for (int i = tid; i < kFSelMaxN / 64; i += kThreads) sh.selbits[i] = 0ull;
+        for (int i = tid; i < kFSelMaxN / 32; i += kThreads) sh.tiebits[i] = 0u;
+        if (tid < kFSelMaxSlices) sh.need[tid] = 0;
+        if (tid == 0) sh.ncand = 0;
+        __syncthreads();
+        clear_hist();  // its values are in LDS now
+        find_bucket<kThreads, kBins>(keff, sh);
+        b0 = sh.bstar;
+        above0 = sh.above;
+        cnt0 = sh.cnt;
+        general = cnt0 > kFSelCand;
+    }
+    if (general) {
+        // wide boundary bucket, long list or many slices: select over the keys
+        __syncthreads();
+        btl = false;  // the select reuses the LDS
+        SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
+        block_topk_general<kThreads>(keys, nullptr, n, k, out, true, ssh);
+        drain();
+        __syncthreads();
+        for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)));
+        return;
+    }
+    // classify one key: above b0 -> selected, in b0 -> candidate
+    auto take = [&](uint64_t pr, bool valid) {
+        const uint32_t key = (uint32_t)pr;
+        const int id = (int)(pr >> 32);
+        const uint32_t bk = key >> 21;
+        if (valid && bk > (uint32_t)b0)
+            atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+        const bool cand = valid && bk == (uint32_t)b0;
+        const uint64_t m = __ballot(cand);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(&sh.ncand, __popcll(m));
+        base = __shfl(base, 0);
+        const int ci = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (cand && ci < kFSelCand) {
+            sh.ckey[ci] = key;
+            sh.cidx[ci] = id;
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+        const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+        const bool valid = sl < nA && p < slice_n(sl);
+        take(pv[j], valid);
+        // the slice's last up-front key still in bucket >= b0: read the rest
+        if (valid && p == kFSelL - 1 && slice_n(sl) > kFSelL && ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
+            sh.need[sl] = 1;
+    }
+    __syncthreads();
+    // round trip 2 (only for slices whose boundary keys run past kFSelL)
+    for (int sl = 0; sl < nA; ++sl) {
+        if (!sh.need[sl]) continue;
+        const int ns = slice_n(sl);
+        for (int p0 = kFSelL; p0 < ns; p0 += kThreads) {
+            const int p = p0 + tid;
+            const uint64_t pr = p < ns ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
+            take(pr, p < ns);
+        }
+    }
+    __syncthreads();
+    // radix passes over the candidates' bits [20:10] and [9:0]
+    int above = above0;
+    uint32_t prefix = (uint32_t)b0 << 21;
+    int fixed = 11;
+    bool take_all = above + cnt0 == keff;
+    for (int pass = 1; pass < 3 && !take_all; ++pass) {
+        const int width = pass == 1 ? 11 : 10;
+        const int shift = 32 - fixed - width;
+        for (int i = tid; i < (1 << width); i += kThreads) sh.hist[i] = 0;
+        __syncthreads();
+        for (int ci = tid; ci < cnt0; ci += kThreads) {
+            const uint32_t x = sh.ckey[ci];
+            if ((x >> (32 - fixed)) == (prefix >> (32 - fixed)))
+                atomicAdd(&sh.hist[(x >> shift) & ((1u << width) - 1u)], 1);
+        }
+        __syncthreads();
+        if (pass == 1) find_bucket<kThreads, 2048>(keff - above, sh);
+        else find_bucket<kThreads, 1024>(keff - above, sh);
+        above += sh.above;
+        prefix |= (uint32_t)sh.bstar << shift;
+        fixed += width;
+        const int cnt = sh.cnt;
+        __syncthreads();
+        if (above + cnt == keff) take_all = true;
+    }
+    const uint32_t lo = prefix;
+    const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
+    for (int ci = tid; ci < cnt0; ci += kThreads) {
+        const uint32_t x = sh.ckey[ci];
+        const int id = sh.cidx[ci];
+        if (x > hi || (take_all && x >= lo))
+            atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+        else if (x >= lo)
+            atomicOr(&sh.tiebits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    constexpr int WPT = kFSelMaxN / 32 / kThreads;  // bitmap words per thread
+    const int nw = (n + 31) / 32;
+    if (!take_all) {
+        // the (keff - above) lowest-index keys equal to the k-th largest
+        const int need_eq = keff - above;
+        uint32_t tb[WPT];
+        int c1 = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int wd = WPT * tid + i;
+            tb[i] = wd < nw ? sh.tiebits[wd] : 0u;
+            c1 += __popc(tb[i]);
+        }
+        int tot;
+        int before = block_excl_scan<kThreads>(c1, &tot, sh.wsum);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            uint32_t add = 0u, rest = tb[i];
+            while (rest && before < need_eq) {
+                const uint32_t bit = rest & (~rest + 1u);
+                add |= bit;
+                rest ^= bit;
+                ++before;
+            }
+            const int wd = WPT * tid + i;
+            if (add) atomicOr((unsigned long long*)&sh.selbits[wd >> 1], (uint64_t)add << (32 * (wd & 1)));
+        }
+        __syncthreads();
+    }
+    // ascending output: popcount scan over the bitmap words
+    uint32_t sb[WPT];
+    int c2 = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        const int wd = WPT * tid + i;
+        sb[i] = wd < nw ? (uint32_t)(sh.selbits[wd >> 1] >> (32 * (wd & 1))) : 0u;
+        c2 += __popc(sb[i]);
+    }
+    int tot;
+    int pos = block_excl_scan<kThreads>(c2, &tot, sh.wsum);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        uint32_t x = sb[i];
+        while (x) {
+            const int bit = __ffs(x) - 1;
+            x &= x - 1u;
+            emit(pos++, (WPT * tid + i) * 32 + bit);
+        }
     }
 }
 
 template <int D>
 __device__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
-                           CombineSmem& cs, int* s_flag) {
+                           CombineSmem& cs, int* wsum, int* s_flag) {
     constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -236,10 +524,24 @@ __device__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsign
                             kt = 16 * t + 4 * lg + r;
                         }
                     }
-                if (kt >= 0 && kt < nval[j]) st_dev(keys + p0 + 32 * (w + 4 * j) + kt, kv);
+                // park the key in the unused columns 32..33 of row 32*j + kt of
+                // this wavefront's V tile (no global store here: a store
+                // in flight would hold up the next wait on this wavefront's
+                // loads)
+                if (kt >= 0 && kt < nval[j]) *(float*)(vt + (32 * j + kt) * (32 + 4) + 32) = kv;
             });
+        // thread t takes key slot t % 64 of wavefront t / 64 (NBW * 32 == 64 slots)
+        static_assert(NBW * 32 * 4 == kThreads, "one key slot per thread");
+        __syncthreads();
+        const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
+        const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
+        const float kv = kpos < cnt
+            ? *(const float*)((__bf16*)smem + (size_t)ws * (D * (32 + 4)) + slot * (32 + 4) + 32)
+            : 0.f;
+        if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
+        __syncthreads();  // the tiles are free
+        bucket_slice(a, u, idx, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
         if (attn) {
-            __syncthreads();
             const size_t pbase = ((size_t)u * a.NS + idx) * G;
             combine_waves<D>(
                 wa, a.tau_log2e, G, (float*)smem, cs,
@@ -253,140 +555,214 @@ __device__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsign
     }
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) *s_flag = add_dev(s.cntA + u, 1u) == (unsigned)(nA - 1);
+    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntA(a, u), 1u) == (unsigned)(nA - 1);
     __syncthreads();
     if (!*s_flag) return;
 
     // last slice of the unit: select and publish
     for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
-    block_topk<kThreads>(keys, nullptr, c.n, a.top_k, a.sel + (size_t)u * a.top_k, true, ssh);
+    select_fused(a, c, nA, keys, smem);
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) st_dev(s.ready + u, 1u);
+    if (threadIdx.x == 0) st_dev(unit_ready(a, u), 1u);
 }
 
-template <int D>
+// Combine the 4 wavefronts' online-softmax states with the folded gist state
+// (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u.
+template <int D, int EJ>
+__device__ void combine_publish(WaveAttn<D>& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
+                                FoldHdr& fh, float* red, CombineSmem& cs) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int G = a.G, GD = a.G * D;
+    const float tl = a.tau_log2e;
+    float l = wa.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lg == 0) {
+        cs.wm[w][lr] = wa.m;
+        cs.wl[w][lr] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * lg + r;
+        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
+        const float sc = (cs.wm[w][h] == -INFINITY) ? 0.f : exp2f((cs.wm[w][h] - M) * tl);
+        if (h < G) {
+#pragma unroll
+            for (int db = 0; db < WaveAttn<D>::DB; ++db)
+                red[((size_t)w * G + h) * D + 16 * db + lr] = wa.o[db][r] * sc;
+        }
+    }
+    const size_t pbase = ((size_t)u * a.NS + slot) * G;
+    if (threadIdx.x < (unsigned)G) {
+        const int h = threadIdx.x;
+        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
+        float Lb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (cs.wm[i][h] != -INFINITY) Lb += cs.wl[i][h] * exp2f((cs.wm[i][h] - M) * tl);
+        const float mb = M == -INFINITY ? -INFINITY : M * tl;
+        const float Mt = fmaxf(fh.m[h], mb);
+        const float fg = fh.m[h] == -INFINITY ? 0.f : exp2f(fh.m[h] - Mt);
+        const float fb = mb == -INFINITY ? 0.f : exp2f(mb - Mt);
+        fh.fg[h] = fg;
+        fh.fb[h] = fb;
+        float* p = (float*)(a.part_ml + pbase + h);
+        st_dev(p, Mt);
+        st_dev(p + 1, fh.l[h] * fg + Lb * fb);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+        const int e = threadIdx.x + j * kThreads;
+        if (e < GD) {
+            const int h = e / D, d = e - h * D;
+            const float bs = red[(size_t)h * D + d] + red[((size_t)G + h) * D + d] +
+                             red[((size_t)2 * G + h) * D + d] + red[((size_t)3 * G + h) * D + d];
+            st_dev(a.part_acc + pbase * D + e, gacc[j] * fh.fg[h] + bs * fh.fb[h]);
+        }
+    }
+}
+
+// EJ: accumulator elements per thread, EJ * kThreads >= G * D.
+template <int D, int EJ>
 __device__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
-                              CombineSmem& cs, int* s_flag) {
-    const int G = a.G;
-    float* facc = (float*)(smem + Lds::acc_off(G, D));
-    FoldHdr& fh = *(FoldHdr*)(smem + Lds::hdr_off(G, D));
+                              CombineSmem& cs, FoldHdr& fh, int* s_flag) {
+    const int G = a.G, C = a.C;
     ListCtx c;
     make_ctx(a, kListUnfolded, u, false, c);
     const int nB = max(1, (c.len + s.TB - 1) / s.TB);
     if (idx >= nB) return;
-    // wait for the unit's selection
-    if (threadIdx.x == 0) {
-        unsigned it = 0;
-        while (ld_dev(s.ready + u) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++it >= kSpinLimit) {
-                st_dev(s.err, 1u);
-                break;
-            }
-        }
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int p0 = idx * s.TB;
     const int cnt = max(0, min(s.TB, c.len - p0));
-
-    if (cnt == 0) fold_init(facc, fh, G, D);
-    if (cnt > 0) {
-        constexpr int NBW = kFusedTB / 128;
-        const int nblk = (cnt + 31) / 32;
-        const int nbw = nblk > w ? (nblk - w + 3) / 4 : 0;
-        size_t off[NBW][2];
-        int nval[NBW];
+    const int raw = c.ns * C;
+    // first raw-tail row (the tail lies in one page): known before the selection
+    const int64_t tail_off = c.tail > 0 ? (int64_t)slot_offset(a, c.b, c.g, c.n * (C + 1)) : 0;
+    // fold the gist-slice partials idx, idx + nB, ... once every slice is done
+    const bool attn = !(a.flags & kFlagSelectedGists);
+    const int nAt = max(1, (c.n + s.TA - 1) / s.TA);   // gist-slice tasks of the unit
+    const int nA = attn ? (c.n + s.TA - 1) / s.TA : 0;  // slices that wrote a partial
+    const int nf = idx < nA ? (nA - idx + nB - 1) / nB : 0;
+    float gacc[EJ];
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            nval[j] = max(0, min(32, cnt - 32 * (w + 4 * j)));
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                // a token past the end reads the task's first row (in range)
-                int rel = 32 * (w + 4 * j) + 16 * t + lr;
-                const void *kb, *vb;
-                off[j][t] = list_row(a, kListUnfolded, c, false, p0 + (rel < cnt ? rel : 0), &kb, &vb,
-                                     true);
-            }
-        }
-        WaveAttn<D> wa;
-        wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
-        __bf16* vt = (__bf16*)smem + (size_t)w * (D * (32 + 4));
-        wa.template stream<NBW, false>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, true,
-                                a.tau_log2e, lr, lg, vt, [](int, const f32x4_t*) {});
+    for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
+    if (threadIdx.x < 16) {
+        fh.m[threadIdx.x] = -INFINITY;
+        fh.l[threadIdx.x] = 0.f;
+    }
+    if (nf > 0) {
+        wait_at_least<32>(unit_cntA(a, u), (unsigned)nAt, s.err);
         __syncthreads();
-        combine_waves<D>(
-            wa, a.tau_log2e, G, (float*)smem, cs, [&](int h, int d, float v) { facc[h * D + d] = v; },
-            [&](int h, float m2, float l) {
-                fh.m[h] = m2;
-                fh.l[h] = l;
-            });
+        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf, gacc, fh);
+    }
+    wait_at_least<8>(unit_ready(a, u), 1u, s.err);
+    __syncthreads();
+    WaveAttn<D> wa;
+    wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
+    if (cnt > 0) {
+        const int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
+        size_t off[1][2];
+        int nval[1];
+        nval[0] = max(0, min(32, cnt - 32 * w));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // a token past the end reads the task's first row (in range)
+            const int rel = 32 * w + 16 * t + lr;
+            const int p = p0 + (rel < cnt ? rel : 0);
+            int64_t o;
+            if (p < raw) {
+                const int j = p / C;
+                o = ld_dev(ro + j) + (int64_t)(p - j * C) * D;
+            } else if (p < raw + c.tail) {
+                o = tail_off + (int64_t)(p - raw) * D;
+            } else {
+                o = ld_dev(ro + (p - raw - c.tail)) + (int64_t)C * D;
+            }
+            off[0][t] = (size_t)o;
+        }
+        __bf16* vt = (__bf16*)smem + (size_t)w * (D * (32 + 4));
+        wa.template stream<1, false>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
+                                     nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, vt,
+                                     [](int, const f32x4_t*) {});
     }
     __syncthreads();
-    // fold the gist-slice partials i = idx, idx + nB, ...
-    const bool attn = !(a.flags & kFlagSelectedGists);
-    const int nA = attn ? (c.n + s.TA - 1) / s.TA : 0;
-    const int nf = idx < nA ? (nA - idx + nB - 1) / nB : 0;
-    if (nf) fold_slots<D>(a, u, [&](int i) { return idx + i * nB; }, nf, facc, fh);
-    // publish this task's partial
-    const size_t pbase = ((size_t)u * a.NS + s.S1 + idx) * G;
-    for (int e = threadIdx.x; e < G * D; e += kThreads) st_dev(a.part_acc + pbase * D + e, facc[e]);
-    if (threadIdx.x < (unsigned)G) {
-        float* p = (float*)(a.part_ml + pbase + threadIdx.x);
-        st_dev(p, fh.m[threadIdx.x]);
-        st_dev(p + 1, fh.l[threadIdx.x]);
-    }
+    combine_publish<D, EJ>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) *s_flag = add_dev(s.cntB + u, 1u) == (unsigned)(nB - 1);
+    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntB(a, u), 1u) == (unsigned)(nB - 1);
     __syncthreads();
     if (!*s_flag) return;
 
     // last unfolded task of the unit: merge and reset the unit's counters
-    fold_init(facc, fh, G, D);
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
+    if (threadIdx.x < 16) {
+        fh.m[threadIdx.x] = -INFINITY;
+        fh.l[threadIdx.x] = 0.f;
+    }
     __syncthreads();
-    fold_slots<D>(a, u, [&](int i) { return s.S1 + i; }, nB, facc, fh);
+    fold_regs<EJ>(a, u, [&](int i) { return s.S1 + i; }, nB, gacc, fh);
     __bf16* out = (__bf16*)a.out + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D;
-    for (int e = threadIdx.x; e < G * D; e += kThreads) {
-        const int h = e / D;
-        float L = fh.l[h];
-        out[e] = (__bf16)((fh.m[h] == -INFINITY || L == 0.f) ? 0.f : facc[e] / L);
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+        const int e = threadIdx.x + j * kThreads;
+        if (e < G * D) {
+            const int h = e / D;
+            const float L = fh.l[h];
+            out[e] = (__bf16)((fh.m[h] == -INFINITY || L == 0.f) ? 0.f : gacc[j] / L);
+        }
     }
     if (threadIdx.x == 0) {
-        st_dev(s.cntA + u, 0u);
-        st_dev(s.cntB + u, 0u);
-        st_dev(s.ready + u, 0u);
+        st_dev(unit_cntA(a, u), 0u);
+        st_dev(unit_cntB(a, u), 0u);
+        st_dev(unit_ready(a, u), 0u);
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s) {
+template <int D, int EJ>
+__global__ __launch_bounds__(kThreads, 3) void gsa_fused_kernel(Args a, Sched s) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ CombineSmem cs;
+    __shared__ FoldHdr fh;
+    __shared__ int wsum[kThreads / 64];
     __shared__ int s_flag;
     const int nA = s.units * s.S1;
     const int t = blockIdx.x;
     if (t < nA) {
         const int u = t / s.S1;
-        task_gists<D>(a, s, u, t - u * s.S1, smem, cs, &s_flag);
+        task_gists<D>(a, s, u, t - u * s.S1, smem, cs, wsum, &s_flag);
     } else {
         const int u = (t - nA) / s.S2;
-        task_unfolded<D>(a, s, u, t - nA - u * s.S2, smem, cs, &s_flag);
+        task_unfolded<D, EJ>(a, s, u, t - nA - u * s.S2, smem, cs, fh, &s_flag);
     }
 }
 
 }  // namespace
 
+namespace {
+template <int D, int EJ>
+void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
+    hipLaunchKernelGGL((gsa_fused_kernel<D, EJ>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+}
+}  // namespace
+
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st) {
     const int lds = Lds::bytes(a.G, a.D);
-    dim3 grid(s.total);
-    if (a.D == 64)
-        hipLaunchKernelGGL((gsa_fused_kernel<64>), grid, dim3(kThreads), lds, st, a, s);
-    else
-        hipLaunchKernelGGL((gsa_fused_kernel<128>), grid, dim3(kThreads), lds, st, a, s);
+    const int ej = (a.G * a.D + kThreads - 1) / kThreads;  // 1 .. 8
+    if (a.D == 64) {
+        if (ej <= 1) launch_fused_t<64, 1>(a, s, lds, st);
+        else if (ej <= 2) launch_fused_t<64, 2>(a, s, lds, st);
+        else launch_fused_t<64, 4>(a, s, lds, st);
+    } else {
+        if (ej <= 1) launch_fused_t<128, 1>(a, s, lds, st);
+        else if (ej <= 2) launch_fused_t<128, 2>(a, s, lds, st);
+        else if (ej <= 4) launch_fused_t<128, 4>(a, s, lds, st);
+        else launch_fused_t<128, 8>(a, s, lds, st);
+    }
     return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@ struct Args {
     int S1;           // token-list splits of the "all gists" / meta list
     int SL;           // tokens per split of that list
     int SR;           // tokens per split of the unfolded list
+    // single-launch path only
+    unsigned* urec;   // [units][kUnitRec] per-unit control records, zero between calls
+    uint64_t* spairs; // [units][S1][kFusedTA] slice keys by bucket: order key | id << 32
+    int64_t* rowoff;  // [units][ro_stride] element offset of each selected chunk's first row
+    int ro_stride;    // min(top_k, num_chunks)
     void* out;        // [B][Hq][D]
 };
 
@@ -98,9 +103,6 @@ int portable_tokens_per_block();
 // Work-queue state and geometry of the single-launch kernel.  The counters
 // live in the caller's workspace and are zero between calls.
 struct Sched {
-    unsigned* cntA;    // [units] finished gist-slice tasks
-    unsigned* cntB;    // [units] finished unfolded tasks
-    unsigned* ready;   // [units] selection published
     unsigned* err;     // set if a wait gave up (never expected)
     int units;
     int S1, S2;        // task slots per unit (capacity)
@@ -109,7 +111,17 @@ struct Sched {
 };
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
-constexpr int kFusedTB = 256;  // tokens per unfolded task
+constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
+constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
+// Control record of one unit (words): the routing-key histogram, then the
+// counters, each in a 64-byte sector of its own.  Records are over 8 KiB
+// apart, so the counters that waiting workgroups poll spread over memory
+// channels instead of queueing on one.
+constexpr int kUnitRec = kBins + 64;
+__device__ inline unsigned* unit_hist(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }
+__device__ inline unsigned* unit_cntA(const Args& a, int u) { return unit_hist(a, u) + kBins; }       // finished gist slices
+__device__ inline unsigned* unit_cntB(const Args& a, int u) { return unit_hist(a, u) + kBins + 16; }  // finished unfolded tasks
+__device__ inline unsigned* unit_ready(const Args& a, int u) { return unit_hist(a, u) + kBins + 32; } // selection published
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);

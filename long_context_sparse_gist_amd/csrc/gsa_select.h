@@ -17,6 +17,7 @@ namespace gsa {
 
 constexpr int kSelCache = 6144;   // general path: keys kept in LDS; longer lists are re-read
 constexpr int kSelFast = 8192;    // fast path: longest list
+constexpr int kSelCandCap = 2048;    // fast path: largest boundary bucket
 
 
 template <int NT>
@@ -24,12 +25,15 @@ struct SelectSmem {
     union {
         uint32_t keys[kSelCache];  // general path: order keys, then per-key flags
         struct {
-            uint32_t selbits[kSelFast / 32];  // selected keys, one bit per index
+            uint64_t selbits[kSelFast / 64];  // selected keys, one bit per index
             uint32_t tiebits[kSelFast / 32];  // keys equal to the threshold
+            uint32_t ckey[kSelCandCap];          // boundary-bucket candidates
+            int cidx[kSelCandCap];
         } f;
     };
     int hist[2048];
     int wsum[NT / 64];
+    int wcnt[NT / 64];
     int bstar, above, cnt;
 };
 
@@ -186,17 +190,20 @@ __device__ int block_topk_general(const float* keys, const int32_t* ids, int n, 
 }
 
 
-// Suffix scan of hist[0..nb) over the block: finds the bucket b* holding the
+// Suffix scan of hist[0..NB) over the block: finds the bucket b* holding the
 // need-th largest key (need >= 1, at most the histogram total) and the count
 // of keys in buckets above it.  Results in sh.bstar / sh.above / sh.cnt.
-template <int NT>
-__device__ inline void find_bucket(int nb, int need, SelectSmem<NT>& sh) {
+template <int NT, int NB, typename Smem>
+__device__ inline void find_bucket(int need, Smem& sh) {
+    constexpr int PER = (NB + NT - 1) / NT;  // consecutive buckets per thread
     const int tid = threadIdx.x;
-    const int per = (nb + NT - 1) / NT;           // consecutive buckets per thread
+    int h[PER];
     int s = 0;
-    for (int j = 0; j < per; ++j) {
-        int bi = tid * per + j;
-        s += bi < nb ? sh.hist[bi] : 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int bi = tid * PER + j;
+        h[j] = bi < NB ? sh.hist[bi] : 0;
+        s += h[j];
     }
     // exclusive scan from the top: sum over higher threads
     const int lane = tid & 63, w = tid >> 6;
@@ -209,20 +216,20 @@ __device__ inline void find_bucket(int nb, int need, SelectSmem<NT>& sh) {
     if (lane == 0) sh.wsum[w] = incl;  // wave total
     __syncthreads();
     int higher = incl - s;
-    for (int i = w + 1; i < NT / 64; ++i) higher += sh.wsum[i];
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) higher += i > w ? sh.wsum[i] : 0;
     if (higher < need && higher + s >= need) {
         int acc = higher;
-        for (int j = per - 1; j >= 0; --j) {
-            int bi = tid * per + j;
-            if (bi >= nb) continue;
-            int h = sh.hist[bi];
-            if (acc + h >= need) {
-                sh.bstar = bi;
+        bool found = false;
+#pragma unroll
+        for (int j = PER - 1; j >= 0; --j) {
+            if (!found && acc + h[j] >= need) {
+                found = true;
+                sh.bstar = tid * PER + j;
                 sh.above = acc;
-                sh.cnt = h;
-                break;
+                sh.cnt = h[j];
             }
-            acc += h;
+            acc += h[j];
         }
     }
     __syncthreads();
@@ -233,26 +240,26 @@ __device__ inline void find_bucket(int nb, int need, SelectSmem<NT>& sh) {
 // Returns min(k, n).  `coherent`: keys are read and out is written with
 // device-scope atomics (other workgroups of the kernel produce / consume them).
 //
-// Fast path (n <= kSelFast): radix select over keys held in registers (key
-// i = tid + j*NT in thread tid).  Passes histogram the digits [31:21],
-// [20:10], [9:0] of the keys that share the digits fixed so far and fix the
-// next digit of the k-th largest key T; a pass stops early when the keys above
-// a bucket boundary are exactly k.  Selected keys are marked in an LDS bitmap
-// (keys equal to T by their own bitmap, of which the lowest indices are
-// taken); a popcount scan of the bitmap then emits the selected ids in
-// ascending index order.  Longer lists use block_topk_general.
+// Fast path (n <= kSelFast): keys sit in registers (key i = tid + j*NT in
+// thread tid, so one wavefront's j-th keys are 64 consecutive indices).
+//   1. histogram of the top 11 bits of every key; bucket b0 holds the k-th
+//      largest key.
+//   2. keys above b0 are marked in the selection bitmap (one ballot per
+//      wavefront and j, no atomics); keys in b0 are compacted into an LDS
+//      candidate list (longer buckets: general path).
+//   3. radix passes over the candidates' bits [20:10] and [9:0] fix the k-th
+//      largest key T; candidates above T join the bitmap, those equal to T go
+//      to a tie bitmap of which the lowest indices are taken.
+//   4. a popcount scan of the bitmap emits the ids in ascending index order.
+// A pass whose boundary bucket is taken whole ends the search early.
 template <int NT>
 __device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, int32_t* out,
                           bool coherent, SelectSmem<NT>& sh) {
     const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int keff = min(k, n);
     if (n > kSelFast || keff == n || keff == 0)
         return block_topk_general<NT>(keys, ids, n, k, out, coherent, sh);
-    auto put = [&](int i, int v) {
-        if (coherent) __hip_atomic_store(out + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else out[i] = v;
-    };
-    for (int i = keff + tid; i < k; i += NT) put(i, -1);
     constexpr int KPT = kSelFast / NT;
     constexpr int WORDS = kSelFast / 32;
     uint32_t kr[KPT];
@@ -264,75 +271,122 @@ __device__ int block_topk(const float* keys, const int32_t* ids, int n, int k, i
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kr[j] = order_key(v[j]);
     }
-    uint32_t prefix = 0;  // fixed high digits of T
-    int fixed = 0;        // number of fixed bits
-    int above = 0;        // keys above the current bucket range
-    bool take_all = false;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int width = pass < 2 ? 11 : 10;
-        const int shift = 32 - fixed - width;
-        const int nb = 1 << width;
-        for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const bool match = (tid + j * NT < n) &&
-                               (fixed == 0 || (kr[j] >> (32 - fixed)) == (prefix >> (32 - fixed)));
-            if (match) atomicAdd(&sh.hist[(kr[j] >> shift) & (nb - 1)], 1);
-        }
-        __syncthreads();
-        find_bucket<NT>(nb, keff - above, sh);
-        above += sh.above;
-        prefix |= (uint32_t)sh.bstar << shift;
-        fixed += width;
-        const int cnt = sh.cnt;
-        __syncthreads();
-        if (above + cnt == keff) {
-            take_all = true;
-            break;
-        }
-    }
-    const uint32_t lo = prefix;
-    const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
-    const int need_eq = keff - above;  // keys to take from [lo, hi]
-
-    for (int i = tid; i < WORDS; i += NT) {
-        sh.f.selbits[i] = 0u;
-        sh.f.tiebits[i] = 0u;
-    }
+    // 1. top-digit histogram
+    for (int i = tid; i < 2048; i += NT) sh.hist[i] = 0;
+    for (int i = tid; i < WORDS; i += NT) sh.f.tiebits[i] = 0u;
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (tid + j * NT < n) atomicAdd(&sh.hist[kr[j] >> 21], 1);
+    __syncthreads();
+    find_bucket<NT, 2048>(keff, sh);
+    const uint32_t b0 = (uint32_t)sh.bstar;
+    int above = sh.above;
+    const int cnt0 = sh.cnt;
+    if (cnt0 > kSelCandCap) {
+        // boundary bucket too long for the candidate list
+        __syncthreads();
+        return block_topk_general<NT>(keys, ids, n, k, out, coherent, sh);
+    }
+    const bool all0 = above + cnt0 == keff;
+    // 2. classify: bitmap words by ballot, candidate count per wavefront
+    int nmine = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        const int i = tid + j * NT;
-        if (i < n) {
-            const uint32_t x = kr[j];
-            if (x > hi || (take_all && x >= lo)) atomicOr(&sh.f.selbits[i >> 5], 1u << (i & 31));
-            else if (x >= lo) atomicOr(&sh.f.tiebits[i >> 5], 1u << (i & 31));
+        const bool valid = tid + j * NT < n;
+        const uint32_t top = kr[j] >> 21;
+        const uint64_t sel = __ballot(valid && (top > b0 || (all0 && top == b0)));
+        if (lane == 0) sh.f.selbits[(j * NT + 64 * w) >> 6] = sel;
+        nmine += __popcll(__ballot(valid && !all0 && top == b0));
+    }
+    if (!all0) {
+        if (lane == 0) sh.wcnt[w] = nmine;
+        __syncthreads();
+        int pos = 0;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) pos += i < w ? sh.wcnt[i] : 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool eq = tid + j * NT < n && (kr[j] >> 21) == b0;
+            const uint64_t m = __ballot(eq);
+            if (eq) {
+                const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+                sh.f.ckey[at] = kr[j];
+                sh.f.cidx[at] = tid + j * NT;
+            }
+            pos += __popcll(m);
         }
     }
     __syncthreads();
-    if (!take_all) {
-        // the need_eq lowest-index keys equal to T join the selection
-        const int wd = tid < WORDS ? tid : -1;
-        const uint32_t tb = wd >= 0 ? sh.f.tiebits[wd] : 0u;
-        int tot;
-        int before = block_excl_scan<NT>(__popc(tb), &tot, sh.wsum);
-        if (wd >= 0 && tb) {
-            uint32_t add = 0u, rest = tb;
-            while (rest && before < need_eq) {
-                const uint32_t bit = rest & (~rest + 1u);
-                add |= bit;
-                rest ^= bit;
-                ++before;
+    if (!all0) {
+        // 3. radix passes over the candidates
+        uint32_t prefix = b0 << 21;
+        int fixed = 11;
+        bool take_all = false;
+#pragma unroll
+        for (int pass = 1; pass < 3; ++pass) {
+            const int width = pass == 1 ? 11 : 10;
+            const int shift = 32 - fixed - width;
+            for (int i = tid; i < (1 << width); i += NT) sh.hist[i] = 0;
+            __syncthreads();
+            for (int c = tid; c < cnt0; c += NT) {
+                const uint32_t x = sh.f.ckey[c];
+                if ((x >> (32 - fixed)) == (prefix >> (32 - fixed)))
+                    atomicAdd(&sh.hist[(x >> shift) & ((1 << width) - 1)], 1);
             }
-            sh.f.selbits[wd] |= add;
+            __syncthreads();
+            if (pass == 1) find_bucket<NT, 2048>(keff - above, sh);
+            else find_bucket<NT, 1024>(keff - above, sh);
+            above += sh.above;
+            prefix |= (uint32_t)sh.bstar << shift;
+            fixed += width;
+            const int cnt = sh.cnt;
+            __syncthreads();
+            if (above + cnt == keff) {
+                take_all = true;
+                break;
+            }
+        }
+        const uint32_t lo = prefix;
+        const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
+        for (int c = tid; c < cnt0; c += NT) {
+            const uint32_t x = sh.f.ckey[c];
+            const int i = sh.f.cidx[c];
+            if (x > hi || (take_all && x >= lo))
+                atomicOr((unsigned long long*)&sh.f.selbits[i >> 6], 1ull << (i & 63));
+            else if (x >= lo)
+                atomicOr(&sh.f.tiebits[i >> 5], 1u << (i & 31));
         }
         __syncthreads();
+        if (!take_all) {
+            // the (keff - above) lowest-index keys equal to T join the selection
+            const int need_eq = keff - above;
+            const int wd = tid < WORDS ? tid : -1;
+            const uint32_t tb = wd >= 0 ? sh.f.tiebits[wd] : 0u;
+            int tot;
+            int before = block_excl_scan<NT>(__popc(tb), &tot, sh.wsum);
+            if (wd >= 0 && tb) {
+                uint32_t add = 0u, rest = tb;
+                while (rest && before < need_eq) {
+                    const uint32_t bit = rest & (~rest + 1u);
+                    add |= bit;
+                    rest ^= bit;
+                    ++before;
+                }
+                if (add) atomicOr((unsigned long long*)&sh.f.selbits[wd >> 1], (uint64_t)add << (32 * (wd & 1)));
+            }
+            __syncthreads();
+        }
     }
-    // ascending output: popcount scan over the bitmap words
+    // 4. ascending output: popcount scan over the bitmap words
+    auto put = [&](int i, int v) {
+        if (coherent) __hip_atomic_store(out + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else out[i] = v;
+    };
+    for (int i = keff + tid; i < k; i += NT) put(i, -1);
     {
         const int wd = tid < WORDS ? tid : -1;
-        uint32_t sb = wd >= 0 ? sh.f.selbits[wd] : 0u;
+        uint32_t sb = wd >= 0 ? (uint32_t)(sh.f.selbits[wd >> 1] >> (32 * (wd & 1))) : 0u;
         int tot;
         int pos = block_excl_scan<NT>(__popc(sb), &tot, sh.wsum);
         while (sb) {

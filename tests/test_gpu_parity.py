@@ -218,4 +218,4 @@ def test_workspace_reuse_across_shapes(gpu):
                              page_chunks=wl.page_chunks, top_k=k, flags=flags, sel_idx=sel, ws=ws)
         torch.cuda.synchronize()
         GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None))
-        assert int(ws[:16384].count_nonzero()) == 0
+        assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
