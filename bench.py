@@ -26,6 +26,34 @@ import long_context_sparse_gist_amd as gsa
 from long_context_sparse_gist_amd import inputs as gi
 
 HBM_PEAK_GBPS = 8000.0
+METRIC = "GSA decode queries/sec (batch\u00d7q-heads) and achieved HBM GB/s vs peak at 128K ctx"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL = "gsa_fused_kernel"
+# sources of the single-launch kernel: measured HBM traffic is reported only
+# while they are unchanged since the counters were taken
+KERNEL_SOURCES = ["fused.hip", "gsa_internal.h", "gsa_lists.h", "gsa_mfma_core.h", "gsa_select.h"]
+
+
+def kernel_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_gist_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter profile of this
+    workload, or None if it is missing or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t["bytes_per_launch"]
 
 
 def alg_bytes(wl: gi.Workload) -> int:
@@ -53,6 +81,9 @@ def parse():
                     help="cache copies rotated between calls (defeats the Infinity Cache)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="before timing, run 5 plain device copies of this many bytes "
+                         "(the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -109,34 +140,61 @@ def main():
     out = torch.empty_like(inp.q)
     stream = torch.cuda.current_stream(dev)
 
-    def step(c):
+    # one prepared call per cache copy: arguments are marshalled once, so the
+    # host enqueues faster than the device runs a call
+    def prepare(c):
         if wl.hgsa:
-            gsa.hgsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.k_meta,
-                            c.v_meta, num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
-                            page_chunks=wl.page_chunks, gists_per_meta=wl.gists_per_meta,
-                            top_k_meta=wl.top_k_meta, top_k=wl.top_k, out=out, stream=stream)
-        else:
-            gsa.gsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
-                           num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
-                           page_chunks=wl.page_chunks, top_k=wl.top_k, out=out, stream=stream)
+            return gsa.prepare_hgsa_decode(
+                c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.k_meta, c.v_meta,
+                num_chunks=wl.num_chunks, chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                gists_per_meta=wl.gists_per_meta, top_k_meta=wl.top_k_meta, top_k=wl.top_k,
+                out=out, stream=stream)
+        return gsa.prepare_gsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                      num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                                      page_chunks=wl.page_chunks, top_k=wl.top_k, out=out,
+                                      stream=stream)
+    calls = [prepare(c) for c in copies]
+
+    def step(i):
+        calls[i % len(calls)]()
+
+    if args.copy_calib > 0:
+        n = args.copy_calib // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
-        step(copies[i % len(copies)])
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` calls; HIP events on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region: exactly `steps` calls, bracketed by device syncs; one HIP
+    # event pair on the launch stream gives the device time per launch (the
+    # host enqueues faster than the device runs, so launches run back to back)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(copies[i % len(copies)])
-        ev[i][1].record(stream)
+        step(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mean_call_s = e0.elapsed_time(e1) / 1e3 / args.steps
+
+    # spread of single launches, each between its own events (after the timed region)
+    n_spread = min(50, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_spread)]
+    for i in range(n_spread):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     call_ms = [a.elapsed_time(b) for a, b in ev]
-    mean_call_s = statistics.fmean(call_ms) / 1e3
 
     queries = wl.batch * wl.num_q_heads
     nbytes = alg_bytes(wl)
@@ -144,8 +202,7 @@ def main():
     value = queries * args.steps / wall
     achieved = nbytes / mean_call_s / 1e9
     res = {
-        "metric": "GSA decode queries/sec (batch x q-heads) and achieved HBM GB/s vs peak "
-                  "at 128K ctx",
+        "metric": METRIC,
         "value": value,
         "unit": "queries/s",
         "n_gpus": 1,
@@ -163,16 +220,19 @@ def main():
                    "top_k": wl.top_k, "page_chunks": wl.page_chunks,
                    "cache_copies": len(copies)},
         "hbm_gbps_alg": achieved,
-        "call_us": {"mean": statistics.fmean(call_ms) * 1e3,
+        "launch_us": mean_call_s * 1e6,
+        "single_launch_us": {"mean": statistics.fmean(call_ms) * 1e3,
                     "median": statistics.median(call_ms) * 1e3,
                     "p10": float(np.percentile(call_ms, 10)) * 1e3,
                     "p90": float(np.percentile(call_ms, 90)) * 1e3},
-        "roofline": {"bound": "hbm", "kernel": "gsa_decode call", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "alg_bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "kernel": KERNEL if not wl.hgsa else "hgsa_decode launches",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(wl.name) if not wl.hgsa else None,
+                     "alg_bytes_per_launch": nbytes, "kernel_hash": kernel_hash()},
     }
     if args.cpu_baseline:
-        del copies
+        del copies, calls
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)

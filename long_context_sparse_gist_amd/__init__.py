@@ -169,6 +169,76 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class PreparedCall:
+    """A decode call whose arguments were marshalled once: each call enqueues
+    the same launch again, reading the tensors it was built from (which must
+    stay alive, unmoved) as they are at that time.  For loops over one shape,
+    where per-call argument marshalling would cost more host time than the
+    kernel takes on the device."""
+
+    def __init__(self, fn, args, keep, name):
+        self._fn, self._args, self._keep, self._name = fn, args, keep, name
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise GsaError(st, self._name)
+
+
+def prepare_gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
+                       chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
+                       flags: int = 0, out=None, sel_idx=None, scores=None, ws=None,
+                       stream=None) -> PreparedCall:
+    """gsa_decode's arguments marshalled into a PreparedCall; `out` is
+    allocated here if not given and can be read back as `.out`."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    Hkv = k_cache.shape[1]
+    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = gsa_workspace_size(p, kv)
+    if nbytes == 0:
+        raise GsaError(2, "gsa_workspace_size")
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    args = (ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(sel_idx), _ptr(scores),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream_ptr(stream, q.device))
+    call = PreparedCall(lib().gsa_decode, args,
+                        (p, kv, q, k_cache, v_cache, block_table, seq_lens, out, sel_idx, scores, ws),
+                        "gsa_decode")
+    call.out = out
+    return call
+
+
+def prepare_hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_meta, *,
+                        num_chunks: int, chunk_size: int, page_chunks: int, gists_per_meta: int,
+                        top_k_meta: int, top_k: int, sm_scale: float = 0.0, flags: int = 0,
+                        out=None, sel_meta=None, sel_idx=None, ws=None,
+                        stream=None) -> PreparedCall:
+    """hgsa_decode's arguments marshalled into a PreparedCall."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    Hkv = k_cache.shape[1]
+    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    m = make_meta(k_meta, v_meta, gists_per_meta, top_k_meta)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = hgsa_workspace_size(p, kv, m)
+    if nbytes == 0:
+        raise GsaError(2, "hgsa_workspace_size")
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    args = (ctypes.byref(p), ctypes.byref(kv), ctypes.byref(m), _ptr(q), _ptr(out),
+            _ptr(sel_meta), _ptr(sel_idx), _ptr(ws), ws.numel() * ws.element_size(),
+            _stream_ptr(stream, q.device))
+    call = PreparedCall(lib().hgsa_decode, args,
+                        (p, kv, m, q, k_cache, v_cache, block_table, seq_lens, k_meta, v_meta, out,
+                         sel_meta, sel_idx, ws), "hgsa_decode")
+    call.out = out
+    return call
+
+
 def gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
                chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
                flags: int = 0, out=None, sel_idx=None, scores=None, ws=None, stream=None):

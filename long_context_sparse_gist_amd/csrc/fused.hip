@@ -49,7 +49,7 @@ constexpr int kFSelMaxSlices = 64;   // slices the bucketed select merges
 constexpr int kFSelMaxN = 16384;     // gists per unit the bucketed select handles
 constexpr int kFSelBt = 1024;        // block-table entries the select keeps in LDS
 constexpr int kFSelCand = 2048;      // largest boundary bucket (else the general select)
-constexpr int kFSelL = 32;           // keys per slice the select reads up front
+constexpr int kFSelL = 64;           // keys per slice the select reads up front
 
 __device__ inline void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,7 +107,7 @@ __device__ inline void wait_at_least(const unsigned* p, unsigned target, unsigne
 
 // Folding state of one partial: per-head running max (exp2 domain) and sum,
 // and the factors of the round being folded.
-constexpr int kFoldRound = 8;  // partials folded per round
+constexpr int kFoldRound = 16;  // partials folded per round
 struct FoldHdr {
     float m[16], l[16], f_self[16], fg[16], fb[16];
     float f[kFoldRound][16];
@@ -123,6 +123,7 @@ struct FSelSmem {
     int hist[kBins];
     int bt[kFSelBt];                   // the unit's block-table row
     int need[kFSelMaxSlices];          // slice has boundary-bucket keys past its first kFSelL
+    uint64_t needmask;                 // the same as a bitmask
     int wsum[kThreads / 64];
     int ncand, bstar, above, cnt;
 };
@@ -149,18 +150,25 @@ struct Lds {
 // element threadIdx.x + j*kThreads of the G x D accumulator.  Eight slots per
 // round, every load of a round in flight together.
 template <int EJ, typename SlotFn>
-__device__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&acc)[EJ], FoldHdr& fh) {
+__device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&acc)[EJ], FoldHdr& fh) {
     const int G = a.G, GD = a.G * a.D;
     const size_t base = (size_t)u * a.NS;
-    for (int r0 = 0; r0 < ns; r0 += kFoldRound) {
-        const int nr = min(kFoldRound, ns - r0);
-        float v[EJ][kFoldRound];
+    constexpr int NR = EJ >= 8 ? kFoldRound / 2 : kFoldRound;  // slots per round (registers)
+    constexpr int HR = NR / 2;
+    for (int r0 = 0; r0 < ns; r0 += NR) {
+        const int nr = min(NR, ns - r0);
+        // two half-round arrays (kept in registers), every load issued up front
+        float va[EJ][HR], vb[EJ][HR];
 #pragma unroll
         for (int j = 0; j < EJ; ++j) {
             const int e = threadIdx.x + j * kThreads;
 #pragma unroll
-            for (int i = 0; i < kFoldRound; ++i)
-                v[j][i] = (e < GD && i < nr) ? ld_dev(a.part_acc + (base + slot_of(r0 + i)) * GD + e) : 0.f;
+            for (int i = 0; i < HR; ++i) {
+                va[j][i] = (e < GD && i < nr) ? ld_dev(a.part_acc + (base + slot_of(r0 + i)) * GD + e) : 0.f;
+                vb[j][i] = (e < GD && HR + i < nr)
+                               ? ld_dev(a.part_acc + (base + slot_of(r0 + HR + i)) * GD + e)
+                               : 0.f;
+            }
         }
         if (threadIdx.x < (unsigned)(nr * G)) {
             const int i = threadIdx.x / G, h = threadIdx.x - i * G;
@@ -191,7 +199,7 @@ __device__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&
                 const int h = e / a.D;
                 float x = acc[j] * fh.f_self[h];
 #pragma unroll
-                for (int i = 0; i < kFoldRound; ++i) x += v[j][i] * fh.f[i][h];
+                for (int i = 0; i < HR; ++i) x += va[j][i] * fh.f[i][h] + vb[j][i] * fh.f[HR + i][h];
                 acc[j] = x;
             }
         }
@@ -205,7 +213,7 @@ __device__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&
 // descending bucket order, staged in LDS and written as whole contiguous lines
 // (the stores write through to memory, and a partially written line costs the
 // memory a read-modify-write).
-__device__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
+__device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
                              unsigned char* smem, int* wsum) {
     constexpr int PER = kBins / kThreads;  // consecutive buckets per thread
     int* hist = (int*)smem;
@@ -261,7 +269,7 @@ __device__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, in
 // them; the rest of any other slice is read in a second round.  Keys above b0
 // are selected, keys in b0 are candidates for two radix passes over their low
 // 21 bits.
-__device__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
+__device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
                              unsigned char* smem) {
     constexpr int PER = kBins / kThreads;
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;  // up-front keys per thread
@@ -321,7 +329,6 @@ __device__ void select_fused(const Args& a, const ListCtx& c, int nA, const floa
         if (tid < kFSelMaxSlices) sh.need[tid] = 0;
         if (tid == 0) sh.ncand = 0;
         __syncthreads();
-        clear_hist();  // its values are in LDS now
         find_bucket<kThreads, kBins>(keff, sh);
         b0 = sh.bstar;
         above0 = sh.above;
@@ -330,6 +337,7 @@ __device__ void select_fused(const Args& a, const ListCtx& c, int nA, const floa
     }
     if (general) {
         // wide boundary bucket, long list or many slices: select over the keys
+        if (fast) clear_hist();  // its values are in LDS
         __syncthreads();
         btl = false;  // the select reuses the LDS
         SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
@@ -357,19 +365,46 @@ __device__ void select_fused(const Args& a, const ListCtx& c, int nA, const floa
             sh.cidx[ci] = id;
         }
     };
+    {
+        // up-front keys: one LDS atomic per wavefront reserves its candidate slots
+        uint64_t cm[KQ];
+        int wtot = 0;
 #pragma unroll
-    for (int j = 0; j < KQ; ++j) {
-        const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-        const bool valid = sl < nA && p < slice_n(sl);
-        take(pv[j], valid);
-        // the slice's last up-front key still in bucket >= b0: read the rest
-        if (valid && p == kFSelL - 1 && slice_n(sl) > kFSelL && ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
-            sh.need[sl] = 1;
+        for (int j = 0; j < KQ; ++j) {
+            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+            const bool valid = sl < nA && p < slice_n(sl);
+            const uint32_t key = (uint32_t)pv[j];
+            const int id = (int)(pv[j] >> 32);
+            const uint32_t bk = key >> 21;
+            if (valid && bk > (uint32_t)b0)
+                atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+            cm[j] = __ballot(valid && bk == (uint32_t)b0);
+            wtot += __popcll(cm[j]);
+            // the slice's last up-front key still in bucket >= b0: read the rest
+            if (valid && p == kFSelL - 1 && slice_n(sl) > kFSelL && bk >= (uint32_t)b0) sh.need[sl] = 1;
+        }
+        int base = 0;
+        if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
+        base = __shfl(base, 0);
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int ci = base + __popcll(cm[j] & ((1ull << lane) - 1ull));
+            if (((cm[j] >> lane) & 1ull) && ci < kFSelCand) {
+                sh.ckey[ci] = (uint32_t)pv[j];
+                sh.cidx[ci] = (int)(pv[j] >> 32);
+            }
+            base += __popcll(cm[j]);
+        }
     }
     __syncthreads();
     // round trip 2 (only for slices whose boundary keys run past kFSelL)
-    for (int sl = 0; sl < nA; ++sl) {
-        if (!sh.need[sl]) continue;
+    if (w == 0) {
+        const uint64_t m = __ballot(lane < kFSelMaxSlices && sh.need[lane]);
+        if (lane == 0) sh.needmask = m;
+    }
+    __syncthreads();
+    for (uint64_t m = sh.needmask; m; m &= m - 1ull) {
+        const int sl = __ffsll((unsigned long long)m) - 1;
         const int ns = slice_n(sl);
         for (int p0 = kFSelL; p0 < ns; p0 += kThreads) {
             const int p = p0 + tid;
@@ -443,6 +478,7 @@ __device__ void select_fused(const Args& a, const ListCtx& c, int nA, const floa
         }
         __syncthreads();
     }
+    clear_hist();  // its values were read in the first round trip
     // ascending output: popcount scan over the bitmap words
     uint32_t sb[WPT];
     int c2 = 0;
@@ -466,7 +502,7 @@ __device__ void select_fused(const Args& a, const ListCtx& c, int nA, const floa
 }
 
 template <int D>
-__device__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
+__device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                            CombineSmem& cs, int* wsum, int* s_flag) {
     constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -570,7 +606,7 @@ __device__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsign
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
 // (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u.
 template <int D, int EJ>
-__device__ void combine_publish(WaveAttn<D>& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
+__device__ __forceinline__ void combine_publish(WaveAttn<D>& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
                                 FoldHdr& fh, float* red, CombineSmem& cs) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -628,7 +664,7 @@ __device__ void combine_publish(WaveAttn<D>& wa, const Args& a, int u, int slot,
 
 // EJ: accumulator elements per thread, EJ * kThreads >= G * D.
 template <int D, int EJ>
-__device__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
+__device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                               CombineSmem& cs, FoldHdr& fh, int* s_flag) {
     const int G = a.G, C = a.C;
     ListCtx c;

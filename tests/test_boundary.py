@@ -169,3 +169,16 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gsa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         gsa.lib()
+
+
+def test_control_block_size_matches_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define GSA_WORKSPACE_CONTROL_BYTES \(\(size_t\)(\d+) \+ \(size_t\)(\d+) \* (\d+)\)",
+                  txt)
+    assert m is not None
+    assert int(m[1]) + int(m[2]) * int(m[3]) == gsa.WORKSPACE_CONTROL_BYTES
+
+
+def test_workspace_covers_control_block(lib):
+    p, kv = params(), kvs()
+    assert lib.gsa_workspace_size(ctypes.byref(p), ctypes.byref(kv)) > gsa.WORKSPACE_CONTROL_BYTES

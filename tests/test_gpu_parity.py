@@ -219,3 +219,21 @@ def test_workspace_reuse_across_shapes(gpu):
         torch.cuda.synchronize()
         GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None))
         assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
+
+
+def test_prepared_call_matches(gpu):
+    """A prepared call gives the same bits as gsa_decode, call after call."""
+    wl = SMALL["b2-g7-d128-c16"]
+    say("[parity] prepared call")
+    g_inp = GU.to(gi.make_inputs(wl, 31, seq_lens=lens_for(wl, "ragged", 2)), gpu)
+    want = gsa.gsa_decode(g_inp.q, g_inp.k_cache, g_inp.v_cache, g_inp.block_table, g_inp.seq_lens,
+                          num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                          page_chunks=wl.page_chunks, top_k=wl.top_k)
+    call = gsa.prepare_gsa_decode(g_inp.q, g_inp.k_cache, g_inp.v_cache, g_inp.block_table,
+                                  g_inp.seq_lens, num_chunks=wl.num_chunks,
+                                  chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                                  top_k=wl.top_k)
+    for _ in range(3):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out, want)
