@@ -88,6 +88,7 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     a.num_pages = kv->num_pages;
     a.max_pages = kv->max_pages;
     a.spp = kv->page_chunks * (kv->chunk_size + 1);
+    a.pc_inv = ((1ull << 32) + (uint64_t)kv->page_chunks - 1) / (uint64_t)kv->page_chunks;
     a.top_k = p->top_k;
     a.tau = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / sqrt((double)a.D));
     a.tau_log2e = (float)((double)a.tau * 1.4426950408889634);

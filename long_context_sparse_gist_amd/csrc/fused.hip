@@ -49,7 +49,7 @@ constexpr int kFSelMaxSlices = 64;   // slices the bucketed select merges
 constexpr int kFSelMaxN = 16384;     // gists per unit the bucketed select handles
 constexpr int kFSelBt = 1024;        // block-table entries the select keeps in LDS
 constexpr int kFSelCand = 2048;      // largest boundary bucket (else the general select)
-constexpr int kFSelL = 64;           // keys per slice the select reads up front
+constexpr int kFSelL = 32;           // keys per slice the select reads up front
 
 __device__ inline void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -120,21 +120,23 @@ struct FSelSmem {
     uint32_t tiebits[kFSelMaxN / 32];  // candidates equal to the k-th largest key
     uint32_t ckey[kFSelCand];          // boundary-bucket candidates: order key, chunk id
     int cidx[kFSelCand];
-    int hist[kBins];
     int bt[kFSelBt];                   // the unit's block-table row
-    int need[kFSelMaxSlices];          // slice has boundary-bucket keys past its first kFSelL
-    uint64_t needmask;                 // the same as a bitmask
+    int uh[kBins];                     // the unit's histogram
+    int hist[128];                     // 7-bit digit histogram of the candidate passes
+    uint64_t needmask;                 // slices whose boundary keys run past kFSelL
     int wsum[kThreads / 64];
-    int ncand, bstar, above, cnt;
+    int ncand;
 };
 
 // Dynamic LDS layout (bytes), uses separated in time:
-//   [0, vt)        V transpose tiles (attention blocks)
+//   [0, vt)        V tiles of the attention blocks, parked routing keys
 //   [0, kBins*4+)  a slice's bucket histogram and staged keys
 //   [0, red)       wavefront combination
 //   [0, sel)       top-k select (last gist slice of a unit)
 struct Lds {
-    static constexpr int vt(int D) { return 4 * (D * (32 + 4) * 2); }
+    // V tiles of the 4 wavefronts, then 64 parked routing keys per wavefront
+    static constexpr int vt(int D) { return 4 * (32 * D * 2) + 4 * 64 * 4; }
+    static constexpr int stash(int D) { return 4 * (32 * D * 2); }
     static constexpr int red(int G, int D) { return 4 * G * D * 4; }
     static int bytes(int G, int D) {
         int m = vt(D);
@@ -258,21 +260,48 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
     __syncthreads();
 }
 
+// Sum of x over the lanes of a wavefront at or above this lane.
+__device__ inline int wave_suffix_incl(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(x, off);
+        if (lane + off < 64) x += y;
+    }
+    return x;
+}
+// Sum of x over the lanes of a wavefront below this lane.
+__device__ inline int wave_prefix_excl(int x) {
+    const int lane = threadIdx.x & 63;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    return incl - x;
+}
+
 // Top-k of unit u (ascending chunk ids, -1 padded) and each selected chunk's
 // first-row offset.  nA: gist slices of the unit, keys: the routing keys.
 // Clears the unit's histogram.
 //
-// One round trip reads the histogram, the first kFSelL keys of every slice
-// (bucket-sorted, so they hold the slice's largest buckets) and the block-table
-// row.  The histogram gives the bucket b0 of the k-th largest key.  A slice
-// whose kFSelL-th key lies below b0 has all its keys of buckets >= b0 among
-// them; the rest of any other slice is read in a second round.  Keys above b0
-// are selected, keys in b0 are candidates for two radix passes over their low
-// 21 bits.
+// One round trip reads the histogram (into wavefront 0's registers), the
+// first kFSelL keys of every slice (bucket-sorted, so they hold the slice's
+// largest buckets) and the block-table row.  Wavefront 0 finds the bucket b0
+// of the k-th largest key.  A slice whose kFSelL-th key lies below b0 has all
+// its keys of buckets >= b0 among them; the rest of any other slice is read in
+// a second round.  Keys above b0 are selected, keys in b0 are candidates.
+// Wavefront 0 alone then runs three 7-bit radix passes over the candidates'
+// low 21 bits, resolves ties to the lower chunk id and writes the selection
+// ascending from the bitmap: a single wavefront needs no block barriers, and
+// the candidates are few.
 __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
-                             unsigned char* smem) {
+                                             unsigned char* smem) {
     constexpr int PER = kBins / kThreads;
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;  // up-front keys per thread
+    constexpr int HB = kBins / 64;                           // histogram bins per lane of wavefront 0
+    constexpr int WPL = kFSelMaxN / 32 / 64;                 // bitmap words per lane of wavefront 0
     FSelSmem& sh = *(FSelSmem*)smem;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
@@ -293,7 +322,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     uint64_t pv[KQ];
     if (fast) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) hv[i] = ld_dev(H + PER * tid + i);
+        for (int i = 0; i < PER; ++i) hv[i] = ld_dev(H + tid + i * kThreads);
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -303,10 +332,9 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     if (btl)
         for (int i = tid; i < a.max_pages; i += kThreads) sh.bt[i] = btrow[i];
     auto row_of = [&](int m) -> int64_t {  // element offset of chunk m's first raw row
-        const int slot = m * (a.C + 1);
-        const int lp = slot / a.spp;
+        const int lp = chunk_page(a, m);
         const int phys = btl ? sh.bt[lp] : btrow[lp];
-        return (((int64_t)phys * a.Hkv + c.g) * a.spp + (slot - lp * a.spp)) * a.D;
+        return (((int64_t)phys * a.Hkv + c.g) * a.spp + (int64_t)(m - lp * a.page_chunks) * (a.C + 1)) * a.D;
     };
     auto emit = [&](int pos, int m) {
         st_dev(out + pos, (int32_t)m);
@@ -322,17 +350,51 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     bool general = !fast;
     int b0 = 0, above0 = 0, cnt0 = 0;
     if (fast) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) sh.hist[PER * tid + i] = (int)hv[i];
         for (int i = tid; i < kFSelMaxN / 64; i += kThreads) sh.selbits[i] = 0ull;
         for (int i = tid; i < kFSelMaxN / 32; i += kThreads) sh.tiebits[i] = 0u;
-        if (tid < kFSelMaxSlices) sh.need[tid] = 0;
-        if (tid == 0) sh.ncand = 0;
+        if (tid == 0) {
+            sh.ncand = 0;
+            sh.needmask = 0ull;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sh.uh[tid + i * kThreads] = (int)hv[i];
         __syncthreads();
-        find_bucket<kThreads, kBins>(keff, sh);
-        b0 = sh.bstar;
-        above0 = sh.above;
-        cnt0 = sh.cnt;
+        {
+            // every wavefront finds the bucket of the keff-th largest key
+            // (lane l reads buckets [HB*l, HB*l + HB)), so no barrier follows
+            int hb[HB];
+            int s = 0;
+#pragma unroll
+            for (int i = 0; i < HB; i += 4) {
+                const int4 v = *(const int4*)&sh.uh[HB * lane + i];
+                hb[i] = v.x;
+                hb[i + 1] = v.y;
+                hb[i + 2] = v.z;
+                hb[i + 3] = v.w;
+                s += v.x + v.y + v.z + v.w;
+            }
+            const int higher = wave_suffix_incl(s) - s;  // keys in the buckets of higher lanes
+            int fb = 0, fa = 0, fc = 0;
+            const bool mine = higher < keff && higher + s >= keff;
+            if (mine) {
+                int acc = higher;
+                bool found = false;
+#pragma unroll
+                for (int j = HB - 1; j >= 0; --j) {
+                    if (!found && acc + hb[j] >= keff) {
+                        found = true;
+                        fb = HB * lane + j;
+                        fa = acc;
+                        fc = hb[j];
+                    }
+                    if (!found) acc += hb[j];
+                }
+            }
+            const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+            b0 = __shfl(fb, src);
+            above0 = __shfl(fa, src);
+            cnt0 = __shfl(fc, src);
+        }
         general = cnt0 > kFSelCand;
     }
     if (general) {
@@ -373,15 +435,16 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
             const bool valid = sl < nA && p < slice_n(sl);
-            const uint32_t key = (uint32_t)pv[j];
-            const int id = (int)(pv[j] >> 32);
-            const uint32_t bk = key >> 21;
-            if (valid && bk > (uint32_t)b0)
+            const uint32_t bk = (uint32_t)pv[j] >> 21;
+            if (valid && bk > (uint32_t)b0) {
+                const int id = (int)(pv[j] >> 32);
                 atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+            }
             cm[j] = __ballot(valid && bk == (uint32_t)b0);
             wtot += __popcll(cm[j]);
             // the slice's last up-front key still in bucket >= b0: read the rest
-            if (valid && p == kFSelL - 1 && slice_n(sl) > kFSelL && bk >= (uint32_t)b0) sh.need[sl] = 1;
+            if (p == kFSelL - 1 && valid && bk >= (uint32_t)b0 && slice_n(sl) > kFSelL)
+                atomicOr((unsigned long long*)&sh.needmask, 1ull << sl);
         }
         int base = 0;
         if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
@@ -398,49 +461,64 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     }
     __syncthreads();
     // round trip 2 (only for slices whose boundary keys run past kFSelL)
-    if (w == 0) {
-        const uint64_t m = __ballot(lane < kFSelMaxSlices && sh.need[lane]);
-        if (lane == 0) sh.needmask = m;
-    }
-    __syncthreads();
-    for (uint64_t m = sh.needmask; m; m &= m - 1ull) {
-        const int sl = __ffsll((unsigned long long)m) - 1;
-        const int ns = slice_n(sl);
-        for (int p0 = kFSelL; p0 < ns; p0 += kThreads) {
-            const int p = p0 + tid;
-            const uint64_t pr = p < ns ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
-            take(pr, p < ns);
+    const uint64_t needmask = sh.needmask;
+    if (needmask) {
+        for (uint64_t m = needmask; m; m &= m - 1ull) {
+            const int sl = __ffsll((unsigned long long)m) - 1;
+            const int ns = slice_n(sl);
+            for (int p0 = kFSelL; p0 < ns; p0 += kThreads) {
+                const int p = p0 + tid;
+                const uint64_t pr = p < ns ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
+                take(pr, p < ns);
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
-    // radix passes over the candidates' bits [20:10] and [9:0]
+    if (w == 0) {
+    // wavefront 0: radix passes over the candidates' bits [20:14], [13:7], [6:0]
     int above = above0;
     uint32_t prefix = (uint32_t)b0 << 21;
     int fixed = 11;
     bool take_all = above + cnt0 == keff;
-    for (int pass = 1; pass < 3 && !take_all; ++pass) {
-        const int width = pass == 1 ? 11 : 10;
-        const int shift = 32 - fixed - width;
-        for (int i = tid; i < (1 << width); i += kThreads) sh.hist[i] = 0;
-        __syncthreads();
-        for (int ci = tid; ci < cnt0; ci += kThreads) {
+    for (int pass = 0; pass < 3 && !take_all; ++pass) {
+        const int shift = 14 - 7 * pass;
+        sh.hist[lane] = 0;
+        sh.hist[lane + 64] = 0;
+        lds_fence();
+        for (int ci = lane; ci < cnt0; ci += 64) {
             const uint32_t x = sh.ckey[ci];
-            if ((x >> (32 - fixed)) == (prefix >> (32 - fixed)))
-                atomicAdd(&sh.hist[(x >> shift) & ((1u << width) - 1u)], 1);
+            if ((x >> (32 - fixed)) == (prefix >> (32 - fixed))) atomicAdd(&sh.hist[(x >> shift) & 127u], 1);
         }
-        __syncthreads();
-        if (pass == 1) find_bucket<kThreads, 2048>(keff - above, sh);
-        else find_bucket<kThreads, 1024>(keff - above, sh);
-        above += sh.above;
-        prefix |= (uint32_t)sh.bstar << shift;
-        fixed += width;
-        const int cnt = sh.cnt;
-        __syncthreads();
-        if (above + cnt == keff) take_all = true;
+        lds_fence();
+        const int h0 = sh.hist[2 * lane], h1 = sh.hist[2 * lane + 1];
+        const int s2 = h0 + h1;
+        const int higher = wave_suffix_incl(s2) - s2;
+        const int need = keff - above;
+        const bool mine = higher < need && higher + s2 >= need;
+        int bsel = 0, abv = 0, cn = 0;
+        if (mine) {
+            if (higher + h1 >= need) {
+                bsel = 2 * lane + 1;
+                abv = higher;
+                cn = h1;
+            } else {
+                bsel = 2 * lane;
+                abv = higher + h1;
+                cn = h0;
+            }
+        }
+        const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        bsel = __shfl(bsel, src);
+        abv = __shfl(abv, src);
+        cn = __shfl(cn, src);
+        above += abv;
+        prefix |= (uint32_t)bsel << shift;
+        fixed += 7;
+        if (above + cn == keff) take_all = true;
     }
     const uint32_t lo = prefix;
     const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
-    for (int ci = tid; ci < cnt0; ci += kThreads) {
+    for (int ci = lane; ci < cnt0; ci += 64) {
         const uint32_t x = sh.ckey[ci];
         const int id = sh.cidx[ci];
         if (x > hi || (take_all && x >= lo))
@@ -448,24 +526,22 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         else if (x >= lo)
             atomicOr(&sh.tiebits[id >> 5], 1u << (id & 31));
     }
-    __syncthreads();
-    constexpr int WPT = kFSelMaxN / 32 / kThreads;  // bitmap words per thread
-    const int nw = (n + 31) / 32;
+    lds_fence();
     if (!take_all) {
+        const int nw = (n + 31) / 32;
         // the (keff - above) lowest-index keys equal to the k-th largest
         const int need_eq = keff - above;
-        uint32_t tb[WPT];
+        uint32_t tb[WPL];
         int c1 = 0;
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int wd = WPT * tid + i;
+        for (int i = 0; i < WPL; ++i) {
+            const int wd = WPL * lane + i;
             tb[i] = wd < nw ? sh.tiebits[wd] : 0u;
             c1 += __popc(tb[i]);
         }
-        int tot;
-        int before = block_excl_scan<kThreads>(c1, &tot, sh.wsum);
+        int before = wave_prefix_excl(c1);
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
+        for (int i = 0; i < WPL; ++i) {
             uint32_t add = 0u, rest = tb[i];
             while (rest && before < need_eq) {
                 const uint32_t bit = rest & (~rest + 1u);
@@ -473,13 +549,16 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
                 rest ^= bit;
                 ++before;
             }
-            const int wd = WPT * tid + i;
+            const int wd = WPL * lane + i;
             if (add) atomicOr((unsigned long long*)&sh.selbits[wd >> 1], (uint64_t)add << (32 * (wd & 1)));
         }
-        __syncthreads();
     }
-    clear_hist();  // its values were read in the first round trip
-    // ascending output: popcount scan over the bitmap words
+    }  // wavefront 0
+    __syncthreads();
+    clear_hist();  // its values are in LDS
+    // ascending output (every thread): popcount scan over the bitmap words
+    constexpr int WPT = kFSelMaxN / 32 / kThreads;  // bitmap words per thread
+    const int nw = (n + 31) / 32;
     uint32_t sb[WPT];
     int c2 = 0;
 #pragma unroll
@@ -540,13 +619,14 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
             for (int t = 0; t < 2; ++t)
                 if (16 * t + lr >= nval[j]) off[j][t] = __shfl(off[j][0], lane & 48);
         }
-        WaveAttn<D> wa;
+        WaveAttnL<D> wa;
         wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
-        __bf16* vt = (__bf16*)smem + (size_t)w * (D * (32 + 4));
+        unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
+        float* stash = (float*)(smem + Lds::stash(D)) + 64 * w;
         const float tau = a.tau;
-        wa.template stream<NBW, false>(
+        wa.template stream<NBW>(
             (const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, attn, a.tau_log2e, lr, lg,
-            vt, [&](int j, const f32x4_t sc[2]) {
+            tile, [&](int j, const f32x4_t sc[2]) {
                 // routing keys: tau * sum over the group's heads (padding heads are 0)
                 float kv = 0.f;
                 int kt = -1;
@@ -560,20 +640,16 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
                             kt = 16 * t + 4 * lg + r;
                         }
                     }
-                // park the key in the unused columns 32..33 of row 32*j + kt of
-                // this wavefront's V tile (no global store here: a store
-                // in flight would hold up the next wait on this wavefront's
-                // loads)
-                if (kt >= 0 && kt < nval[j]) *(float*)(vt + (32 * j + kt) * (32 + 4) + 32) = kv;
+                // park the key in LDS (no global store here: a store in
+                // flight would hold up the next wait on this wavefront's loads)
+                if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kv;
             });
         // thread t takes key slot t % 64 of wavefront t / 64 (NBW * 32 == 64 slots)
         static_assert(NBW * 32 * 4 == kThreads, "one key slot per thread");
         __syncthreads();
         const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
         const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
-        const float kv = kpos < cnt
-            ? *(const float*)((__bf16*)smem + (size_t)ws * (D * (32 + 4)) + slot * (32 + 4) + 32)
-            : 0.f;
+        const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
         __syncthreads();  // the tiles are free
         bucket_slice(a, u, idx, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
@@ -595,7 +671,9 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
     __syncthreads();
     if (!*s_flag) return;
 
-    // last slice of the unit: select and publish
+    // last slice of the unit: select and publish (ahead of the streaming
+    // workgroups sharing this CU: everything of the unit waits for it)
+    __builtin_amdgcn_s_setprio(2);
     for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
     select_fused(a, c, nA, keys, smem);
     drain();
@@ -605,8 +683,8 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
 // (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u.
-template <int D, int EJ>
-__device__ __forceinline__ void combine_publish(WaveAttn<D>& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
+template <int D, int EJ, typename WA>
+__device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
                                 FoldHdr& fh, float* red, CombineSmem& cs) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -627,7 +705,7 @@ __device__ __forceinline__ void combine_publish(WaveAttn<D>& wa, const Args& a, 
         const float sc = (cs.wm[w][h] == -INFINITY) ? 0.f : exp2f((cs.wm[w][h] - M) * tl);
         if (h < G) {
 #pragma unroll
-            for (int db = 0; db < WaveAttn<D>::DB; ++db)
+            for (int db = 0; db < WA::DB; ++db)
                 red[((size_t)w * G + h) * D + 16 * db + lr] = wa.o[db][r] * sc;
         }
     }
@@ -697,7 +775,8 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     }
     wait_at_least<8>(unit_ready(a, u), 1u, s.err);
     __syncthreads();
-    WaveAttn<D> wa;
+    __builtin_amdgcn_s_setprio(1);  // the unit's result waits for this task
+    WaveAttnL<D> wa;
     wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
     if (cnt > 0) {
         const int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
@@ -720,10 +799,10 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
             }
             off[0][t] = (size_t)o;
         }
-        __bf16* vt = (__bf16*)smem + (size_t)w * (D * (32 + 4));
-        wa.template stream<1, false>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
-                                     nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, vt,
-                                     [](int, const f32x4_t*) {});
+        unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
+        wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
+                              nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, tile,
+                              [](int, const f32x4_t*) {});
     }
     __syncthreads();
     combine_publish<D, EJ>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);

@@ -53,6 +53,7 @@ struct Args {
     uint64_t* spairs; // [units][S1][kFusedTA] slice keys by bucket: order key | id << 32
     int64_t* rowoff;  // [units][ro_stride] element offset of each selected chunk's first row
     int ro_stride;    // min(top_k, num_chunks)
+    uint64_t pc_inv;  // ceil(2^32 / page_chunks): chunk -> logical page by multiply
     void* out;        // [B][Hq][D]
 };
 
@@ -67,6 +68,14 @@ __device__ inline void seq_shape(const Args& a, int b, int& n, int& tail) {
     if (n > a.num_chunks) { n = a.num_chunks; tail = 0; }
     long cap = (long)a.max_pages * a.spp - (long)n * (a.C + 1);
     if (tail > cap) tail = (int)cap;
+}
+
+// Logical page of chunk m.  Slots number below 2^30, so m < 2^29 and
+// m * ceil(2^32 / page_chunks) / 2^32 exceeds m / page_chunks by less than
+// 1/4: the quotient is exact or one too large, and one compare corrects it.
+__device__ inline int chunk_page(const Args& a, int m) {
+    const int q = (int)(((uint64_t)(uint32_t)m * a.pc_inv) >> 32);
+    return q * a.page_chunks > m ? q - 1 : q;
 }
 
 // Element offset of logical slot s of sequence b, kv-head g in the paged cache.

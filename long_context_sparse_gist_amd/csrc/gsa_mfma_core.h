@@ -227,8 +227,8 @@ struct CombineSmem {
 // (max in the exp2 domain, sum, weighted V sum) and hand each element to
 // `emit_acc(h, d, value)` / `emit_ml(h, m2, l)`.  red: >= 4*G*D floats of LDS
 // (may alias the V tiles: a barrier separates their uses).
-template <int D, typename EmitAcc, typename EmitMl>
-__device__ inline void combine_waves(WaveAttn<D>& wa, float tau_log2e, int G, float* red,
+template <int D, typename WA, typename EmitAcc, typename EmitMl>
+__device__ inline void combine_waves(WA& wa, float tau_log2e, int G, float* red,
                                      CombineSmem& cs, EmitAcc emit_acc, EmitMl emit_ml) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -247,7 +247,7 @@ __device__ inline void combine_waves(WaveAttn<D>& wa, float tau_log2e, int G, fl
         float sc = (cs.wm[w][h] == -INFINITY) ? 0.f : exp2f((cs.wm[w][h] - M) * tau_log2e);
         if (h < G) {
 #pragma unroll
-            for (int db = 0; db < WaveAttn<D>::DB; ++db)
+            for (int db = 0; db < WA::DB; ++db)
                 red[((size_t)w * G + h) * D + 16 * db + lr] = wa.o[db][r] * sc;
         }
     }
@@ -268,5 +268,177 @@ __device__ inline void combine_waves(WaveAttn<D>& wa, float tau_log2e, int G, fl
     }
     __syncthreads();
 }
+
+}  // namespace gsa
+
+namespace gsa {
+
+typedef short v4s16_t __attribute__((ext_vector_type(4)));
+typedef short v8s16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Per-wavefront attention core with V staged through LDS.
+//
+// A block's 32 V rows go from global memory straight into a wavefront tile
+// (global_load_lds_dwordx4: lane l of an instruction writes the tile's 16-byte
+// chunk 64*q + l, holding no registers), and the PV product reads its B
+// operand back transposed (ds_read_b64_tr_b16: within a group of 16 lanes,
+// lane j receives element j%4 of the 8 bytes read by lanes j/4 + 4i, i < 4).
+// Tile rows are D bf16; chunk c of row r sits at 16-byte position
+// c ^ 2(r mod CPR/2), so the four rows one 16-lane group reads hit different
+// banks.  Scores, online softmax and the P operand are those of WaveAttn.
+template <int D>
+struct WaveAttnL {
+    static constexpr int KK = D / 32;        // k-steps over the head dimension
+    static constexpr int DB = D / 16;        // 16-wide output column blocks
+    static constexpr int CPR = D / 8;        // 16-byte chunks per V row
+    static constexpr int TILE_BYTES = 32 * D * 2;
+
+    bf16x8_t qB[KK];
+    f32x4_t o[DB];
+    float m, l;
+
+    __device__ static inline int swz(int r) { return 2 * (r % (CPR / 2)); }
+
+    __device__ inline void init(const __bf16* qgroup, int G, int lr, int lg) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (lr < G) {
+                qB[kk] = *(const bf16x8_t*)(qgroup + (size_t)lr * D + 32 * kk + 8 * lg);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qB[kk][i] = (__bf16)0.0f;
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+    }
+
+    // Scores of one 32-token block from its K operands (token 16*t + lr).
+    __device__ inline void scores(const bf16x8_t kA[2][KK], f32x4_t s[2]) const {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[t][kk], qB[kk], acc, 0, 0, 0);
+            s[t] = acc;
+        }
+    }
+
+    // Issue the direct loads of one block's V rows into `tile`.  off0 / off1:
+    // element offsets (from vbase) of this lane's rows lr and 16 + lr; row r's
+    // offset is taken from lane r % 16.
+    __device__ inline void load_v(const __bf16* vbase, size_t off0, size_t off1,
+                                  unsigned char* tile) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int q = 0; q < CPR / 2; ++q) {
+            const int f = 64 * q + lane, r = f / CPR, p = f % CPR, c = p ^ swz(r);
+            const size_t src = (64 * q) / CPR < 16 ? off0 : off1;  // uniform per q
+            const unsigned lo = __shfl((unsigned)src, r % 16), hi = __shfl((unsigned)(src >> 32), r % 16);
+            const size_t ro = ((size_t)hi << 32) | lo;
+            __builtin_amdgcn_global_load_lds(vbase + ro + 8 * c, (lds_void_t*)(tile + 1024 * q), 16, 0, 0);
+        }
+    }
+
+    // Online-softmax update for one block; returns its probabilities as the
+    // PV A operand.  nvalid: tokens [0, nvalid) are real (>= 1).
+    __device__ inline bf16x8_t softmax(const f32x4_t s[2], int nvalid, float tau_log2e, int lg) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * t + 4 * lg + r < nvalid) bm = fmaxf(bm, s[t][r]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mnew = fmaxf(m, bm);  // finite: the block has a real token
+        const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on the first block
+        const float mb = mnew * tau_log2e;
+        bf16x8_t P;
+        float ls = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float pv = (16 * t + 4 * lg + r < nvalid) ? exp2f(s[t][r] * tau_log2e - mb) : 0.f;
+                __bf16 pb = (__bf16)pv;
+                ls += (float)pb;
+                P[4 * t + r] = pb;
+            }
+        const bool first = m == -INFINITY;
+        l = l * alpha + ls;
+        m = mnew;
+        if (!first) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db][r] *= ar;
+            }
+        }
+        return P;
+    }
+
+    // PV product of one block from its tile (the tile's loads have completed).
+    __device__ inline void pv(const bf16x8_t& P, const unsigned char* tile) {
+        const int lane = threadIdx.x & 63, kq = lane >> 4, s = lane & 15;
+        int rowb[2], x[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + 4 * kq + (s >> 2);
+            rowb[h] = r * 2 * D + 16 * ((s & 3) >> 1) + 8 * (s & 1);
+            x[h] = r % (CPR / 2);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            v4s16_t hv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s16_t*)(tile + rowb[h] + 32 * (db ^ x[h])));
+            // whole-vector reinterpretation (element-wise bf16 inserts of the
+            // 16-bit lanes were lowered to wrong byte permutes)
+            const v8s16_t both = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, both);
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P, vb, o[db], 0, 0, 0);
+        }
+    }
+
+    // Stream this wavefront's blocks j < nbw (<= NBW): block j's rows sit at
+    // element offsets off[j][t] and its first nval[j] tokens are real.
+    // on_scores(j, s) sees every block's scores; attn = false skips V and PV.
+    template <int NBW, typename OnScores>
+    __device__ inline void stream(const __bf16* kbase, const __bf16* vbase,
+                                  const size_t (&off)[NBW][2], const int (&nval)[NBW], int nbw,
+                                  bool attn, float tau_log2e, int lr, int lg, unsigned char* tile,
+                                  OnScores on_scores) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            if (j < nbw) {
+                bf16x8_t kb[2][KK];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        kb[t][kk] = *(const bf16x8_t*)(kbase + off[j][t] + 32 * kk + 8 * lg);
+                if (attn) load_v(vbase, off[j][0], off[j][1], tile);
+                f32x4_t s[2];
+                scores(kb, s);
+                on_scores(j, s);
+                if (attn) {
+                    bf16x8_t P = softmax(s, nval[j], tau_log2e, lg);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tile is loaded
+                    pv(P, tile);
+                    // the next block's loads overwrite the tile: its reads are done
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+            }
+        }
+    }
+};
 
 }  // namespace gsa
