@@ -126,7 +126,7 @@ typedef struct {
 /* Size of the control block at the start of every workspace: work-queue
  * counters and per-(batch, kv-head) routing-key histograms of the
  * single-launch path. */
-#define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 8448)
+#define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 8704)
 
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the
  * shapes are invalid).  The workspace must be 256-byte aligned and its first

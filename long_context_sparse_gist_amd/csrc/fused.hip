@@ -111,7 +111,6 @@ constexpr int kFoldRound = 16;  // partials folded per round
 struct FoldHdr {
     float m[16], l[16], f_self[16], fg[16], fb[16];
     float f[kFoldRound][16];
-    float2 ml[kFoldRound][16];
 };
 
 // LDS of the top-k select (last gist slice of a unit).
@@ -172,26 +171,29 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
                                : 0.f;
             }
         }
-        if (threadIdx.x < (unsigned)(nr * G)) {
-            const int i = threadIdx.x / G, h = threadIdx.x - i * G;
-            const float* p = (const float*)(a.part_ml + (base + slot_of(r0 + i)) * G + h);
-            fh.ml[i][h] = make_float2(ld_dev(p), ld_dev(p + 1));
-        }
-        __syncthreads();
-        if (threadIdx.x < (unsigned)G) {
-            const int h = threadIdx.x;
-            float M = fh.m[h];
-            for (int i = 0; i < nr; ++i) M = fmaxf(M, fh.ml[i][h].x);
-            const float fself = (fh.m[h] == -INFINITY) ? 0.f : exp2f(fh.m[h] - M);
-            float L = fh.l[h] * fself;
-            for (int i = 0; i < kFoldRound; ++i) {
-                const float fi = (i >= nr || fh.ml[i][h].x == -INFINITY) ? 0.f : exp2f(fh.ml[i][h].x - M);
-                fh.f[i][h] = fi;
-                if (i < nr) L += fh.ml[i][h].y * fi;
+        {
+            // factors: the 16 lanes of row h hold slots 0..15 of head h
+            const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
+            float x = -INFINITY, y = 0.f;
+            if (h < G && i < nr) {
+                const float* p = (const float*)(a.part_ml + (base + slot_of(r0 + i)) * G + h);
+                x = ld_dev(p);
+                y = ld_dev(p + 1);
             }
-            fh.f_self[h] = fself;
-            fh.m[h] = M;
-            fh.l[h] = L;
+            const float mold = h < G ? fh.m[h] : -INFINITY;
+            const float lold = h < G ? fh.l[h] : 0.f;
+            const float M = fmaxf(mold, rowmax16(x));
+            const float fi = x == -INFINITY ? 0.f : exp2f(x - M);
+            const float fself = mold == -INFINITY ? 0.f : exp2f(mold - M);
+            const float L = lold * fself + rowsum16(y * fi);
+            if (h < G) {
+                fh.f[i][h] = fi;
+                if (i == 0) {
+                    fh.f_self[h] = fself;
+                    fh.m[h] = M;
+                    fh.l[h] = L;
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -237,6 +239,9 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         if (h[i]) __hip_atomic_fetch_add(H + i, (unsigned)h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    static_assert(32 % PER == 0, "a thread's buckets lie in one coarse bucket");
+    if (s) __hip_atomic_fetch_add(unit_coarse(a, u) + PER * tid / 32, (unsigned)s, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     int tot;
     const int below = block_excl_scan<kThreads>(s, &tot, wsum);
     int run = tot - below - s;  // keys in the buckets of higher threads
@@ -315,12 +320,16 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     auto clear_hist = [&]() {
 #pragma unroll
         for (int i = 0; i < PER; ++i) st_dev(H + PER * tid + i, 0u);
+        if (tid < kCoarse) st_dev(unit_coarse(a, u) + tid, 0u);
     };
     auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
     // round trip 1
     unsigned hv[PER];
     uint64_t pv[KQ];
+    int cv = 0;  // coarse bucket kCoarse - 1 - lane (descending over the lanes)
     if (fast) {
+        static_assert(kCoarse == 64, "one coarse bucket per lane");
+        cv = (int)ld_dev(unit_coarse(a, u) + (kCoarse - 1 - lane));
 #pragma unroll
         for (int i = 0; i < PER; ++i) hv[i] = ld_dev(H + tid + i * kThreads);
 #pragma unroll
@@ -360,40 +369,19 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         for (int i = 0; i < PER; ++i) sh.uh[tid + i * kThreads] = (int)hv[i];
         __syncthreads();
         {
-            // every wavefront finds the bucket of the keff-th largest key
-            // (lane l reads buckets [HB*l, HB*l + HB)), so no barrier follows
-            int hb[HB];
-            int s = 0;
-#pragma unroll
-            for (int i = 0; i < HB; i += 4) {
-                const int4 v = *(const int4*)&sh.uh[HB * lane + i];
-                hb[i] = v.x;
-                hb[i + 1] = v.y;
-                hb[i + 2] = v.z;
-                hb[i + 3] = v.w;
-                s += v.x + v.y + v.z + v.w;
-            }
-            const int higher = wave_suffix_incl(s) - s;  // keys in the buckets of higher lanes
-            int fb = 0, fa = 0, fc = 0;
-            const bool mine = higher < keff && higher + s >= keff;
-            if (mine) {
-                int acc = higher;
-                bool found = false;
-#pragma unroll
-                for (int j = HB - 1; j >= 0; --j) {
-                    if (!found && acc + hb[j] >= keff) {
-                        found = true;
-                        fb = HB * lane + j;
-                        fa = acc;
-                        fc = hb[j];
-                    }
-                    if (!found) acc += hb[j];
-                }
-            }
-            const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-            b0 = __shfl(fb, src);
-            above0 = __shfl(fa, src);
-            cnt0 = __shfl(fc, src);
+            // every wavefront finds the bucket of the keff-th largest key:
+            // suffix counts of the coarse buckets, then of the 32 fine
+            // buckets of the coarse one that holds it (no barrier follows)
+            const int cp = wave_prefix_incl_dpp(cv);  // keys in coarse buckets >= 63 - lane
+            const int lc = __ffsll((unsigned long long)__ballot(cp >= keff)) - 1;
+            const int B0 = kCoarse - 1 - lc;
+            const int abovec = __builtin_amdgcn_readlane(cp, lc) - __builtin_amdgcn_readlane(cv, lc);
+            const int fv = lane < 32 ? sh.uh[32 * B0 + 31 - lane] : 0;
+            const int fp = wave_prefix_incl_dpp(fv) + abovec;
+            const int lf = __ffsll((unsigned long long)__ballot(lane < 32 && fp >= keff)) - 1;
+            b0 = 32 * B0 + 31 - lf;
+            cnt0 = __builtin_amdgcn_readlane(fv, lf);
+            above0 = __builtin_amdgcn_readlane(fp, lf) - cnt0;
         }
         general = cnt0 > kFSelCand;
     }
@@ -839,7 +827,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
 }
 
 template <int D, int EJ>
-__global__ __launch_bounds__(kThreads, 3) void gsa_fused_kernel(Args a, Sched s) {
+__global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ CombineSmem cs;
     __shared__ FoldHdr fh;

@@ -38,6 +38,27 @@ __device__ inline float dpp_row(float x, int which) {
     return __builtin_bit_cast(float, r);
 }
 
+// Max over the 16 lanes of a row; every lane of the row gets it.
+__device__ inline float rowmax16(float x) {
+    x = fmaxf(x, dpp_row(x, 0));
+    x = fmaxf(x, dpp_row(x, 1));
+    x = fmaxf(x, dpp_row(x, 2));
+    x = fmaxf(x, dpp_row(x, 3));
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (DPP row shifts, then
+// row broadcasts of lanes 15 and 31).
+__device__ inline int wave_prefix_incl_dpp(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 // Sum over the 16 lanes of a row; every lane of the row gets the total.
 __device__ inline float rowsum16(float x) {
     x += dpp_row(x, 0);
