@@ -123,9 +123,8 @@ typedef struct {
     int32_t top_k_meta;      /* k1 >= 0 meta-gists kept per (batch, kv-head) */
 } hgsa_meta_t;
 
-/* Size of the control block at the start of every workspace: work-queue
- * counters and per-(batch, kv-head) routing-key histograms of the
- * single-launch path. */
+/* Size of the control block at the start of every workspace: an error word
+ * and the per-(batch, kv-head) counters of the single-launch path. */
 #define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 8704)
 
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the

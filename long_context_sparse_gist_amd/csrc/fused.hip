@@ -3,11 +3,11 @@
 // Workgroup t runs task t.  Tasks are numbered gist slices first (every unit,
 // unit-major), then unfolded-list tasks:
 //   gist slice (u, i)  scores gists [i*TA, (i+1)*TA) of unit u, writes their
-//                      routing keys, sorts them by the top 11 bits of their
-//                      order key (bucket) and publishes per-bucket suffix
-//                      counts, and (all-gists set) one softmax partial.  The
-//                      unit's last slice to finish runs the top-k select from
-//                      the slices' bucket counts and publishes the selection.
+//                      routing keys, publishes them sorted by the top 11 bits
+//                      of their order key (bucket), largest first, and
+//                      (all-gists set) one softmax partial.  The unit's last
+//                      slice to finish runs the top-k select over the sorted
+//                      slices and publishes the selection.
 //   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
 //                      select runs, waits for the selection, attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
@@ -29,13 +29,9 @@
 // Select.  A wavefront issues at most one instruction every few cycles, so a
 // single workgroup that touches every key of a unit several times is slow
 // (thousands of keys per wavefront).  The per-key work is done where the keys
-// are made instead: each slice (one key per thread) histograms its keys'
-// buckets, stores the inclusive suffix count of every bucket and scatters its
-// keys in descending bucket order.  The select then reads the suffix counts at
-// every 32nd bucket, then the 33 around the bucket holding the k-th largest
-// key, and gathers from each slice only the keys above that bucket (taken) and
-// inside it (candidates); two radix passes over the candidates' low 21 bits
-// fix the k-th largest key, ties go to the lower chunk index.
+// are made instead: each slice (one key per thread) sorts its keys by bucket.
+// The select then needs only the first few keys of every slice, plus the rest
+// of the rare slice that holds many of the largest keys (select_fused).
 #include "gsa_lists.h"
 #include "gsa_mfma_core.h"
 #include "gsa_select.h"
@@ -120,11 +116,13 @@ struct FSelSmem {
     uint32_t ckey[kFSelCand];          // boundary-bucket candidates: order key, chunk id
     int cidx[kFSelCand];
     int bt[kFSelBt];                   // the unit's block-table row
-    int uh[kBins];                     // the unit's histogram
+    int uh[kBins];                     // bucket histogram of the candidates
+    int coarse[kBins / 32];            // its sums over 32 buckets
     int hist[128];                     // 7-bit digit histogram of the candidate passes
     uint64_t needmask;                 // slices whose boundary keys run past kFSelL
     int wsum[kThreads / 64];
     int ncand;
+    int nr2;                           // keys kept from the second round
 };
 
 // Dynamic LDS layout (bytes), uses separated in time:
@@ -212,11 +210,10 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
 }
 
 // Bucket sort of one slice's keys, one per thread: kv (the key) and pos (its
-// position in the slice, -1: none).  Adds the slice's bucket counts to the
-// unit's histogram and publishes its keys (order key | chunk id << 32) in
-// descending bucket order, staged in LDS and written as whole contiguous lines
-// (the stores write through to memory, and a partially written line costs the
-// memory a read-modify-write).
+// position in the slice, -1: none).  Publishes the keys (order key | chunk id
+// << 32) in descending bucket order, staged in LDS and written as whole
+// contiguous lines (the stores write through to memory, and a partially
+// written line costs the memory a read-modify-write).
 __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
                              unsigned char* smem, int* wsum) {
     constexpr int PER = kBins / kThreads;  // consecutive buckets per thread
@@ -235,13 +232,6 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
         h[i] = hist[PER * tid + i];
         s += h[i];
     }
-    unsigned* H = unit_hist(a, u) + PER * tid;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-        if (h[i]) __hip_atomic_fetch_add(H + i, (unsigned)h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    static_assert(32 % PER == 0, "a thread's buckets lie in one coarse bucket");
-    if (s) __hip_atomic_fetch_add(unit_coarse(a, u) + PER * tid / 32, (unsigned)s, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
     int tot;
     const int below = block_excl_scan<kThreads>(s, &tot, wsum);
     int run = tot - below - s;  // keys in the buckets of higher threads
@@ -289,49 +279,40 @@ __device__ inline int wave_prefix_excl(int x) {
 
 // Top-k of unit u (ascending chunk ids, -1 padded) and each selected chunk's
 // first-row offset.  nA: gist slices of the unit, keys: the routing keys.
-// Clears the unit's histogram.
 //
-// One round trip reads the histogram (into wavefront 0's registers), the
-// first kFSelL keys of every slice (bucket-sorted, so they hold the slice's
-// largest buckets) and the block-table row.  Wavefront 0 finds the bucket b0
-// of the k-th largest key.  A slice whose kFSelL-th key lies below b0 has all
-// its keys of buckets >= b0 among them; the rest of any other slice is read in
-// a second round.  Keys above b0 are selected, keys in b0 are candidates.
+// Every slice left its keys sorted by bucket (the top 11 bits of the order
+// key), largest first.  One round trip reads the first kFSelL keys of every
+// slice and the block-table row; an LDS histogram of these candidates gives
+// the bucket bT of their k-th largest key.  The k-th largest key overall lies
+// in a bucket >= bT, and a slice whose kFSelL-th key lies below bT has all
+// its keys of buckets >= bT among the candidates.  The keys of buckets >= bT
+// past kFSelL in the other slices are read in a second round and join the
+// histogram, which is then exact from bT up and gives the bucket b0 of the
+// k-th largest key.  Keys above b0 are selected, keys in b0 are candidates.
 // Wavefront 0 alone then runs three 7-bit radix passes over the candidates'
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
 __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
                                              unsigned char* smem) {
-    constexpr int PER = kBins / kThreads;
-    constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;  // up-front keys per thread
-    constexpr int HB = kBins / 64;                           // histogram bins per lane of wavefront 0
+    constexpr int PER = kBins / kThreads;                    // histogram buckets per thread
+    constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
+    constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
     constexpr int WPL = kFSelMaxN / 32 / 64;                 // bitmap words per lane of wavefront 0
+    static_assert(PER == 8 && kBins / 32 == 64, "4 threads per coarse bucket, one coarse bucket per lane");
     FSelSmem& sh = *(FSelSmem*)smem;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
     int32_t* out = a.sel + (size_t)u * k;
     int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
-    unsigned* H = unit_hist(a, u);
     const uint64_t* pairs = a.spairs + (size_t)u * a.S1 * kFusedTA;
     const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
     const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
     bool btl = fast && a.max_pages <= kFSelBt;
-    auto clear_hist = [&]() {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) st_dev(H + PER * tid + i, 0u);
-        if (tid < kCoarse) st_dev(unit_coarse(a, u) + tid, 0u);
-    };
     auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
     // round trip 1
-    unsigned hv[PER];
     uint64_t pv[KQ];
-    int cv = 0;  // coarse bucket kCoarse - 1 - lane (descending over the lanes)
     if (fast) {
-        static_assert(kCoarse == 64, "one coarse bucket per lane");
-        cv = (int)ld_dev(unit_coarse(a, u) + (kCoarse - 1 - lane));
-#pragma unroll
-        for (int i = 0; i < PER; ++i) hv[i] = ld_dev(H + tid + i * kThreads);
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -350,44 +331,122 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         st_dev(ro + pos, row_of(m));
     };
     for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
-    if (!fast) clear_hist();
     if (keff == 0) return;
     if (keff == n) {
         for (int i = tid; i < n; i += kThreads) emit(i, i);
         return;
     }
-    bool general = !fast;
+    // bucket of the keff-th largest key in the LDS histogram (its counts must
+    // be exact from that bucket up), the keys above it and the keys in it.
+    // Coarse buckets of 32 (4 threads each) locate it, then its 32 buckets;
+    // every wavefront computes the same answer.
     int b0 = 0, above0 = 0, cnt0 = 0;
+    auto find_boundary = [&]() {
+        const int4 h0 = *(const int4*)&sh.uh[PER * tid], h1 = *(const int4*)&sh.uh[PER * tid + 4];
+        int cs = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
+        cs += __shfl_xor(cs, 1);
+        cs += __shfl_xor(cs, 2);
+        if ((tid & 3) == 0) sh.coarse[tid >> 2] = cs;
+        __syncthreads();
+        const int cv = sh.coarse[63 - lane];       // coarse buckets, largest first
+        const int cp = wave_prefix_incl_dpp(cv);   // keys in coarse buckets >= 63 - lane
+        const uint64_t reach = __ballot(cp >= keff);
+        if (!reach) {  // fewer than keff keys in the histogram: every bucket counts
+            b0 = 0;
+            cnt0 = 0;
+            above0 = 0;
+            return;
+        }
+        const int lc = __ffsll((unsigned long long)reach) - 1;
+        const int B0 = 63 - lc;
+        const int abovec = __builtin_amdgcn_readlane(cp, lc) - __builtin_amdgcn_readlane(cv, lc);
+        const int fv = lane < 32 ? sh.uh[32 * B0 + 31 - lane] : 0;
+        const int fp = wave_prefix_incl_dpp(fv) + abovec;
+        const int lf = __ffsll((unsigned long long)__ballot(lane < 32 && fp >= keff)) - 1;
+        b0 = 32 * B0 + 31 - lf;
+        cnt0 = __builtin_amdgcn_readlane(fv, lf);
+        above0 = __builtin_amdgcn_readlane(fp, lf) - cnt0;
+    };
+    bool general = !fast;
+    int nr2 = 0;           // second-round keys kept
+    uint32_t rk[KR];       // this thread's share of them: order key, chunk id
+    int ri[KR];
     if (fast) {
+        *(int4*)&sh.uh[PER * tid] = make_int4(0, 0, 0, 0);
+        *(int4*)&sh.uh[PER * tid + 4] = make_int4(0, 0, 0, 0);
         for (int i = tid; i < kFSelMaxN / 64; i += kThreads) sh.selbits[i] = 0ull;
         for (int i = tid; i < kFSelMaxN / 32; i += kThreads) sh.tiebits[i] = 0u;
         if (tid == 0) {
             sh.ncand = 0;
+            sh.nr2 = 0;
             sh.needmask = 0ull;
         }
-#pragma unroll
-        for (int i = 0; i < PER; ++i) sh.uh[tid + i * kThreads] = (int)hv[i];
         __syncthreads();
-        {
-            // every wavefront finds the bucket of the keff-th largest key:
-            // suffix counts of the coarse buckets, then of the 32 fine
-            // buckets of the coarse one that holds it (no barrier follows)
-            const int cp = wave_prefix_incl_dpp(cv);  // keys in coarse buckets >= 63 - lane
-            const int lc = __ffsll((unsigned long long)__ballot(cp >= keff)) - 1;
-            const int B0 = kCoarse - 1 - lc;
-            const int abovec = __builtin_amdgcn_readlane(cp, lc) - __builtin_amdgcn_readlane(cv, lc);
-            const int fv = lane < 32 ? sh.uh[32 * B0 + 31 - lane] : 0;
-            const int fp = wave_prefix_incl_dpp(fv) + abovec;
-            const int lf = __ffsll((unsigned long long)__ballot(lane < 32 && fp >= keff)) - 1;
-            b0 = 32 * B0 + 31 - lf;
-            cnt0 = __builtin_amdgcn_readlane(fv, lf);
-            above0 = __builtin_amdgcn_readlane(fp, lf) - cnt0;
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+            if (sl < nA && p < slice_n(sl)) atomicAdd(&sh.uh[(uint32_t)pv[j] >> 21], 1);
         }
-        general = cnt0 > kFSelCand;
+        __syncthreads();
+        find_boundary();  // bT: the bucket of the keff-th largest candidate
+        // a slice whose kFSelL-th key is in a bucket >= bT may hold more such keys
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+            if (p == kFSelL - 1 && sl < nA && slice_n(sl) > kFSelL && ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
+                atomicOr((unsigned long long*)&sh.needmask, 1ull << sl);
+        }
+        __syncthreads();
+        const uint64_t needmask = sh.needmask;
+        if (needmask) {
+            // round trip 2: their keys of buckets >= bT past kFSelL join the
+            // histogram and are parked in the candidate arrays
+            const uint32_t bT = (uint32_t)b0;
+            const int nneed = __popcll(needmask);
+            constexpr int R = kFusedTA - kFSelL;  // keys past kFSelL per slice
+            for (int q0 = 0; q0 < nneed * R; q0 += kThreads) {
+                const int q = q0 + tid, i = q / R, p = kFSelL + (q - i * R);
+                int sl = 0;
+                if (q < nneed * R) {
+                    uint64_t m = needmask;
+                    for (int t = 0; t < i; ++t) m &= m - 1ull;
+                    sl = __ffsll((unsigned long long)m) - 1;
+                }
+                const bool ok = q < nneed * R && p < slice_n(sl);
+                const uint64_t pr = ok ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
+                const bool keep = ok && ((uint32_t)pr >> 21) >= bT;
+                const uint64_t km = __ballot(keep);
+                int base = 0;
+                if (lane == 0 && km) base = atomicAdd(&sh.nr2, __popcll(km));
+                base = __shfl(base, 0);
+                const int at = base + __popcll(km & ((1ull << lane) - 1ull));
+                if (keep) {
+                    atomicAdd(&sh.uh[(uint32_t)pr >> 21], 1);
+                    if (at < kFSelCand) {
+                        sh.ckey[at] = (uint32_t)pr;
+                        sh.cidx[at] = (int)(pr >> 32);
+                    }
+                }
+            }
+            __syncthreads();
+            find_boundary();  // exact from bT up: b0
+            nr2 = sh.nr2;
+            if (nr2 > kFSelCand) {
+                general = true;
+            } else {
+#pragma unroll
+                for (int j = 0; j < KR; ++j) {
+                    const int q = tid + j * kThreads;
+                    rk[j] = q < nr2 ? sh.ckey[q] : 0u;
+                    ri[j] = q < nr2 ? sh.cidx[q] : 0;
+                }
+            }
+            __syncthreads();  // the candidate arrays are free
+        }
+        general = general || cnt0 > kFSelCand;
     }
     if (general) {
         // wide boundary bucket, long list or many slices: select over the keys
-        if (fast) clear_hist();  // its values are in LDS
         __syncthreads();
         btl = false;  // the select reuses the LDS
         SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
@@ -398,9 +457,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         return;
     }
     // classify one key: above b0 -> selected, in b0 -> candidate
-    auto take = [&](uint64_t pr, bool valid) {
-        const uint32_t key = (uint32_t)pr;
-        const int id = (int)(pr >> 32);
+    auto take = [&](uint32_t key, int id, bool valid) {
         const uint32_t bk = key >> 21;
         if (valid && bk > (uint32_t)b0)
             atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
@@ -430,9 +487,6 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
             }
             cm[j] = __ballot(valid && bk == (uint32_t)b0);
             wtot += __popcll(cm[j]);
-            // the slice's last up-front key still in bucket >= b0: read the rest
-            if (p == kFSelL - 1 && valid && bk >= (uint32_t)b0 && slice_n(sl) > kFSelL)
-                atomicOr((unsigned long long*)&sh.needmask, 1ull << sl);
         }
         int base = 0;
         if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
@@ -447,21 +501,11 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
             base += __popcll(cm[j]);
         }
     }
-    __syncthreads();
-    // round trip 2 (only for slices whose boundary keys run past kFSelL)
-    const uint64_t needmask = sh.needmask;
-    if (needmask) {
-        for (uint64_t m = needmask; m; m &= m - 1ull) {
-            const int sl = __ffsll((unsigned long long)m) - 1;
-            const int ns = slice_n(sl);
-            for (int p0 = kFSelL; p0 < ns; p0 += kThreads) {
-                const int p = p0 + tid;
-                const uint64_t pr = p < ns ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
-                take(pr, p < ns);
-            }
-        }
-        __syncthreads();
+    if (nr2 > 0) {
+#pragma unroll
+        for (int j = 0; j < KR; ++j) take(rk[j], ri[j], tid + j * kThreads < nr2);
     }
+    __syncthreads();
     if (w == 0) {
     // wavefront 0: radix passes over the candidates' bits [20:14], [13:7], [6:0]
     int above = above0;
@@ -543,7 +587,6 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     }
     }  // wavefront 0
     __syncthreads();
-    clear_hist();  // its values are in LDS
     // ascending output (every thread): popcount scan over the bitmap words
     constexpr int WPT = kFSelMaxN / 32 / kThreads;  // bitmap words per thread
     const int nw = (n + 31) / 32;

@@ -122,18 +122,13 @@ hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
 constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
-// Control record of one unit (words): the routing-key histogram, then the
-// counters, each in a 64-byte sector of its own.  Records are over 8 KiB
-// apart, so the counters that waiting workgroups poll spread over memory
-// channels instead of queueing on one.
-// The histogram has kBins fine buckets, then kBins/32 coarse ones (sums of 32).
-constexpr int kCoarse = kBins / 32;
-constexpr int kUnitRec = kBins + kCoarse + 64;
-__device__ inline unsigned* unit_hist(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }
-__device__ inline unsigned* unit_coarse(const Args& a, int u) { return unit_hist(a, u) + kBins; }
-__device__ inline unsigned* unit_cntA(const Args& a, int u) { return unit_hist(a, u) + kBins + kCoarse; }       // finished gist slices
-__device__ inline unsigned* unit_cntB(const Args& a, int u) { return unit_hist(a, u) + kBins + kCoarse + 16; }  // finished unfolded tasks
-__device__ inline unsigned* unit_ready(const Args& a, int u) { return unit_hist(a, u) + kBins + kCoarse + 32; } // selection published
+// Control record of one unit (words): three counters, each in a 64-byte
+// sector of its own.  Records are 8.5 KiB apart, so the counters that waiting
+// workgroups poll spread over memory channels instead of queueing on one.
+constexpr int kUnitRec = 2176;
+__device__ inline unsigned* unit_cntA(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }       // finished gist slices
+__device__ inline unsigned* unit_cntB(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 16; }  // finished unfolded tasks
+__device__ inline unsigned* unit_ready(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 32; } // selection published
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);

@@ -1,0 +1,175 @@
+"""Selection stress cases of the single-launch path, through the C ABI.
+
+The gist keys are shaped so that every branch of the select runs: slices that
+hold many of the largest keys (a second read round), fewer up-front keys than
+k, a boundary bucket wider than the candidate buffer (the general select),
+exact ties and NaN keys.  Each selection is checked exactly against the
+top-k of the GPU's own routing keys (larger key first, ties to the lower
+chunk index, NaN last), and the whole result against the oracle under the
+gap rule of the parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_gist_amd import inputs as gi
+from tests import gpu_util as GU
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def set_gist_k(inp, b, g, chunks, rows):
+    """Overwrite the gist key rows of `chunks` of unit (b, g) (pure indexing)."""
+    wl = inp.wl
+    C, spp = wl.chunk_size, wl.slots_per_page
+    bt = inp.block_table[b].long().cpu()
+    for m, r in zip(chunks, rows):
+        s = int(m) * (C + 1) + C
+        inp.k_cache[int(bt[s // spp]), g, s % spp] = r.to(inp.k_cache.dtype)
+
+
+def order_key(x):
+    """Order-preserving uint32 image of float32 keys: NaN lowest, -0 == +0."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = np.where(u == 0x80000000, 0, u)
+    k = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return np.where(np.isnan(np.asarray(x, np.float32)), 0, k)
+
+
+def exact_topk(keys, k):
+    """Ascending ids of the k largest keys: larger order key first, then lower id."""
+    ok = order_key(keys)
+    idx = np.arange(len(keys))
+    order = np.lexsort((idx, -ok.astype(np.int64)))
+    return np.sort(order[:min(k, len(keys))])
+
+
+def check_exact(wl, sel, sc, top_k, lens=None):
+    C = wl.chunk_size
+    for b in range(wl.batch):
+        n = wl.num_chunks if lens is None else lens[b] // C
+        for g in range(wl.num_kv_heads):
+            want = exact_topk(sc[b, g, :n], top_k)
+            keff = len(want)
+            got = sel[b, g, :keff]
+            assert np.array_equal(got, want), f"unit ({b},{g}): selection is not the exact top-k"
+            assert np.all(sel[b, g, keff:] == -1)
+
+
+def base(name, num_chunks, top_k, batch=2):
+    return gi.Workload(name, gi.BF16, batch, 8, 2, 128, 16, num_chunks, top_k, 16)
+
+
+def case_cluster():
+    # 100 of the largest keys in one slice of 256 gists (slice 1), the others
+    # spread: slice 1 holds more than the keys read up front
+    wl = base("sel-cluster", 1000, 100)
+    inp = gi.make_inputs(wl, 501)
+    qdir = gi.group_direction(inp.q.float(), wl.num_kv_heads)
+    gen = torch.Generator().manual_seed(7)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            ms = list(range(256, 356)) if g == 0 else list(range(5, 1000, 10))
+            noise = 0.3 * torch.randn(len(ms), wl.head_dim, generator=gen)
+            set_gist_k(inp, b, g, ms, 2.0 * math.sqrt(wl.head_dim) * qdir[b, g] + noise)
+    return wl, inp, wl.top_k
+
+
+def case_few_upfront():
+    # top_k above the keys read up front (2 slices x 32 < 200 < 300 gists)
+    wl = base("sel-few", 300, 200)
+    return wl, gi.make_inputs(wl, 502), wl.top_k
+
+
+def _all_equal(name, num_chunks, top_k, seed):
+    wl = base(name, num_chunks, top_k)
+    inp = gi.make_inputs(wl, seed)
+    gen = torch.Generator().manual_seed(seed)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            r = torch.randn(wl.head_dim, generator=gen)
+            set_gist_k(inp, b, g, range(num_chunks), r.expand(num_chunks, -1))
+    return wl, inp, top_k
+
+
+def case_ties():
+    # every key equal: the lowest chunk ids win
+    return _all_equal("sel-ties", 1000, 100, 503)
+
+
+def case_ties_wide():
+    # every key equal and more of them than the candidate buffer holds
+    return _all_equal("sel-ties-wide", 3000, 100, 504)
+
+
+def case_tie_groups():
+    # three distinct keys, each shared by about a third of the gists
+    wl = base("sel-groups", 2000, 700)
+    inp = gi.make_inputs(wl, 505)
+    gen = torch.Generator().manual_seed(505)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            vecs = torch.randn(3, wl.head_dim, generator=gen)
+            which = torch.randint(0, 3, (wl.num_chunks,), generator=gen)
+            set_gist_k(inp, b, g, range(wl.num_chunks), vecs[which])
+    return wl, inp, wl.top_k
+
+
+CASES = {"cluster": case_cluster, "few_upfront": case_few_upfront, "ties": case_ties,
+         "ties_wide": case_ties_wide, "tie_groups": case_tie_groups}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_select_stress(gpu, case):
+    say(f"[select] {case}")
+    wl, inp, top_k = CASES[case]()
+    res = GU.run_gpu(GU.to(inp, gpu), top_k=top_k)
+    out, sel, sc = res
+    check_exact(wl, sel, sc, top_k)
+    if case.startswith("ties"):
+        assert np.all(sel[:, :, :top_k] == np.arange(top_k)), "equal keys: the lowest ids win"
+    GU.check_gsa(inp, res, top_k=top_k)
+
+
+def test_select_nan_keys(gpu):
+    # NaN keys rank below every number; the selection is checked exactly (the
+    # attended NaN gists make the outputs NaN, which carry no information)
+    wl = base("sel-nan", 600, 50)
+    inp = gi.make_inputs(wl, 506)
+    gen = torch.Generator().manual_seed(506)
+    nan_ids = {}
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            ms = torch.randperm(wl.num_chunks, generator=gen)[:40].tolist()
+            nan_ids[(b, g)] = set(ms)
+            set_gist_k(inp, b, g, ms, torch.full((len(ms), wl.head_dim), float("nan")))
+    say("[select] nan")
+    out, sel, sc = GU.run_gpu(GU.to(inp, gpu), top_k=wl.top_k)
+    check_exact(wl, sel, sc, wl.top_k)
+    for (b, g), ids in nan_ids.items():
+        assert np.all(np.isnan(sc[b, g, sorted(ids)]))
+        assert not (set(sel[b, g].tolist()) & ids), "a NaN key was selected"
+
+
+def test_select_nan_fill(gpu):
+    # more NaN keys than non-NaN ones: the NaN keys fill the rest, lowest ids first
+    wl = base("sel-nan-fill", 400, 100)
+    inp = gi.make_inputs(wl, 507)
+    keep = {}
+    gen = torch.Generator().manual_seed(507)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            ms = torch.randperm(wl.num_chunks, generator=gen)[:350].tolist()
+            keep[(b, g)] = sorted(set(range(wl.num_chunks)) - set(ms))
+            set_gist_k(inp, b, g, ms, torch.full((len(ms), wl.head_dim), float("nan")))
+    say("[select] nan fill")
+    out, sel, sc = GU.run_gpu(GU.to(inp, gpu), top_k=wl.top_k)
+    check_exact(wl, sel, sc, wl.top_k)
+    for (b, g), ids in keep.items():
+        assert set(ids) <= set(sel[b, g].tolist()), "every non-NaN key must be selected"
