@@ -16,8 +16,8 @@ constexpr int kMaxGroup = 16;
 constexpr long kMaxTopK = 1L << 20;
 constexpr int kVersion = 100;  // 0.1.0
 // Control block at the start of every workspace layout: the single-launch
-// kernel's counters (first 16 KiB) and per-unit routing-key histograms, zero
-// between calls.  No layout writes scratch data below its end, so reusing one
+// kernel's error word (first 16 KiB) and per-unit records (counters and the
+// selection's row offsets), zero between calls.  No layout writes scratch data below its end, so reusing one
 // workspace across shapes keeps it zero.
 constexpr size_t kCtlWords = GSA_WORKSPACE_CONTROL_BYTES / 4;
 constexpr size_t kHdrWords = 4096;  // header: error word
@@ -38,7 +38,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, off_rowoff, total;
+        off_spairs, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -118,7 +118,8 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         long k2 = p->top_k < cc ? p->top_k : cc;
         cap2 = k2 * C + (C - 1) + k2 + (a.R - 1);
     }
-    pl.fused = pl.mfma && !pl.hier && units <= kMaxFusedUnits;
+    pl.fused = pl.mfma && !pl.hier && units <= kMaxFusedUnits &&
+               (p->top_k < M ? p->top_k : M) <= gsa::kRecRowOffs;
     const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
     const int TB = pl.fused ? gsa::kFusedTB : pl.TB;
     pl.S1 = (int)((cap1 + TA - 1) / TA);
@@ -152,8 +153,6 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_acc = off;   off += align_up(sizeof(float) * units * a.NS * a.G * a.D);
     const size_t fslices = pl.fused ? (size_t)units * pl.S1 : 0;
     pl.off_spairs = off; off += align_up(sizeof(uint64_t) * fslices * gsa::kFusedTA);
-    a.ro_stride = (int)(p->top_k < M ? p->top_k : M);
-    pl.off_rowoff = off; off += align_up(sizeof(int64_t) * (pl.fused ? units * a.ro_stride : 0));
     pl.total = off;
 }
 
@@ -238,7 +237,6 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
         pl.sc.err = ctl + 2;
         a.urec = ctl + kHdrWords;
         a.spairs = (uint64_t*)(ws + pl.off_spairs);
-        a.rowoff = (int64_t*)(ws + pl.off_rowoff);
         GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
         return GSA_OK;
     }

@@ -9,7 +9,8 @@
 //                      slice to finish runs the top-k select over the sorted
 //                      slices and publishes the selection.
 //   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
-//                      select runs, waits for the selection, attends tokens
+//                      select runs, polls its chunks' row offsets (written
+//                      by the select into the unit's record), attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
 //                      the selected chunks, raw tail, selected gists) and
 //                      writes one partial.  The unit's last one merges them
@@ -23,8 +24,10 @@
 // streaming, and the unfolded tasks of early units overlap the gist slices of
 // later ones.  Data passed between workgroups is written and read with
 // device-scope atomics (coherent across the XCDs' L2s); a producer waits for
-// its stores to complete before it bumps a counter or sets a flag, and the
-// unit's merging task returns the unit's counters to zero.
+// its stores to complete before it bumps a counter.  The selection's row
+// offsets need no such wait: each is one 64-bit word, nonzero once written,
+// that its readers poll.  The unit's merging task returns the unit's record
+// to zero.
 //
 // Select.  A wavefront issues at most one instruction every few cycles, so a
 // single workgroup that touches every key of a unit several times is slow
@@ -304,7 +307,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
     int32_t* out = a.sel + (size_t)u * k;
-    int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
+    int64_t* ro = unit_rowoff(a, u);  // one plus each selected chunk's first-row offset
     const uint64_t* pairs = a.spairs + (size_t)u * a.S1 * kFusedTA;
     const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
     const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
@@ -328,7 +331,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     };
     auto emit = [&](int pos, int m) {
         st_dev(out + pos, (int32_t)m);
-        st_dev(ro + pos, row_of(m));
+        st_dev(ro + pos, row_of(m) + 1);
     };
     for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
     if (keff == 0) return;
@@ -453,7 +456,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         block_topk_general<kThreads>(keys, nullptr, n, k, out, true, ssh);
         drain();
         __syncthreads();
-        for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)));
+        for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)) + 1);
         return;
     }
     // classify one key: above b0 -> selected, in b0 -> candidate
@@ -707,9 +710,6 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
     __builtin_amdgcn_s_setprio(2);
     for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
     select_fused(a, c, nA, keys, smem);
-    drain();
-    __syncthreads();
-    if (threadIdx.x == 0) st_dev(unit_ready(a, u), 1u);
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
@@ -804,32 +804,51 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         __syncthreads();
         fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf, gacc, fh);
     }
-    wait_at_least<8>(unit_ready(a, u), 1u, s.err);
-    __syncthreads();
     __builtin_amdgcn_s_setprio(1);  // the unit's result waits for this task
     WaveAttnL<D> wa;
     wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
     if (cnt > 0) {
-        const int64_t* ro = a.rowoff + (size_t)u * a.ro_stride;
+        // each token row: the raw tail (known), or a row of a selected chunk,
+        // whose offset the wavefront polls in the unit's record until the
+        // select has written it (one plus the offset; 0 before)
+        const int64_t* ro = unit_rowoff(a, u);
         size_t off[1][2];
         int nval[1];
         nval[0] = max(0, min(32, cnt - 32 * w));
+        int jr[2];      // selection entry of the row, -1 for a tail row
+        int64_t o[2];   // one plus the base offset, 0 while unknown
+        int64_t add[2]; // offset of the row from that base
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             // a token past the end reads the task's first row (in range)
             const int rel = 32 * w + 16 * t + lr;
             const int p = p0 + (rel < cnt ? rel : 0);
-            int64_t o;
             if (p < raw) {
-                const int j = p / C;
-                o = ld_dev(ro + j) + (int64_t)(p - j * C) * D;
+                jr[t] = p / C;
+                add[t] = (int64_t)(p - jr[t] * C) * D;
             } else if (p < raw + c.tail) {
-                o = tail_off + (int64_t)(p - raw) * D;
+                jr[t] = -1;
+                add[t] = (int64_t)(p - raw) * D;
             } else {
-                o = ld_dev(ro + (p - raw - c.tail)) + (int64_t)C * D;
+                jr[t] = p - raw - c.tail;
+                add[t] = (int64_t)C * D;
             }
-            off[0][t] = (size_t)o;
+            o[t] = jr[t] >= 0 ? ld_dev(ro + jr[t]) : tail_off + 1;
         }
+        for (unsigned it = 0; __ballot(o[0] == 0 || o[1] == 0); ++it) {
+            if (it >= kSpinLimit) {  // never expected: report, read a row in range
+                if (lane == 0) st_dev(s.err, 1u);
+                o[0] = o[0] == 0 ? 1 : o[0];
+                o[1] = o[1] == 0 ? 1 : o[1];
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (o[t] == 0) o[t] = ld_dev(ro + jr[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) off[0][t] = (size_t)(o[t] - 1 + add[t]);
         unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
         wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
                               nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, tile,
@@ -862,10 +881,11 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
             out[e] = (__bf16)((fh.m[h] == -INFINITY || L == 0.f) ? 0.f : gacc[j] / L);
         }
     }
+    // every task of the unit has read the selection: clear its row offsets
+    for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
     if (threadIdx.x == 0) {
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);
-        st_dev(unit_ready(a, u), 0u);
     }
 }
 

@@ -51,8 +51,6 @@ struct Args {
     // single-launch path only
     unsigned* urec;   // [units][kUnitRec] per-unit control records, zero between calls
     uint64_t* spairs; // [units][S1][kFusedTA] slice keys by bucket: order key | id << 32
-    int64_t* rowoff;  // [units][ro_stride] element offset of each selected chunk's first row
-    int ro_stride;    // min(top_k, num_chunks)
     uint64_t pc_inv;  // ceil(2^32 / page_chunks): chunk -> logical page by multiply
     void* out;        // [B][Hq][D]
 };
@@ -122,13 +120,18 @@ hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
 constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
-// Control record of one unit (words): three counters, each in a 64-byte
-// sector of its own.  Records are 8.5 KiB apart, so the counters that waiting
-// workgroups poll spread over memory channels instead of queueing on one.
+// Control record of one unit (words): two counters, each in a 64-byte sector
+// of its own, then from word 64 the selection's row offsets: entry i is one
+// plus the element offset of the i-th selected chunk's first raw row, 0 until
+// the select writes it (the waiting tasks poll the entries themselves).
+// Records are 8.5 KiB apart, so the words that waiting workgroups poll spread
+// over memory channels instead of queueing on one.
 constexpr int kUnitRec = 2176;
+constexpr int kRecRowOffs = 1024;  // selected chunks a record holds
+static_assert(64 + 2 * kRecRowOffs <= kUnitRec, "control record");
 __device__ inline unsigned* unit_cntA(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }       // finished gist slices
 __device__ inline unsigned* unit_cntB(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 16; }  // finished unfolded tasks
-__device__ inline unsigned* unit_ready(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 32; } // selection published
+__device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(a.urec + (size_t)u * kUnitRec + 64); }
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
