@@ -4,22 +4,27 @@
 // unit-major), then unfolded-list tasks:
 //   gist slice (u, i)  scores gists [i*TA, (i+1)*TA) of unit u, writes their
 //                      routing keys, publishes them sorted by the top 11 bits
-//                      of their order key (bucket), largest first, and
-//                      (all-gists set) one softmax partial.  The unit's last
-//                      slice to finish runs the top-k select over the sorted
-//                      slices and publishes the selection.
+//                      of their order key (bucket), largest first (the
+//                      leading ones also into the unit's record), and
+//                      (all-gists set) one softmax partial.  The unit's
+//                      next-to-last slice to finish runs the top-k select
+//                      over the sorted slices and publishes the selection.
 //   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
 //                      select runs, polls its chunks' row offsets (written
 //                      by the select into the unit's record), attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
 //                      the selected chunks, raw tail, selected gists) and
-//                      writes one partial.  The unit's last one merges them
-//                      into the output and resets the unit's counters.
-// Only unfolded tasks wait, and only on gist-slice tasks, which have smaller
-// workgroup ids: the device dispatches each XCD's workgroups in id order, so
-// every slice a waiting task depends on has been dispatched and runs to
-// completion (it never waits).  A wait is nevertheless bounded; giving up
-// sets the error word of the control block.  Several workgroups per CU hide
+//                      writes one partial.  The unit's last one to finish
+//                      merges them into the output and returns the unit's
+//                      record to zero.
+// Waits: unfolded tasks on gist slices (smaller workgroup ids), and the
+// selecting slice of a unit on the unit's other slices.  The device
+// dispatches each XCD's workgroups in id order, and ids run gist slices
+// first, unit by unit, so the workgroups queued ahead of an awaited slice
+// have smaller ids: slices that wait on nothing, or the one selecting slice
+// of an earlier unit (or of the same unit, already running).  By induction
+// over units every awaited slice is dispatched and every wait ends.  A wait is
+// nevertheless bounded; giving up sets the error word of the control block.  Several workgroups per CU hide
 // each task's serial latencies (table lookups, drains) behind the others'
 // streaming, and the unfolded tasks of early units overlap the gist slices of
 // later ones.  Data passed between workgroups is written and read with
@@ -44,11 +49,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 24;
-constexpr int kFSelMaxSlices = 64;   // slices the bucketed select merges
+constexpr int kFSelMaxSlices = kRecSlices;  // slices the bucketed select merges
 constexpr int kFSelMaxN = 16384;     // gists per unit the bucketed select handles
 constexpr int kFSelBt = 1024;        // block-table entries the select keeps in LDS
 constexpr int kFSelCand = 2048;      // largest boundary bucket (else the general select)
-constexpr int kFSelL = 32;           // keys per slice the select reads up front
+constexpr int kFSelL = kRecLead;     // keys per slice the select reads up front
 
 __device__ inline void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,9 +112,9 @@ __device__ inline void wait_at_least(const unsigned* p, unsigned target, unsigne
 // Folding state of one partial: per-head running max (exp2 domain) and sum,
 // and the factors of the round being folded.
 constexpr int kFoldRound = 16;  // partials folded per round
-struct FoldHdr {
+struct __attribute__((aligned(16))) FoldHdr {
     float m[16], l[16], f_self[16], fg[16], fb[16];
-    float f[kFoldRound][16];
+    float f[16][kFoldRound];  // [head][slot of the round]
 };
 
 // LDS of the top-k select (last gist slice of a unit).
@@ -188,7 +193,7 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
             const float fself = mold == -INFINITY ? 0.f : exp2f(mold - M);
             const float L = lold * fself + rowsum16(y * fi);
             if (h < G) {
-                fh.f[i][h] = fi;
+                fh.f[h][i] = fi;
                 if (i == 0) {
                     fh.f_self[h] = fself;
                     fh.m[h] = M;
@@ -202,9 +207,18 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
             const int e = threadIdx.x + j * kThreads;
             if (e < GD) {
                 const int h = e / a.D;
+                float f[NR];  // the head's factors, 16 bytes per LDS read
+#pragma unroll
+                for (int q = 0; q < NR / 4; ++q) {
+                    const float4 v = ((const float4*)fh.f[h])[q];
+                    f[4 * q] = v.x;
+                    f[4 * q + 1] = v.y;
+                    f[4 * q + 2] = v.z;
+                    f[4 * q + 3] = v.w;
+                }
                 float x = acc[j] * fh.f_self[h];
 #pragma unroll
-                for (int i = 0; i < HR; ++i) x += va[j][i] * fh.f[i][h] + vb[j][i] * fh.f[HR + i][h];
+                for (int i = 0; i < HR; ++i) x += va[j][i] * f[i] + vb[j][i] * f[HR + i];
                 acc[j] = x;
             }
         }
@@ -216,9 +230,10 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
 // position in the slice, -1: none).  Publishes the keys (order key | chunk id
 // << 32) in descending bucket order, staged in LDS and written as whole
 // contiguous lines (the stores write through to memory, and a partially
-// written line costs the memory a read-modify-write).
+// written line costs the memory a read-modify-write); with `lead`, also the
+// first kFSelL of them into the unit's record.
 __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
-                             unsigned char* smem, int* wsum) {
+                             bool lead, unsigned char* smem, int* wsum) {
     constexpr int PER = kBins / kThreads;  // consecutive buckets per thread
     int* hist = (int*)smem;
     uint64_t* pair_st = (uint64_t*)(smem + kBins * 4);  // kFusedTA pairs
@@ -255,6 +270,8 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
     __syncthreads();
     static_assert(kFusedTA == kThreads, "one pair per thread");
     if (tid < tot) st_dev(a.spairs + ((size_t)u * a.S1 + idx) * kFusedTA + tid, pair_st[tid]);
+    // the leading keys again, into the unit's record, id + 1: nonzero once written
+    if (lead && tid < min(tot, kFSelL)) st_dev(unit_lead(a, u) + idx * kFSelL + tid, pair_st[tid] + (1ull << 32));
     __syncthreads();
 }
 
@@ -296,8 +313,8 @@ __device__ inline int wave_prefix_excl(int x) {
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
-__device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, int nA, const float* keys,
-                                             unsigned char* smem) {
+__device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int nA,
+                                             const float* keys, unsigned char* smem) {
     constexpr int PER = kBins / kThreads;                    // histogram buckets per thread
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
@@ -309,21 +326,49 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     int32_t* out = a.sel + (size_t)u * k;
     int64_t* ro = unit_rowoff(a, u);  // one plus each selected chunk's first-row offset
     const uint64_t* pairs = a.spairs + (size_t)u * a.S1 * kFusedTA;
+    const uint64_t* lead = unit_lead(a, u);
     const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
     const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
     bool btl = fast && a.max_pages <= kFSelBt;
     auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
-    // round trip 1
+    // everything but the leading keys waits for every slice to be done
+    auto wait_slices = [&]() {
+        wait_at_least<8>(unit_cntA(a, u), (unsigned)nA, sc.err);
+        __syncthreads();
+    };
+    if (!fast && n > 0) wait_slices();
+    // round trip 1: the slices' leading keys, polled (the last slice may
+    // still be writing its own); 1 << 32 marks an unused slot
     uint64_t pv[KQ];
     if (fast) {
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            pv[j] = (sl < nA && p < slice_n(sl)) ? ld_dev(pairs + (size_t)sl * kFusedTA + p) : 0ull;
+            pv[j] = (sl < nA && p < slice_n(sl)) ? ld_dev(lead + q) : (1ull << 32);
         }
     }
     if (btl)
         for (int i = tid; i < a.max_pages; i += kThreads) sh.bt[i] = btrow[i];
+    if (fast) {
+        for (unsigned it = 0;; ++it) {
+            bool miss = false;
+#pragma unroll
+            for (int j = 0; j < KQ; ++j) miss |= pv[j] == 0ull;
+            if (!__ballot(miss)) break;
+            if (it >= kSpinLimit) {  // never expected: report, continue with chunk 0
+                if (lane == 0) st_dev(sc.err, 1u);
+#pragma unroll
+                for (int j = 0; j < KQ; ++j) pv[j] = pv[j] ? pv[j] : (1ull << 32);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+            for (int j = 0; j < KQ; ++j)
+                if (pv[j] == 0ull) pv[j] = ld_dev(lead + tid + j * kThreads);
+        }
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) pv[j] -= 1ull << 32;
+    }
     auto row_of = [&](int m) -> int64_t {  // element offset of chunk m's first raw row
         const int lp = chunk_page(a, m);
         const int phys = btl ? sh.bt[lp] : btrow[lp];
@@ -334,10 +379,10 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         st_dev(ro + pos, row_of(m) + 1);
     };
     for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
-    if (keff == 0) return;
+    if (keff == 0) return fast;
     if (keff == n) {
         for (int i = tid; i < n; i += kThreads) emit(i, i);
-        return;
+        return fast;
     }
     // bucket of the keff-th largest key in the LDS histogram (its counts must
     // be exact from that bucket up), the keys above it and the keys in it.
@@ -404,6 +449,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         if (needmask) {
             // round trip 2: their keys of buckets >= bT past kFSelL join the
             // histogram and are parked in the candidate arrays
+            wait_slices();
             const uint32_t bT = (uint32_t)b0;
             const int nneed = __popcll(needmask);
             constexpr int R = kFusedTA - kFSelL;  // keys past kFSelL per slice
@@ -450,6 +496,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     }
     if (general) {
         // wide boundary bucket, long list or many slices: select over the keys
+        if (fast) wait_slices();  // (else done above)
         __syncthreads();
         btl = false;  // the select reuses the LDS
         SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
@@ -457,7 +504,7 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
         drain();
         __syncthreads();
         for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)) + 1);
-        return;
+        return fast;
     }
     // classify one key: above b0 -> selected, in b0 -> candidate
     auto take = [&](uint32_t key, int id, bool valid) {
@@ -603,15 +650,22 @@ __device__ __forceinline__ void select_fused(const Args& a, const ListCtx& c, in
     }
     int tot;
     int pos = block_excl_scan<kThreads>(c2, &tot, sh.wsum);
+    // the ids in ascending order into LDS (the candidate arrays are free),
+    // then an even share of the outputs per thread
+    static_assert(kRecRowOffs <= kFSelCand, "the selection fits the candidate arrays");
+    int* ids = (int*)sh.ckey;
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
         uint32_t x = sb[i];
         while (x) {
             const int bit = __ffs(x) - 1;
             x &= x - 1u;
-            emit(pos++, (WPT * tid + i) * 32 + bit);
+            ids[pos++] = (WPT * tid + i) * 32 + bit;
         }
     }
+    __syncthreads();
+    for (int i = tid; i < keff; i += kThreads) emit(i, ids[i]);
+    return fast;
 }
 
 template <int D>
@@ -686,7 +740,7 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
         const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
         __syncthreads();  // the tiles are free
-        bucket_slice(a, u, idx, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+        bucket_slice(a, u, idx, p0, kv, kpos < cnt ? kpos : -1, nA <= kRecSlices, smem, wsum);
         if (attn) {
             const size_t pbase = ((size_t)u * a.NS + idx) * G;
             combine_waves<D>(
@@ -701,15 +755,26 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
     }
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntA(a, u), 1u) == (unsigned)(nA - 1);
+    // the next-to-last slice to finish selects (the only one with nA == 1):
+    // it polls the last slice's leading keys instead of waiting for its count
+    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntA(a, u), 1u) == (unsigned)(nA >= 2 ? nA - 2 : 0);
     __syncthreads();
     if (!*s_flag) return;
 
-    // last slice of the unit: select and publish (ahead of the streaming
-    // workgroups sharing this CU: everything of the unit waits for it)
+    // select and publish (ahead of the streaming workgroups sharing this CU:
+    // everything of the unit waits for it)
     __builtin_amdgcn_s_setprio(2);
     for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    select_fused(a, c, nA, keys, smem);
+    select_fused(a, s, c, nA, keys, smem);
+    // return the leading keys in the record to zero: each has been read by the
+    // select, or every slice is done (the select waited for it)
+    if (nA <= kRecSlices) {
+        uint64_t* lead = unit_lead(a, u);
+        for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
+            const int sl = i / kFSelL;
+            if (i - sl * kFSelL < min(kFusedTA, c.n - sl * kFusedTA)) st_dev(lead + i, 0ull);
+        }
+    }
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
@@ -862,7 +927,8 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     __syncthreads();
     if (!*s_flag) return;
 
-    // last unfolded task of the unit: merge and reset the unit's counters
+    // the last unfolded task of the unit: merge, write the output, return the
+    // unit's record to zero
 #pragma unroll
     for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
     if (threadIdx.x < 16) {

@@ -120,18 +120,25 @@ hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
 constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
-// Control record of one unit (words): two counters, each in a 64-byte sector
-// of its own, then from word 64 the selection's row offsets: entry i is one
-// plus the element offset of the i-th selected chunk's first raw row, 0 until
-// the select writes it (the waiting tasks poll the entries themselves).
-// Records are 8.5 KiB apart, so the words that waiting workgroups poll spread
-// over memory channels instead of queueing on one.
-constexpr int kUnitRec = 2176;
+// Control record of one unit (words): the counts of finished gist slices and
+// unfolded tasks, each in a 64-byte sector of its own; from word 64 the selection's row offsets (entry i: one plus the
+// element offset of the i-th selected chunk's first raw row); from word
+// 64 + 2*kRecRowOffs the leading keys of every gist slice (kRecLead per
+// slice: order key | (chunk id + 1) << 32).  An entry is 0 until written, and
+// its readers poll it; the unit's last tasks return every entry to 0.
+// Records are 24.5 KiB apart, so the words that waiting workgroups poll
+// spread over memory channels instead of queueing on one.
 constexpr int kRecRowOffs = 1024;  // selected chunks a record holds
-static_assert(64 + 2 * kRecRowOffs <= kUnitRec, "control record");
+constexpr int kRecSlices = 64;     // gist slices whose leading keys a record holds
+constexpr int kRecLead = 32;       // leading keys per slice
+constexpr int kUnitRec = 6272;
+static_assert(64 + 2 * kRecRowOffs + 2 * kRecSlices * kRecLead <= kUnitRec, "control record");
 __device__ inline unsigned* unit_cntA(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }       // finished gist slices
 __device__ inline unsigned* unit_cntB(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 16; }  // finished unfolded tasks
 __device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(a.urec + (size_t)u * kUnitRec + 64); }
+__device__ inline uint64_t* unit_lead(const Args& a, int u) {
+    return (uint64_t*)(a.urec + (size_t)u * kUnitRec + 64 + 2 * kRecRowOffs);
+}
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);

@@ -173,3 +173,17 @@ def test_select_nan_fill(gpu):
     check_exact(wl, sel, sc, wl.top_k)
     for (b, g), ids in keep.items():
         assert set(ids) <= set(sel[b, g].tolist()), "every non-NaN key must be selected"
+
+
+@pytest.mark.parametrize("top_k, tail, tasks", [(504, 5, 64), (600, 3, 76), (63, 0, 8)])
+def test_unfolded_task_counts(gpu, top_k, tail, tasks):
+    # many unfolded tasks per unit (their partials all merge into one output),
+    # with ragged and exact last tasks
+    wl = gi.Workload("many-tasks", gi.BF16, 1, 4, 2, 128, 16, 600, top_k, 16)
+    L = wl.num_chunks * wl.chunk_size + tail
+    inp = gi.make_inputs(wl, 600 + tasks, seq_lens=[L])
+    assert -(-(top_k * wl.chunk_size + tail) // 128) == tasks
+    say(f"[select] unfolded tasks {tasks}")
+    res = GU.run_gpu(GU.to(inp, gpu), top_k=top_k)
+    check_exact(wl, res[1], res[2], top_k, lens=[L])
+    GU.check_gsa(inp, res, top_k=top_k)
