@@ -275,28 +275,6 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
     __syncthreads();
 }
 
-// Sum of x over the lanes of a wavefront at or above this lane.
-__device__ inline int wave_suffix_incl(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(x, off);
-        if (lane + off < 64) x += y;
-    }
-    return x;
-}
-// Sum of x over the lanes of a wavefront below this lane.
-__device__ inline int wave_prefix_excl(int x) {
-    const int lane = threadIdx.x & 63;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    return incl - x;
-}
-
 // Top-k of unit u (ascending chunk ids, -1 padded) and each selected chunk's
 // first-row offset.  nA: gist slices of the unit, keys: the routing keys.
 //
@@ -315,11 +293,11 @@ __device__ inline int wave_prefix_excl(int x) {
 // the candidates are few.
 __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int nA,
                                              const float* keys, unsigned char* smem) {
-    constexpr int PER = kBins / kThreads;                    // histogram buckets per thread
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
-    constexpr int WPL = kFSelMaxN / 32 / 64;                 // bitmap words per lane of wavefront 0
-    static_assert(PER == 8 && kBins / 32 == 64, "4 threads per coarse bucket, one coarse bucket per lane");
+    constexpr int WPL = kFSelMaxN / 32 / 64;                 // 32-bit bitmap words per lane of wavefront 0
+    static_assert(kBins == 64 * 32, "64 coarse buckets of 32");
+    static_assert(kFSelMaxN / 64 == kThreads, "one 64-bit bitmap word per thread");
     FSelSmem& sh = *(FSelSmem*)smem;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
@@ -350,6 +328,16 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     if (btl)
         for (int i = tid; i < a.max_pages; i += kThreads) sh.bt[i] = btrow[i];
     if (fast) {
+        // clear the LDS state while the keys are in flight
+        *(int4*)&sh.uh[8 * tid] = make_int4(0, 0, 0, 0);
+        *(int4*)&sh.uh[8 * tid + 4] = make_int4(0, 0, 0, 0);
+        sh.selbits[tid] = 0ull;
+        for (int i = tid; i < kFSelMaxN / 32; i += kThreads) sh.tiebits[i] = 0u;
+        if (tid == 0) {
+            sh.ncand = 0;
+            sh.nr2 = 0;
+            sh.needmask = 0ull;
+        }
         for (unsigned it = 0;; ++it) {
             bool miss = false;
 #pragma unroll
@@ -384,19 +372,20 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         for (int i = tid; i < n; i += kThreads) emit(i, i);
         return fast;
     }
-    // bucket of the keff-th largest key in the LDS histogram (its counts must
-    // be exact from that bucket up), the keys above it and the keys in it.
-    // Coarse buckets of 32 (4 threads each) locate it, then its 32 buckets;
-    // every wavefront computes the same answer.
+    // bucket b0 of the keff-th largest key in the LDS histogram (whose counts
+    // must be exact from that bucket up), the keys above it and in it.  Every
+    // wavefront sums the 64 coarse buckets of 32 itself (lane l: coarse bucket
+    // 63 - l, its 16-byte reads staggered over the banks) and scans them, then
+    // the 32 buckets of the coarse one holding it: no barrier.
     int b0 = 0, above0 = 0, cnt0 = 0;
     auto find_boundary = [&]() {
-        const int4 h0 = *(const int4*)&sh.uh[PER * tid], h1 = *(const int4*)&sh.uh[PER * tid + 4];
-        int cs = h0.x + h0.y + h0.z + h0.w + h1.x + h1.y + h1.z + h1.w;
-        cs += __shfl_xor(cs, 1);
-        cs += __shfl_xor(cs, 2);
-        if ((tid & 3) == 0) sh.coarse[tid >> 2] = cs;
-        __syncthreads();
-        const int cv = sh.coarse[63 - lane];       // coarse buckets, largest first
+        const int4* hp = (const int4*)&sh.uh[32 * (63 - lane)];
+        int cv = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int4 h = hp[(i + lane) & 7];
+            cv += h.x + h.y + h.z + h.w;
+        }
         const int cp = wave_prefix_incl_dpp(cv);   // keys in coarse buckets >= 63 - lane
         const uint64_t reach = __ballot(cp >= keff);
         if (!reach) {  // fewer than keff keys in the histogram: every bucket counts
@@ -415,21 +404,32 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         cnt0 = __builtin_amdgcn_readlane(fv, lf);
         above0 = __builtin_amdgcn_readlane(fp, lf) - cnt0;
     };
-    bool general = !fast;
-    int nr2 = 0;           // second-round keys kept
-    uint32_t rk[KR];       // this thread's share of them: order key, chunk id
-    int ri[KR];
-    if (fast) {
-        *(int4*)&sh.uh[PER * tid] = make_int4(0, 0, 0, 0);
-        *(int4*)&sh.uh[PER * tid + 4] = make_int4(0, 0, 0, 0);
-        for (int i = tid; i < kFSelMaxN / 64; i += kThreads) sh.selbits[i] = 0ull;
-        for (int i = tid; i < kFSelMaxN / 32; i += kThreads) sh.tiebits[i] = 0u;
-        if (tid == 0) {
-            sh.ncand = 0;
-            sh.nr2 = 0;
-            sh.needmask = 0ull;
+    // one key against b0: above -> selected, in b0 -> candidate (slots taken
+    // with one LDS atomic per wavefront)
+    auto take = [&](uint32_t key, int id, bool valid) {
+        const uint32_t bk = key >> 21;
+        if (valid && bk > (uint32_t)b0)
+            atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+        const bool cand = valid && bk == (uint32_t)b0;
+        const uint64_t m = __ballot(cand);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(&sh.ncand, __popcll(m));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const int ci = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (cand && ci < kFSelCand) {
+            sh.ckey[ci] = key;
+            sh.cidx[ci] = id;
         }
-        __syncthreads();
+    };
+    auto take_upfront = [&]() {
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+            take((uint32_t)pv[j], (int)(pv[j] >> 32), sl < nA && p < slice_n(sl));
+        }
+    };
+    bool general = !fast;
+    if (fast) {
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -437,7 +437,9 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         }
         __syncthreads();
         find_boundary();  // bT: the bucket of the keff-th largest candidate
-        // a slice whose kFSelL-th key is in a bucket >= bT may hold more such keys
+        // classify against bT; a slice whose kFSelL-th key is in a bucket >= bT
+        // may hold more such keys: then a second round, and classify again
+        take_upfront();
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -447,10 +449,12 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         __syncthreads();
         const uint64_t needmask = sh.needmask;
         if (needmask) {
-            // round trip 2: their keys of buckets >= bT past kFSelL join the
-            // histogram and are parked in the candidate arrays
-            wait_slices();
+            // round trip 2: the keys of buckets >= bT past kFSelL of those
+            // slices join the histogram and are parked in the candidate arrays
             const uint32_t bT = (uint32_t)b0;
+            sh.selbits[tid] = 0ull;
+            if (tid == 0) sh.ncand = 0;
+            wait_slices();
             const int nneed = __popcll(needmask);
             constexpr int R = kFusedTA - kFSelL;  // keys past kFSelL per slice
             for (int q0 = 0; q0 < nneed * R; q0 += kThreads) {
@@ -467,7 +471,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 const uint64_t km = __ballot(keep);
                 int base = 0;
                 if (lane == 0 && km) base = atomicAdd(&sh.nr2, __popcll(km));
-                base = __shfl(base, 0);
+                base = __builtin_amdgcn_readfirstlane(base);
                 const int at = base + __popcll(km & ((1ull << lane) - 1ull));
                 if (keep) {
                     atomicAdd(&sh.uh[(uint32_t)pr >> 21], 1);
@@ -479,24 +483,30 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             }
             __syncthreads();
             find_boundary();  // exact from bT up: b0
-            nr2 = sh.nr2;
+            const int nr2 = sh.nr2;
             if (nr2 > kFSelCand) {
                 general = true;
             } else {
+                uint32_t rk[KR];  // this thread's share of the parked keys
+                int ri[KR];
 #pragma unroll
                 for (int j = 0; j < KR; ++j) {
                     const int q = tid + j * kThreads;
                     rk[j] = q < nr2 ? sh.ckey[q] : 0u;
                     ri[j] = q < nr2 ? sh.cidx[q] : 0;
                 }
+                __syncthreads();  // the candidate arrays are free
+                take_upfront();
+#pragma unroll
+                for (int j = 0; j < KR; ++j) take(rk[j], ri[j], tid + j * kThreads < nr2);
+                __syncthreads();
             }
-            __syncthreads();  // the candidate arrays are free
         }
         general = general || cnt0 > kFSelCand;
     }
     if (general) {
         // wide boundary bucket, long list or many slices: select over the keys
-        if (fast) wait_slices();  // (else done above)
+        if (fast && !sh.needmask) wait_slices();  // (else done above)
         __syncthreads();
         btl = false;  // the select reuses the LDS
         SelectSmem<kThreads>& ssh = *(SelectSmem<kThreads>*)smem;
@@ -506,163 +516,112 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)) + 1);
         return fast;
     }
-    // classify one key: above b0 -> selected, in b0 -> candidate
-    auto take = [&](uint32_t key, int id, bool valid) {
-        const uint32_t bk = key >> 21;
-        if (valid && bk > (uint32_t)b0)
-            atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
-        const bool cand = valid && bk == (uint32_t)b0;
-        const uint64_t m = __ballot(cand);
-        int base = 0;
-        if (lane == 0 && m) base = atomicAdd(&sh.ncand, __popcll(m));
-        base = __shfl(base, 0);
-        const int ci = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (cand && ci < kFSelCand) {
-            sh.ckey[ci] = key;
-            sh.cidx[ci] = id;
-        }
-    };
-    {
-        // up-front keys: one LDS atomic per wavefront reserves its candidate slots
-        uint64_t cm[KQ];
-        int wtot = 0;
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) {
-            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            const bool valid = sl < nA && p < slice_n(sl);
-            const uint32_t bk = (uint32_t)pv[j] >> 21;
-            if (valid && bk > (uint32_t)b0) {
-                const int id = (int)(pv[j] >> 32);
-                atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
-            }
-            cm[j] = __ballot(valid && bk == (uint32_t)b0);
-            wtot += __popcll(cm[j]);
-        }
-        int base = 0;
-        if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
-        base = __shfl(base, 0);
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) {
-            const int ci = base + __popcll(cm[j] & ((1ull << lane) - 1ull));
-            if (((cm[j] >> lane) & 1ull) && ci < kFSelCand) {
-                sh.ckey[ci] = (uint32_t)pv[j];
-                sh.cidx[ci] = (int)(pv[j] >> 32);
-            }
-            base += __popcll(cm[j]);
-        }
-    }
-    if (nr2 > 0) {
-#pragma unroll
-        for (int j = 0; j < KR; ++j) take(rk[j], ri[j], tid + j * kThreads < nr2);
-    }
-    __syncthreads();
+    int* ids = (int*)sh.ckey;  // the selection, ascending (written by wavefront 0)
+    static_assert(kRecRowOffs <= kFSelCand, "the selection fits the candidate arrays");
     if (w == 0) {
-    // wavefront 0: radix passes over the candidates' bits [20:14], [13:7], [6:0]
-    int above = above0;
-    uint32_t prefix = (uint32_t)b0 << 21;
-    int fixed = 11;
-    bool take_all = above + cnt0 == keff;
-    for (int pass = 0; pass < 3 && !take_all; ++pass) {
-        const int shift = 14 - 7 * pass;
-        sh.hist[lane] = 0;
-        sh.hist[lane + 64] = 0;
-        lds_fence();
+        // wavefront 0: radix passes over the candidates' bits [20:14], [13:7], [6:0]
+        int above = above0;
+        uint32_t prefix = (uint32_t)b0 << 21;
+        int fixed = 11;
+        bool take_all = above + cnt0 == keff;
+        for (int pass = 0; pass < 3 && !take_all; ++pass) {
+            const int shift = 14 - 7 * pass;
+            sh.hist[lane] = 0;
+            sh.hist[lane + 64] = 0;
+            lds_fence();
+            for (int ci = lane; ci < cnt0; ci += 64) {
+                const uint32_t x = sh.ckey[ci];
+                if ((x >> (32 - fixed)) == (prefix >> (32 - fixed))) atomicAdd(&sh.hist[(x >> shift) & 127u], 1);
+            }
+            lds_fence();
+            const int h0 = sh.hist[2 * lane], h1 = sh.hist[2 * lane + 1];
+            const int s2 = h0 + h1;
+            const int pi = wave_prefix_incl_dpp(s2);
+            const int higher = __builtin_amdgcn_readlane(pi, 63) - pi;  // keys in higher digit pairs
+            const int need = keff - above;
+            const bool mine = higher < need && higher + s2 >= need;
+            int bsel = 0, abv = 0, cn = 0;
+            if (mine) {
+                if (higher + h1 >= need) {
+                    bsel = 2 * lane + 1;
+                    abv = higher;
+                    cn = h1;
+                } else {
+                    bsel = 2 * lane;
+                    abv = higher + h1;
+                    cn = h0;
+                }
+            }
+            const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+            bsel = __builtin_amdgcn_readlane(bsel, src);
+            abv = __builtin_amdgcn_readlane(abv, src);
+            cn = __builtin_amdgcn_readlane(cn, src);
+            above += abv;
+            prefix |= (uint32_t)bsel << shift;
+            fixed += 7;
+            if (above + cn == keff) take_all = true;
+        }
+        const uint32_t lo = prefix;
+        const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
         for (int ci = lane; ci < cnt0; ci += 64) {
             const uint32_t x = sh.ckey[ci];
-            if ((x >> (32 - fixed)) == (prefix >> (32 - fixed))) atomicAdd(&sh.hist[(x >> shift) & 127u], 1);
+            const int id = sh.cidx[ci];
+            if (x > hi || (take_all && x >= lo))
+                atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+            else if (x >= lo)
+                atomicOr(&sh.tiebits[id >> 5], 1u << (id & 31));
         }
         lds_fence();
-        const int h0 = sh.hist[2 * lane], h1 = sh.hist[2 * lane + 1];
-        const int s2 = h0 + h1;
-        const int higher = wave_suffix_incl(s2) - s2;
-        const int need = keff - above;
-        const bool mine = higher < need && higher + s2 >= need;
-        int bsel = 0, abv = 0, cn = 0;
-        if (mine) {
-            if (higher + h1 >= need) {
-                bsel = 2 * lane + 1;
-                abv = higher;
-                cn = h1;
-            } else {
-                bsel = 2 * lane;
-                abv = higher + h1;
-                cn = h0;
+        if (!take_all) {
+            const int nw = (n + 31) / 32;
+            // the (keff - above) lowest-index keys equal to the k-th largest
+            const int need_eq = keff - above;
+            uint32_t tb[WPL];
+            int c1 = 0;
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const int wd = WPL * lane + i;
+                tb[i] = wd < nw ? sh.tiebits[wd] : 0u;
+                c1 += __popc(tb[i]);
+            }
+            int before = wave_prefix_incl_dpp(c1) - c1;
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                uint32_t add = 0u, rest = tb[i];
+                while (rest && before < need_eq) {
+                    const uint32_t bit = rest & (~rest + 1u);
+                    add |= bit;
+                    rest ^= bit;
+                    ++before;
+                }
+                const int wd = WPL * lane + i;
+                if (add) atomicOr((unsigned long long*)&sh.selbits[wd >> 1], (uint64_t)add << (32 * (wd & 1)));
+            }
+            lds_fence();
+        }
+        // the selection in ascending order: a popcount scan over the bitmap
+        // (the candidate arrays are free now)
+        constexpr int WL = kFSelMaxN / 64 / 64;  // 64-bit bitmap words per lane
+        const int nw64 = (n + 63) / 64;
+        uint64_t sb[WL];
+        int c2 = 0;
+#pragma unroll
+        for (int i = 0; i < WL; ++i) {
+            const int wd = WL * lane + i;
+            sb[i] = wd < nw64 ? sh.selbits[wd] : 0ull;
+            c2 += __popcll(sb[i]);
+        }
+        int pos = wave_prefix_incl_dpp(c2) - c2;
+#pragma unroll
+        for (int i = 0; i < WL; ++i) {
+            uint64_t x = sb[i];
+            while (x) {
+                const int bit = __ffsll((unsigned long long)x) - 1;
+                x &= x - 1ull;
+                ids[pos++] = (WL * lane + i) * 64 + bit;
             }
         }
-        const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-        bsel = __shfl(bsel, src);
-        abv = __shfl(abv, src);
-        cn = __shfl(cn, src);
-        above += abv;
-        prefix |= (uint32_t)bsel << shift;
-        fixed += 7;
-        if (above + cn == keff) take_all = true;
-    }
-    const uint32_t lo = prefix;
-    const uint32_t hi = fixed >= 32 ? prefix : (prefix | ((1u << (32 - fixed)) - 1u));
-    for (int ci = lane; ci < cnt0; ci += 64) {
-        const uint32_t x = sh.ckey[ci];
-        const int id = sh.cidx[ci];
-        if (x > hi || (take_all && x >= lo))
-            atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
-        else if (x >= lo)
-            atomicOr(&sh.tiebits[id >> 5], 1u << (id & 31));
-    }
-    lds_fence();
-    if (!take_all) {
-        const int nw = (n + 31) / 32;
-        // the (keff - above) lowest-index keys equal to the k-th largest
-        const int need_eq = keff - above;
-        uint32_t tb[WPL];
-        int c1 = 0;
-#pragma unroll
-        for (int i = 0; i < WPL; ++i) {
-            const int wd = WPL * lane + i;
-            tb[i] = wd < nw ? sh.tiebits[wd] : 0u;
-            c1 += __popc(tb[i]);
-        }
-        int before = wave_prefix_excl(c1);
-#pragma unroll
-        for (int i = 0; i < WPL; ++i) {
-            uint32_t add = 0u, rest = tb[i];
-            while (rest && before < need_eq) {
-                const uint32_t bit = rest & (~rest + 1u);
-                add |= bit;
-                rest ^= bit;
-                ++before;
-            }
-            const int wd = WPL * lane + i;
-            if (add) atomicOr((unsigned long long*)&sh.selbits[wd >> 1], (uint64_t)add << (32 * (wd & 1)));
-        }
-    }
     }  // wavefront 0
-    __syncthreads();
-    // ascending output (every thread): popcount scan over the bitmap words
-    constexpr int WPT = kFSelMaxN / 32 / kThreads;  // bitmap words per thread
-    const int nw = (n + 31) / 32;
-    uint32_t sb[WPT];
-    int c2 = 0;
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-        const int wd = WPT * tid + i;
-        sb[i] = wd < nw ? (uint32_t)(sh.selbits[wd >> 1] >> (32 * (wd & 1))) : 0u;
-        c2 += __popc(sb[i]);
-    }
-    int tot;
-    int pos = block_excl_scan<kThreads>(c2, &tot, sh.wsum);
-    // the ids in ascending order into LDS (the candidate arrays are free),
-    // then an even share of the outputs per thread
-    static_assert(kRecRowOffs <= kFSelCand, "the selection fits the candidate arrays");
-    int* ids = (int*)sh.ckey;
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-        uint32_t x = sb[i];
-        while (x) {
-            const int bit = __ffs(x) - 1;
-            x &= x - 1u;
-            ids[pos++] = (WPT * tid + i) * 32 + bit;
-        }
-    }
     __syncthreads();
     for (int i = tid; i < keff; i += kThreads) emit(i, ids[i]);
     return fast;
