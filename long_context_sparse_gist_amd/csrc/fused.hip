@@ -421,11 +421,34 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             sh.cidx[ci] = id;
         }
     };
+    // the up-front keys: one LDS atomic per wavefront reserves all their
+    // candidate slots
     auto take_upfront = [&]() {
+        uint64_t cm[KQ];
+        int wtot = 0;
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            take((uint32_t)pv[j], (int)(pv[j] >> 32), sl < nA && p < slice_n(sl));
+            const bool valid = sl < nA && p < slice_n(sl);
+            const uint32_t bk = (uint32_t)pv[j] >> 21;
+            if (valid && bk > (uint32_t)b0) {
+                const int id = (int)(pv[j] >> 32);
+                atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
+            }
+            cm[j] = __ballot(valid && bk == (uint32_t)b0);
+            wtot += __popcll(cm[j]);
+        }
+        int base = 0;
+        if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
+        base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int ci = base + __popcll(cm[j] & ((1ull << lane) - 1ull));
+            if (((cm[j] >> lane) & 1ull) && ci < kFSelCand) {
+                sh.ckey[ci] = (uint32_t)pv[j];
+                sh.cidx[ci] = (int)(pv[j] >> 32);
+            }
+            base += __popcll(cm[j]);
         }
     };
     bool general = !fast;
