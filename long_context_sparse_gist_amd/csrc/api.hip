@@ -38,7 +38,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, total;
+        off_spairs, off_spairs_c, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -118,16 +118,22 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         long k2 = p->top_k < cc ? p->top_k : cc;
         cap2 = k2 * C + (C - 1) + k2 + (a.R - 1);
     }
-    pl.fused = pl.mfma && !pl.hier && units <= kMaxFusedUnits &&
-               (p->top_k < M ? p->top_k : M) <= gsa::kRecRowOffs;
+    // single launch while the record holds the selection (and the kept meta-groups)
+    {
+        const long kc = pl.hier ? pl.cand_cap : M;
+        const long ksel = p->top_k < kc ? p->top_k : kc;
+        const long kmeta = pl.hier ? (m->top_k_meta < cap1 ? m->top_k_meta : cap1) : 0;
+        pl.fused = pl.mfma && units <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs && kmeta <= gsa::kRecMeta;
+    }
     const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
     const int TB = pl.fused ? gsa::kFusedTB : pl.TB;
     pl.S1 = (int)((cap1 + TA - 1) / TA);
-    pl.Sc = (int)((pl.cand_cap + pl.TB - 1) / pl.TB);
+    pl.Sc = (int)((pl.cand_cap + TA - 1) / TA);
     pl.S2 = (int)((cap2 + TB - 1) / TB);
     if (pl.fused) {  // every unit owns at least one task of each kind
         pl.S1 = pl.S1 > 0 ? pl.S1 : 1;
         pl.S2 = pl.S2 > 0 ? pl.S2 : 1;
+        if (pl.hier) pl.Sc = pl.Sc > 0 ? pl.Sc : 1;
     }
     a.S1 = pl.S1;
     a.SL = TA;
@@ -135,10 +141,12 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     a.NS = pl.S1 + pl.S2;
     pl.sc.units = (int)units;
     pl.sc.S1 = pl.S1;
+    pl.sc.S3 = pl.fused && pl.hier ? pl.Sc : 0;
     pl.sc.S2 = pl.S2;
     pl.sc.TA = TA;
     pl.sc.TB = TB;
-    pl.sc.total = (int)(units * (pl.S1 + pl.S2));
+    pl.sc.total = (int)(units * (pl.S1 + pl.sc.S3 + pl.S2));
+    pl.sc.hier = pl.hier ? 1 : 0;
     a.key_stride = kv->num_chunks;
     a.cand_stride = pl.cand_cap;
     size_t off = 0;
@@ -153,6 +161,7 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_acc = off;   off += align_up(sizeof(float) * units * a.NS * a.G * a.D);
     const size_t fslices = pl.fused ? (size_t)units * pl.S1 : 0;
     pl.off_spairs = off; off += align_up(sizeof(uint64_t) * fslices * gsa::kFusedTA);
+    pl.off_spairs_c = off; off += align_up(sizeof(uint64_t) * (size_t)units * pl.sc.S3 * gsa::kFusedTA);
     pl.total = off;
 }
 
@@ -279,6 +288,15 @@ gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_m
     a.out = out;
     hipStream_t st = (hipStream_t)stream;
 
+    if (pl.fused) {
+        unsigned* ctl = (unsigned*)(ws + pl.off_ctl);
+        pl.sc.err = ctl + 2;
+        a.urec = ctl + kHdrWords;
+        a.spairs = (uint64_t*)(ws + pl.off_spairs);
+        a.spairs_c = (uint64_t*)(ws + pl.off_spairs_c);
+        GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
+        return GSA_OK;
+    }
     if ((s = run_attn(pl, gsa::kListMeta, pl.S1, st)) != GSA_OK) return s;
     GSA_LAUNCH(gsa::launch_select(a, gsa::kSelMeta, st));
     if ((s = run_attn(pl, gsa::kListCand, pl.Sc, st)) != GSA_OK) return s;

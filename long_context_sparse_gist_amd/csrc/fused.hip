@@ -227,13 +227,13 @@ __device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, 
 }
 
 // Bucket sort of one slice's keys, one per thread: kv (the key) and pos (its
-// position in the slice, -1: none).  Publishes the keys (order key | chunk id
-// << 32) in descending bucket order, staged in LDS and written as whole
-// contiguous lines (the stores write through to memory, and a partially
-// written line costs the memory a read-modify-write); with `lead`, also the
-// first kFSelL of them into the unit's record.
-__device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int p0, float kv, int pos,
-                             bool lead, unsigned char* smem, int* wsum) {
+// position in the slice, -1: none).  Publishes the keys (order key | list
+// index << 32) in descending bucket order to `pairs`, staged in LDS and written
+// as whole contiguous lines (the stores write through to memory, and a
+// partially written line costs the memory a read-modify-write); with `lead`,
+// also the first kFSelL of them (the slice's place in the unit's record).
+__device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, int p0, float kv, int pos,
+                             unsigned char* smem, int* wsum) {
     constexpr int PER = kBins / kThreads;  // consecutive buckets per thread
     int* hist = (int*)smem;
     uint64_t* pair_st = (uint64_t*)(smem + kBins * 4);  // kFusedTA pairs
@@ -269,9 +269,9 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
     }
     __syncthreads();
     static_assert(kFusedTA == kThreads, "one pair per thread");
-    if (tid < tot) st_dev(a.spairs + ((size_t)u * a.S1 + idx) * kFusedTA + tid, pair_st[tid]);
-    // the leading keys again, into the unit's record, id + 1: nonzero once written
-    if (lead && tid < min(tot, kFSelL)) st_dev(unit_lead(a, u) + idx * kFSelL + tid, pair_st[tid] + (1ull << 32));
+    if (tid < tot) st_dev(pairs + tid, pair_st[tid]);
+    // the leading keys again, into the unit's record, index + 1: nonzero once written
+    if (lead && tid < min(tot, kFSelL)) st_dev(lead + tid, pair_st[tid] + (1ull << 32));
     __syncthreads();
 }
 
@@ -291,8 +291,8 @@ __device__ __forceinline__ void bucket_slice(const Args& a, int u, int idx, int 
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
-__device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int nA,
-                                             const float* keys, unsigned char* smem) {
+__device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int kind, int n,
+                                             int nA, const float* keys, unsigned char* smem) {
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
     constexpr int WPL = kFSelMaxN / 32 / 64;                 // 32-bit bitmap words per lane of wavefront 0
@@ -300,18 +300,32 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     static_assert(kFSelMaxN / 64 == kThreads, "one 64-bit bitmap word per thread");
     FSelSmem& sh = *(FSelSmem*)smem;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int u = c.u, n = c.n, k = a.top_k, keff = min(k, n);
-    int32_t* out = a.sel + (size_t)u * k;
+    const int u = c.u;
+    const bool meta = kind == kListMeta, cand = kind == kListCand;
+    const int k = meta ? a.top_k_meta : a.top_k, keff = min(k, n);
+    int32_t* out = (meta ? a.sel_meta : a.sel) + (size_t)u * k;
     int64_t* ro = unit_rowoff(a, u);  // one plus each selected chunk's first-row offset
-    const uint64_t* pairs = a.spairs + (size_t)u * a.S1 * kFusedTA;
-    const uint64_t* lead = unit_lead(a, u);
+    unsigned* mo = unit_meta(a, u);   // one plus each kept meta-group
+    const uint64_t* pairs = cand ? a.spairs_c + (size_t)u * sc.S3 * kFusedTA : a.spairs + (size_t)u * sc.S1 * kFusedTA;
+    const uint64_t* lead = cand ? unit_lead_c(a, u) : unit_lead(a, u);
     const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
     const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
-    bool btl = fast && a.max_pages <= kFSelBt;
+    bool btl = fast && !meta && a.max_pages <= kFSelBt;
+    // candidate list index -> chunk id: the gists of the kept meta-groups,
+    // then the gists past the last complete group (ascending either way)
+    const int head = c.ns1 * a.R;
+    unsigned kept[kRecMeta / kThreads];  // this thread's share of the kept groups (+1)
+    if (cand) {
+#pragma unroll
+        for (int j = 0; j < kRecMeta / kThreads; ++j) {
+            const int i = tid + j * kThreads;
+            kept[j] = i < c.ns1 ? ld_dev(mo + i) : 1u;
+        }
+    }
     auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
     // everything but the leading keys waits for every slice to be done
     auto wait_slices = [&]() {
-        wait_at_least<8>(unit_cntA(a, u), (unsigned)nA, sc.err);
+        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)nA, sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) wait_slices();
@@ -362,13 +376,38 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         const int phys = btl ? sh.bt[lp] : btrow[lp];
         return (((int64_t)phys * a.Hkv + c.g) * a.spp + (int64_t)(m - lp * a.page_chunks) * (a.C + 1)) * a.D;
     };
+    const int* kept_lds = (const int*)((FSelSmem*)smem)->cidx;  // kept groups (cand), filled before the output
     auto emit = [&](int pos, int m) {
-        st_dev(out + pos, (int32_t)m);
-        st_dev(ro + pos, row_of(m) + 1);
+        if (meta) {
+            st_dev(out + pos, (int32_t)m);
+            st_dev(mo + pos, (unsigned)m + 1u);
+            return;
+        }
+        const int ch = !cand ? m : (m < head ? kept_lds[m / a.R] * a.R + (m - (m / a.R) * a.R) : c.nm * a.R + (m - head));
+        st_dev(out + pos, (int32_t)ch);
+        st_dev(ro + pos, (row_of(ch) + 1) | (cand && ch >= c.nm * a.R ? (int64_t)kRowPastGroups : 0));
+    };
+    // the kept groups into LDS for the candidate output (no other use of cidx then)
+    auto park_kept = [&]() {
+        if (!cand) return;
+#pragma unroll
+        for (int j = 0; j < kRecMeta / kThreads; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < c.ns1) {
+                unsigned v = kept[j];
+                for (unsigned it = 0; v == 0u && it < kSpinLimit; ++it) {  // written before any candidate
+                    __builtin_amdgcn_s_sleep(2);                          // task could start; never expected
+                    v = ld_dev(mo + i);
+                }
+                ((int*)((FSelSmem*)smem)->cidx)[i] = (int)v - 1;
+            }
+        }
+        __syncthreads();
     };
     for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
     if (keff == 0) return fast;
     if (keff == n) {
+        park_kept();
         for (int i = tid; i < n; i += kThreads) emit(i, i);
         return fast;
     }
@@ -453,6 +492,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     };
     bool general = !fast;
     if (fast) {
+        __syncthreads();  // every thread's part of the LDS state is clear
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -536,11 +576,22 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         block_topk_general<kThreads>(keys, nullptr, n, k, out, true, ssh);
         drain();
         __syncthreads();
-        for (int i = tid; i < keff; i += kThreads) st_dev(ro + i, row_of(ld_dev(out + i)) + 1);
+        int mi[kRecRowOffs / kThreads];  // this thread's list indices (keff <= kRecRowOffs)
+#pragma unroll
+        for (int j = 0; j < kRecRowOffs / kThreads; ++j) {
+            const int i = tid + j * kThreads;
+            mi[j] = i < keff ? ld_dev(out + i) : 0;
+        }
+        __syncthreads();  // the LDS is the select's no more
+        park_kept();
+#pragma unroll
+        for (int j = 0; j < kRecRowOffs / kThreads; ++j)
+            if (tid + j * kThreads < keff) emit(tid + j * kThreads, mi[j]);
         return fast;
     }
     int* ids = (int*)sh.ckey;  // the selection, ascending (written by wavefront 0)
     static_assert(kRecRowOffs <= kFSelCand, "the selection fits the candidate arrays");
+    static_assert(kRecMeta <= kFSelCand && kRecMeta % kThreads == 0, "the kept groups fit the candidate ids");
     if (w == 0) {
         // wavefront 0: radix passes over the candidates' bits [20:14], [13:7], [6:0]
         int above = above0;
@@ -646,36 +697,98 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         }
     }  // wavefront 0
     __syncthreads();
+    park_kept();
     for (int i = tid; i < keff; i += kThreads) emit(i, ids[i]);
     return fast;
 }
 
+// One slice (TA rows) of a scored list of unit u: the gists (flat GSA), the
+// meta-gists or the candidate gists (H-GSA).  Scores the rows (routing keys),
+// attends them when the set needs them (all gists, all meta-gists), publishes
+// the keys sorted by bucket and its partial; the next-to-last slice of the
+// list to finish runs the list's select.
 template <int D>
-__device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
-                           CombineSmem& cs, int* wsum, int* s_flag) {
+__device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int kind, int u, int idx,
+                                            unsigned char* smem, CombineSmem& cs, int* wsum, int* s_flag) {
     constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int G = a.G, C = a.C;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
     const int p0 = idx * s.TA;
-    // block-table lookups of this lane's tokens (blocks w, w+4, ...), issued
-    // together with the length load
+    const bool meta = kind == kListMeta, cand = kind == kListCand;
+    auto row_p = [&](int j, int t) { return p0 + 32 * (w + 4 * j) + 16 * t + lr; };
+    // gist rows of the flat list: block-table lookups issued with the length load
     size_t off[NBW][2];
+    if (kind == kListGists) {
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            int p = min(p0 + 32 * (w + 4 * j) + 16 * t + lr, a.num_chunks - 1);
-            off[j][t] = slot_offset(a, b, g, max(p, 0) * (C + 1) + C);
-        }
+            for (int t = 0; t < 2; ++t) {
+                const int p = min(row_p(j, t), a.num_chunks - 1);
+                off[j][t] = slot_offset(a, b, g, max(p, 0) * (C + 1) + C);
+            }
+    }
     ListCtx c;
-    make_ctx(a, kListGists, u, false, c);
-    const int nA = max(1, (c.n + s.TA - 1) / s.TA);
+    make_ctx(a, kind, u, s.hier != 0, c);
+    const int n = c.len;
+    const int nA = max(1, (n + s.TA - 1) / s.TA);
     if (idx >= nA) return;
-    const bool attn = !(a.flags & kFlagSelectedGists);
-    const int cnt = max(0, min(s.TA, c.n - p0));
-    float* keys = a.keys + (size_t)u * a.key_stride;
+    const int cnt = max(0, min(s.TA, n - p0));
+    if (meta) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int p = max(min(row_p(j, t), n - 1), 0);
+                off[j][t] = (((size_t)b * a.Hkv + g) * a.max_meta + p) * (size_t)D;
+            }
+    } else if (cand && cnt > 0) {
+        // the gists of the kept meta-groups (the meta select's entries in the
+        // unit's record, polled), then the gists past the last complete group
+        const unsigned* mo = unit_meta(a, u);
+        const int head = c.ns1 * a.R;
+        unsigned grp[NBW][2];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int p = min(row_p(j, t), n - 1);
+                grp[j][t] = p < head ? ld_dev(mo + p / a.R) : 1u;
+            }
+        for (unsigned it = 0;; ++it) {
+            bool miss = false;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) miss |= grp[j][0] == 0u || grp[j][1] == 0u;
+            if (!__ballot(miss)) break;
+            if (it >= kSpinLimit) {  // never expected: report, read group 0
+                if (lane == 0) st_dev(s.err, 1u);
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) grp[j][t] = grp[j][t] ? grp[j][t] : 1u;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (grp[j][t] == 0u) grp[j][t] = ld_dev(mo + min(row_p(j, t), n - 1) / a.R);
+        }
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int p = min(row_p(j, t), n - 1);
+                const int r = p / a.R;
+                const int gist = p < head ? (int)(grp[j][t] - 1u) * a.R + (p - r * a.R) : c.nm * a.R + (p - head);
+                off[j][t] = slot_offset(a, b, g, gist * (C + 1) + C);
+            }
+    }
+    const bool attn = meta || (kind == kListGists && !(a.flags & kFlagSelectedGists));
+    float* keys = meta ? a.mkeys + (size_t)u * a.max_meta
+                : cand ? a.ckeys + (size_t)u * a.cand_stride : a.keys + (size_t)u * a.key_stride;
 
     if (cnt > 0) {
         int nval[NBW];
@@ -695,8 +808,8 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
         float* stash = (float*)(smem + Lds::stash(D)) + 64 * w;
         const float tau = a.tau;
         wa.template stream<NBW>(
-            (const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, attn, a.tau_log2e, lr, lg,
-            tile, [&](int j, const f32x4_t sc[2]) {
+            (const __bf16*)(meta ? a.km : a.kc), (const __bf16*)(meta ? a.vm : a.vc), off, nval, nbw, attn,
+            a.tau_log2e, lr, lg, tile, [&](int j, const f32x4_t sc[2]) {
                 // routing keys: tau * sum over the group's heads (padding heads are 0)
                 float kv = 0.f;
                 int kt = -1;
@@ -722,7 +835,10 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
         const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
         __syncthreads();  // the tiles are free
-        bucket_slice(a, u, idx, p0, kv, kpos < cnt ? kpos : -1, nA <= kRecSlices, smem, wsum);
+        uint64_t* pairs = cand ? a.spairs_c + ((size_t)u * s.S3 + idx) * kFusedTA
+                               : a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
+        uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
+        bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
         if (attn) {
             const size_t pbase = ((size_t)u * a.NS + idx) * G;
             combine_waves<D>(
@@ -739,24 +855,31 @@ __device__ __forceinline__ void task_gists(const Args& a, const Sched& s, int u,
     __syncthreads();
     // the next-to-last slice to finish selects (the only one with nA == 1):
     // it polls the last slice's leading keys instead of waiting for its count
-    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntA(a, u), 1u) == (unsigned)(nA >= 2 ? nA - 2 : 0);
+    if (threadIdx.x == 0)
+        *s_flag = add_dev(cand ? unit_cntC(a, u) : unit_cntA(a, u), 1u) == (unsigned)(nA >= 2 ? nA - 2 : 0);
     __syncthreads();
     if (!*s_flag) return;
 
     // select and publish (ahead of the streaming workgroups sharing this CU:
     // everything of the unit waits for it)
     __builtin_amdgcn_s_setprio(2);
-    for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    select_fused(a, s, c, nA, keys, smem);
+    if (kind == kListGists)
+        for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
+    select_fused(a, s, c, kind, n, nA, keys, smem);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
-        uint64_t* lead = unit_lead(a, u);
+        uint64_t* lead = cand ? unit_lead_c(a, u) : unit_lead(a, u);
         for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
             const int sl = i / kFSelL;
-            if (i - sl * kFSelL < min(kFusedTA, c.n - sl * kFusedTA)) st_dev(lead + i, 0ull);
+            if (i - sl * kFSelL < min(kFusedTA, n - sl * kFusedTA)) st_dev(lead + i, 0ull);
         }
     }
+    // the record entries this select wrote or cleared are in place: the
+    // unit's merging task resets the record only after every select says so
+    drain();
+    __syncthreads();
+    if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
@@ -823,21 +946,31 @@ template <int D, int EJ>
 __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                               CombineSmem& cs, FoldHdr& fh, int* s_flag) {
     const int G = a.G, C = a.C;
+    const bool hier = s.hier != 0;
+    // the list: raw tokens of the selected chunks, the raw tail, then (H-GSA)
+    // the gists past the last complete meta-group and one entry per selected
+    // chunk for its gist, attended only when the chunk lies in a complete
+    // group (those come first: the selection is ascending), or (flat GSA,
+    // selected-gists set) the selected gists
     ListCtx c;
-    make_ctx(a, kListUnfolded, u, false, c);
-    const int nB = max(1, (c.len + s.TB - 1) / s.TB);
+    make_ctx(a, hier ? kListMeta : kListUnfolded, u, hier, c);
+    const int ninc = hier ? c.n - c.nm * a.R : 0;
+    const int len = hier ? c.ns * C + c.tail + ninc + c.ns : c.len;
+    const int nB = max(1, (len + s.TB - 1) / s.TB);
     if (idx >= nB) return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int p0 = idx * s.TB;
-    const int cnt = max(0, min(s.TB, c.len - p0));
+    const int cnt = max(0, min(s.TB, len - p0));
     const int raw = c.ns * C;
     // first raw-tail row (the tail lies in one page): known before the selection
     const int64_t tail_off = c.tail > 0 ? (int64_t)slot_offset(a, c.b, c.g, c.n * (C + 1)) : 0;
-    // fold the gist-slice partials idx, idx + nB, ... once every slice is done
-    const bool attn = !(a.flags & kFlagSelectedGists);
-    const int nAt = max(1, (c.n + s.TA - 1) / s.TA);   // gist-slice tasks of the unit
-    const int nA = attn ? (c.n + s.TA - 1) / s.TA : 0;  // slices that wrote a partial
+    // fold the partials of the sliced list (gists, or meta-gists) idx, idx + nB,
+    // ... once every slice is done
+    const bool attn = hier || !(a.flags & kFlagSelectedGists);
+    const int n1 = hier ? c.nm : c.n;                  // rows of the sliced list
+    const int nAt = max(1, (n1 + s.TA - 1) / s.TA);   // its slice tasks
+    const int nA = attn ? (n1 + s.TA - 1) / s.TA : 0;  // slices that wrote a partial
     const int nf = idx < nA ? (nA - idx + nB - 1) / nB : 0;
     float gacc[EJ];
 #pragma unroll
@@ -861,26 +994,34 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         const int64_t* ro = unit_rowoff(a, u);
         size_t off[1][2];
         int nval[1];
-        nval[0] = max(0, min(32, cnt - 32 * w));
-        int jr[2];      // selection entry of the row, -1 for a tail row
-        int64_t o[2];   // one plus the base offset, 0 while unknown
+        int jr[2];      // selection entry of the row, -1 for a known row
+        int64_t o[2];   // one plus the base offset (H-GSA: past-groups flag), 0 while unknown
         int64_t add[2]; // offset of the row from that base
+        bool gsec[2];   // the row is a selected chunk's gist
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             // a token past the end reads the task's first row (in range)
             const int rel = 32 * w + 16 * t + lr;
             const int p = p0 + (rel < cnt ? rel : 0);
+            gsec[t] = false;
             if (p < raw) {
                 jr[t] = p / C;
                 add[t] = (int64_t)(p - jr[t] * C) * D;
             } else if (p < raw + c.tail) {
                 jr[t] = -1;
-                add[t] = (int64_t)(p - raw) * D;
+                add[t] = 0;
+                o[t] = tail_off + (int64_t)(p - raw) * D + 1;
+            } else if (p < raw + c.tail + ninc) {
+                jr[t] = -1;
+                add[t] = 0;
+                const int m = c.nm * a.R + (p - raw - c.tail);
+                o[t] = (int64_t)slot_offset(a, c.b, c.g, m * (C + 1) + C) + 1;
             } else {
-                jr[t] = p - raw - c.tail;
+                jr[t] = p - raw - c.tail - ninc;
                 add[t] = (int64_t)C * D;
+                gsec[t] = true;
             }
-            o[t] = jr[t] >= 0 ? ld_dev(ro + jr[t]) : tail_off + 1;
+            if (jr[t] >= 0) o[t] = ld_dev(ro + jr[t]);
         }
         for (unsigned it = 0; __ballot(o[0] == 0 || o[1] == 0); ++it) {
             if (it >= kSpinLimit) {  // never expected: report, read a row in range
@@ -894,8 +1035,17 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
             for (int t = 0; t < 2; ++t)
                 if (o[t] == 0) o[t] = ld_dev(ro + jr[t]);
         }
+        // rows this block attends: before the end, and (H-GSA) a selected
+        // chunk's gist only inside a complete group; they form a prefix of
+        // the block, so their count is the block's length
+        int nv = 0;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) off[0][t] = (size_t)(o[t] - 1 + add[t]);
+        for (int t = 0; t < 2; ++t) {
+            const bool valid = 32 * w + 16 * t + lr < cnt && !(gsec[t] && (o[t] & (int64_t)kRowPastGroups));
+            nv += __popcll(__ballot(valid && lg == 0));
+            off[0][t] = (size_t)((o[t] & ~(int64_t)kRowPastGroups) - 1 + add[t]);
+        }
+        nval[0] = nv;
         unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
         wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
                               nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, tile,
@@ -929,11 +1079,27 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
             out[e] = (__bf16)((fh.m[h] == -INFINITY || L == 0.f) ? 0.f : gacc[j] / L);
         }
     }
-    // every task of the unit has read the selection: clear its row offsets
+    // every unfolded task has read the selection; wait until every slice and
+    // candidate task has counted in and every select has finished writing the
+    // record (long done in practice: nothing else orders them before this
+    // point when the selection is empty), then return the record to zero
+    if (threadIdx.x == 0) {
+        wait_at_least<8>(unit_cntA(a, u), (unsigned)nAt, s.err);
+        if (hier) {
+            const int ncand = c.ns1 * a.R + ninc;
+            wait_at_least<8>(unit_cntC(a, u), (unsigned)max(1, (ncand + s.TA - 1) / s.TA), s.err);
+        }
+        wait_at_least<8>(unit_cntS(a, u), hier ? 2u : 1u, s.err);
+    }
+    __syncthreads();
     for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
+    if (hier)
+        for (int i = threadIdx.x; i < c.ns1; i += kThreads) st_dev(unit_meta(a, u) + i, 0u);
     if (threadIdx.x == 0) {
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);
+        st_dev(unit_cntS(a, u), 0u);
+        if (hier) st_dev(unit_cntC(a, u), 0u);
     }
 }
 
@@ -944,14 +1110,17 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     __shared__ FoldHdr fh;
     __shared__ int wsum[kThreads / 64];
     __shared__ int s_flag;
-    const int nA = s.units * s.S1;
+    const int nA = s.units * s.S1, nC = s.units * s.S3;
     const int t = blockIdx.x;
     if (t < nA) {
         const int u = t / s.S1;
-        task_gists<D>(a, s, u, t - u * s.S1, smem, cs, wsum, &s_flag);
+        task_slices<D>(a, s, s.hier ? kListMeta : kListGists, u, t - u * s.S1, smem, cs, wsum, &s_flag);
+    } else if (t < nA + nC) {
+        const int u = (t - nA) / s.S3;
+        task_slices<D>(a, s, kListCand, u, t - nA - u * s.S3, smem, cs, wsum, &s_flag);
     } else {
-        const int u = (t - nA) / s.S2;
-        task_unfolded<D, EJ>(a, s, u, t - nA - u * s.S2, smem, cs, fh, &s_flag);
+        const int u = (t - nA - nC) / s.S2;
+        task_unfolded<D, EJ>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);
     }
 }
 

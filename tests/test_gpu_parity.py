@@ -221,6 +221,48 @@ def test_workspace_reuse_across_shapes(gpu):
         assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
 
 
+def test_workspace_reuse_degenerate_selections(gpu):
+    """One workspace shared by calls whose selections are empty, complete or
+    absent (k = 0, the selected-gists set, H-GSA with no kept group or no
+    selected chunk): after every call the control block is zero again and the
+    next call is right."""
+    say("[parity] workspace reuse, degenerate selections")
+    ws = torch.zeros(96 << 20, dtype=torch.uint8, device=gpu)
+    flat = [("b2-g7-d128-c16", 0, 0), ("b2-g7-d128-c16", gsa.GSA_SET_SELECTED_GISTS, 0),
+            ("b2-g7-d128-c16", gsa.GSA_SET_SELECTED_GISTS, 5), ("b3-g4-d64-c8", 0, 10 ** 5),
+            ("b2-g7-d128-c16", 0, 8)]
+    hier = [(0, 5), (2, 0), (0, 0), (10 ** 5, 10 ** 5), (6, 12)]
+    for i, (name, flags, k) in enumerate(flat):
+        wl = SMALL[name]
+        inp = gi.make_inputs(wl, 400 + i, seq_lens=lens_for(wl, "edge" if i % 2 else "ragged", i))
+        g_inp = GU.to(inp, gpu)
+        sel = torch.full((wl.batch, wl.num_kv_heads, max(k, 1)), -7, dtype=torch.int32, device=gpu)
+        out = gsa.gsa_decode(g_inp.q, g_inp.k_cache, g_inp.v_cache, g_inp.block_table,
+                             g_inp.seq_lens, num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                             page_chunks=wl.page_chunks, top_k=k, flags=flags,
+                             sel_idx=sel if k > 0 else None, ws=ws)
+        torch.cuda.synchronize()
+        if k > 0:
+            GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None), top_k=k, flags=flags)
+        assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0, (name, flags, k)
+    wl = SMALL_H["h-b2-g4-d64-r4"]
+    for i, (k1, k2) in enumerate(hier):
+        inp = gi.make_inputs(wl, 500 + i, seq_lens=lens_for(wl, "ragged", 20 + i))
+        g_inp = GU.to(inp, gpu)
+        s1 = torch.full((wl.batch, wl.num_kv_heads, max(k1, 1)), -7, dtype=torch.int32, device=gpu)
+        s2 = torch.full((wl.batch, wl.num_kv_heads, max(k2, 1)), -7, dtype=torch.int32, device=gpu)
+        out = gsa.hgsa_decode(g_inp.q, g_inp.k_cache, g_inp.v_cache, g_inp.block_table,
+                              g_inp.seq_lens, g_inp.k_meta, g_inp.v_meta, num_chunks=wl.num_chunks,
+                              chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                              gists_per_meta=wl.gists_per_meta, top_k_meta=k1, top_k=k2,
+                              sel_meta=s1 if k1 > 0 else None, sel_idx=s2 if k2 > 0 else None, ws=ws)
+        torch.cuda.synchronize()
+        if k1 > 0 and k2 > 0:
+            GU.check_hgsa(inp, (out.float().cpu().numpy(), s1.cpu().numpy(), s2.cpu().numpy()),
+                          top_k=k2, top_k_meta=k1)
+        assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0, ("hgsa", k1, k2)
+
+
 def test_prepared_call_matches(gpu):
     """A prepared call gives the same bits as gsa_decode, call after call."""
     wl = SMALL["b2-g7-d128-c16"]

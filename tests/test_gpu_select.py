@@ -187,3 +187,18 @@ def test_unfolded_task_counts(gpu, top_k, tail, tasks):
     res = GU.run_gpu(GU.to(inp, gpu), top_k=top_k)
     check_exact(wl, res[1], res[2], top_k, lens=[L])
     GU.check_gsa(inp, res, top_k=top_k)
+
+
+@pytest.mark.parametrize("name", ["llama3.2-1b-32k-c8", "qwen2-7b-128k-c16", "multidoc-120k-c32"])
+def test_full_workload_every_unit_exact(gpu, name):
+    # every unit of the full-size workloads, two calls sharing one workspace:
+    # the selection equals the top-k of the GPU's own routing keys (the
+    # oracle comparison of sampled units lives in the parity tests)
+    wl = gi.BY_NAME[name]
+    inp = gi.make_inputs(wl, gi.seed_of(gi.WORKLOADS.index(wl)), device=gpu)
+    for call in range(2):
+        say(f"[select] full {name} call {call}")
+        out, sel, sc = GU.run_gpu(inp)
+        check_exact(wl, sel, sc, wl.top_k)
+    del inp
+    torch.cuda.empty_cache()
