@@ -125,7 +125,7 @@ typedef struct {
 
 /* Size of the control block at the start of every workspace: an error word
  * and the per-(batch, kv-head) counters of the single-launch path. */
-#define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 45568)
+#define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 25088)
 
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the
  * shapes are invalid).  The workspace must be 256-byte aligned and its first

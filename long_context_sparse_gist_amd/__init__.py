@@ -27,7 +27,7 @@ GSA_SET_ALL_GISTS = 0x0
 GSA_SET_SELECTED_GISTS = 0x2
 GSA_PATH_PORTABLE = 0x100
 # bytes at the start of every workspace that must be zero between calls
-WORKSPACE_CONTROL_BYTES = 16384 + 512 * 45568
+WORKSPACE_CONTROL_BYTES = 16384 + 512 * 25088
 
 STATUS = {0: "GSA_OK", 1: "GSA_ERR_NULL_ARG", 2: "GSA_ERR_BAD_SHAPE", 3: "GSA_ERR_BAD_DTYPE",
           4: "GSA_ERR_BAD_FLAGS", 5: "GSA_ERR_WORKSPACE", 6: "GSA_ERR_DEVICE",

@@ -123,7 +123,9 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         const long kc = pl.hier ? pl.cand_cap : M;
         const long ksel = p->top_k < kc ? p->top_k : kc;
         const long kmeta = pl.hier ? (m->top_k_meta < cap1 ? m->top_k_meta : cap1) : 0;
-        pl.fused = pl.mfma && units <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs && kmeta <= gsa::kRecMeta;
+        pl.fused = pl.mfma && units * (pl.hier ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
+                   kmeta <= gsa::kRecMeta;
+        a.recs_per_unit = pl.hier ? 2 : 1;
     }
     const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
     const int TB = pl.fused ? gsa::kFusedTB : pl.TB;

@@ -291,8 +291,9 @@ __device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, in
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
-__device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int kind, int n,
-                                             int nA, const float* keys, unsigned char* smem) {
+template <int KIND>
+__device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int n, int nA,
+                                             const float* keys, unsigned char* smem) {
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
     constexpr int WPL = kFSelMaxN / 32 / 64;                 // 32-bit bitmap words per lane of wavefront 0
@@ -301,7 +302,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     FSelSmem& sh = *(FSelSmem*)smem;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int u = c.u;
-    const bool meta = kind == kListMeta, cand = kind == kListCand;
+    constexpr bool meta = KIND == kListMeta, cand = KIND == kListCand;
     const int k = meta ? a.top_k_meta : a.top_k, keff = min(k, n);
     int32_t* out = (meta ? a.sel_meta : a.sel) + (size_t)u * k;
     int64_t* ro = unit_rowoff(a, u);  // one plus each selected chunk's first-row offset
@@ -707,16 +708,17 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
 // attends them when the set needs them (all gists, all meta-gists), publishes
 // the keys sorted by bucket and its partial; the next-to-last slice of the
 // list to finish runs the list's select.
-template <int D>
-__device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int kind, int u, int idx,
+template <int D, int KIND>
+__device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
                                             unsigned char* smem, CombineSmem& cs, int* wsum, int* s_flag) {
+    constexpr int kind = KIND;
     constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int G = a.G, C = a.C;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
     const int p0 = idx * s.TA;
-    const bool meta = kind == kListMeta, cand = kind == kListCand;
+    constexpr bool meta = kind == kListMeta, cand = kind == kListCand;
     auto row_p = [&](int j, int t) { return p0 + 32 * (w + 4 * j) + 16 * t + lr; };
     // gist rows of the flat list: block-table lookups issued with the length load
     size_t off[NBW][2];
@@ -730,7 +732,7 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int k
             }
     }
     ListCtx c;
-    make_ctx(a, kind, u, s.hier != 0, c);
+    make_ctx(a, kind, u, kind != kListGists, c);
     const int n = c.len;
     const int nA = max(1, (n + s.TA - 1) / s.TA);
     if (idx >= nA) return;
@@ -865,7 +867,7 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int k
     __builtin_amdgcn_s_setprio(2);
     if (kind == kListGists)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    select_fused(a, s, c, kind, n, nA, keys, smem);
+    select_fused<KIND>(a, s, c, n, nA, keys, smem);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
@@ -942,11 +944,11 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
 }
 
 // EJ: accumulator elements per thread, EJ * kThreads >= G * D.
-template <int D, int EJ>
+template <int D, int EJ, bool HIER>
 __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                               CombineSmem& cs, FoldHdr& fh, int* s_flag) {
     const int G = a.G, C = a.C;
-    const bool hier = s.hier != 0;
+    constexpr bool hier = HIER;
     // the list: raw tokens of the selected chunks, the raw tail, then (H-GSA)
     // the gists past the last complete meta-group and one entry per selected
     // chunk for its gist, attended only when the chunk lies in a complete
@@ -1060,7 +1062,14 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     if (!*s_flag) return;
 
     // the last unfolded task of the unit: merge, write the output, return the
-    // unit's record to zero
+    // unit's record to zero.  The reset needs every slice, candidate task and
+    // select counted in: read the counts now, the fold hides the round trip.
+    unsigned seen[3] = {0u, 0u, 0u};
+    if (threadIdx.x == 0) {
+        seen[0] = ld_dev(unit_cntA(a, u));
+        seen[1] = ld_dev(unit_cntS(a, u));
+        if (hier) seen[2] = ld_dev(unit_cntC(a, u));
+    }
 #pragma unroll
     for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
     if (threadIdx.x < 16) {
@@ -1084,12 +1093,12 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     // record (long done in practice: nothing else orders them before this
     // point when the selection is empty), then return the record to zero
     if (threadIdx.x == 0) {
-        wait_at_least<8>(unit_cntA(a, u), (unsigned)nAt, s.err);
+        if (seen[0] < (unsigned)nAt) wait_at_least<8>(unit_cntA(a, u), (unsigned)nAt, s.err);
+        if (seen[1] < (hier ? 2u : 1u)) wait_at_least<8>(unit_cntS(a, u), hier ? 2u : 1u, s.err);
         if (hier) {
-            const int ncand = c.ns1 * a.R + ninc;
-            wait_at_least<8>(unit_cntC(a, u), (unsigned)max(1, (ncand + s.TA - 1) / s.TA), s.err);
+            const unsigned nCt = (unsigned)max(1, (c.ns1 * a.R + ninc + s.TA - 1) / s.TA);
+            if (seen[2] < nCt) wait_at_least<8>(unit_cntC(a, u), nCt, s.err);
         }
-        wait_at_least<8>(unit_cntS(a, u), hier ? 2u : 1u, s.err);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
@@ -1103,7 +1112,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     }
 }
 
-template <int D, int EJ>
+template <int D, int EJ, bool HIER>
 __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ CombineSmem cs;
@@ -1114,13 +1123,13 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     const int t = blockIdx.x;
     if (t < nA) {
         const int u = t / s.S1;
-        task_slices<D>(a, s, s.hier ? kListMeta : kListGists, u, t - u * s.S1, smem, cs, wsum, &s_flag);
-    } else if (t < nA + nC) {
+        task_slices<D, HIER ? kListMeta : kListGists>(a, s, u, t - u * s.S1, smem, cs, wsum, &s_flag);
+    } else if (HIER && t < nA + nC) {
         const int u = (t - nA) / s.S3;
-        task_slices<D>(a, s, kListCand, u, t - nA - u * s.S3, smem, cs, wsum, &s_flag);
+        task_slices<D, kListCand>(a, s, u, t - nA - u * s.S3, smem, cs, wsum, &s_flag);
     } else {
         const int u = (t - nA - nC) / s.S2;
-        task_unfolded<D, EJ>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);
+        task_unfolded<D, EJ, HIER>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);
     }
 }
 
@@ -1129,7 +1138,10 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
 namespace {
 template <int D, int EJ>
 void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
-    hipLaunchKernelGGL((gsa_fused_kernel<D, EJ>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    if (s.hier)
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    else
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false>), dim3(s.total), dim3(kThreads), lds, st, a, s);
 }
 }  // namespace
 

@@ -49,7 +49,8 @@ struct Args {
     int SL;           // tokens per split of that list
     int SR;           // tokens per split of the unfolded list
     // single-launch path only
-    unsigned* urec;   // [units][kUnitRec] per-unit control records, zero between calls
+    unsigned* urec;   // [units][recs_per_unit][kUnitRec] per-unit control records, zero between calls
+    int recs_per_unit;
     uint64_t* spairs; // [units][S1][kFusedTA] slice keys by bucket: order key | id << 32
     uint64_t* spairs_c;  // [units][S3][kFusedTA] the same for the candidate tasks (H-GSA)
     uint64_t pc_inv;  // ceil(2^32 / page_chunks): chunk -> logical page by multiply
@@ -124,37 +125,38 @@ constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block p
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
 // Control record of one unit (words): the counts of finished gist (or
 // meta-gist) slices, unfolded tasks, candidate tasks and finished selects,
-// each in a 64-byte sector of its own; from word 64 the selection's row offsets (entry i: one
-// plus the element offset of the i-th selected chunk's first raw row, bit 62
-// set when the chunk lies past the last complete meta-group); then the
-// leading keys of every gist or meta-gist slice and of every candidate task
-// (kRecLead per slice: order key | (list index + 1) << 32); then the kept
+// each in a 64-byte sector of its own; from word 64 the selection's row
+// offsets (entry i: one plus the element offset of the i-th selected chunk's
+// first raw row, bit 62 set when the chunk lies past the last complete
+// meta-group); then the leading keys of every gist or meta-gist slice
+// (kRecLead per slice: order key | (list index + 1) << 32).  An H-GSA unit
+// owns two consecutive records: the second one's leading-key region holds
+// the candidate tasks' leading keys and its row-offset region the kept
 // meta-groups (entry i: one plus the i-th kept group).  An entry is 0 until
 // written, and its readers poll it; the unit's last tasks return every entry
-// to 0.  Records are 44.5 KiB apart, so the words that waiting workgroups
+// to 0.  Records are 24.5 KiB apart, so the words that waiting workgroups
 // poll spread over memory channels instead of queueing on one.
-constexpr int kRecRowOffs = 1024;  // selected chunks a record holds
-constexpr int kRecSlices = 64;     // slices whose leading keys a record holds (per list)
+constexpr int kRecRowOffs = 1024;  // selected chunks (or kept meta-groups) a record holds
+constexpr int kRecSlices = 64;     // slices whose leading keys a record holds
 constexpr int kRecLead = 32;       // leading keys per slice
-constexpr int kRecMeta = 1024;     // kept meta-groups a record holds
-constexpr int kRecLeadWords = 2 * kRecSlices * kRecLead;
-constexpr int kUnitRec = 11392;
-static_assert(64 + 2 * kRecRowOffs + 2 * kRecLeadWords + kRecMeta <= kUnitRec, "control record");
+constexpr int kRecMeta = kRecRowOffs;
+constexpr int kUnitRec = 6272;
+static_assert(64 + 2 * kRecRowOffs + 2 * kRecSlices * kRecLead <= kUnitRec, "control record");
 constexpr uint64_t kRowPastGroups = 1ull << 62;  // row-offset flag (H-GSA)
-__device__ inline unsigned* unit_cntA(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec; }       // finished gist / meta slices
-__device__ inline unsigned* unit_cntB(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 16; }  // finished unfolded tasks
-__device__ inline unsigned* unit_cntC(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 32; }  // finished candidate tasks
-__device__ inline unsigned* unit_cntS(const Args& a, int u) { return a.urec + (size_t)u * kUnitRec + 48; }  // selects done writing the record
-__device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(a.urec + (size_t)u * kUnitRec + 64); }
-__device__ inline uint64_t* unit_lead(const Args& a, int u) {
-    return (uint64_t*)(a.urec + (size_t)u * kUnitRec + 64 + 2 * kRecRowOffs);
+// records per unit: 1 (flat GSA) or 2 (H-GSA)
+__device__ inline unsigned* unit_rec(const Args& a, int u, int second = 0) {
+    return a.urec + ((size_t)u * a.recs_per_unit + second) * kUnitRec;
 }
+__device__ inline unsigned* unit_cntA(const Args& a, int u) { return unit_rec(a, u); }       // finished gist / meta slices
+__device__ inline unsigned* unit_cntB(const Args& a, int u) { return unit_rec(a, u) + 16; }  // finished unfolded tasks
+__device__ inline unsigned* unit_cntC(const Args& a, int u) { return unit_rec(a, u) + 32; }  // finished candidate tasks
+__device__ inline unsigned* unit_cntS(const Args& a, int u) { return unit_rec(a, u) + 48; }  // selects done writing the record
+__device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(unit_rec(a, u) + 64); }
+__device__ inline uint64_t* unit_lead(const Args& a, int u) { return (uint64_t*)(unit_rec(a, u) + 64 + 2 * kRecRowOffs); }
 __device__ inline uint64_t* unit_lead_c(const Args& a, int u) {
-    return (uint64_t*)(a.urec + (size_t)u * kUnitRec + 64 + 2 * kRecRowOffs + kRecLeadWords);
+    return (uint64_t*)(unit_rec(a, u, 1) + 64 + 2 * kRecRowOffs);
 }
-__device__ inline unsigned* unit_meta(const Args& a, int u) {
-    return a.urec + (size_t)u * kUnitRec + 64 + 2 * kRecRowOffs + 2 * kRecLeadWords;
-}
+__device__ inline unsigned* unit_meta(const Args& a, int u) { return unit_rec(a, u, 1) + 64; }
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
