@@ -7,10 +7,12 @@
 //                      of their order key (bucket), largest first (the
 //                      leading ones also into the unit's record), and
 //                      (all-gists set) one softmax partial.  The unit's
-//                      next-to-last slice to finish runs the top-k select
-//                      over the sorted slices and publishes the selection.
+//                      last slice runs the top-k select over the sorted
+//                      slices as soon as its own keys are sorted, publishes
+//                      the selection, then its own partial.
 //   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
-//                      select runs, polls its chunks' row offsets (written
+//                      select runs (the selecting slice's partial after its
+//                      own stream), polls its chunks' row offsets (written
 //                      by the select into the unit's record), attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
 //                      the selected chunks, raw tail, selected gists) and
@@ -18,13 +20,13 @@
 //                      merges them into the output and returns the unit's
 //                      record to zero.
 // Waits: unfolded tasks on gist slices (smaller workgroup ids), and the
-// selecting slice of a unit on the unit's other slices.  The device
+// selecting slice of a unit (its last) on the unit's other slices.  The device
 // dispatches each XCD's workgroups in id order, and ids run gist slices
 // first, unit by unit, so the workgroups queued ahead of an awaited slice
-// have smaller ids: slices that wait on nothing, or the one selecting slice
-// of an earlier unit (or of the same unit, already running).  By induction
-// over units every awaited slice is dispatched and every wait ends.  A wait is
-// nevertheless bounded; giving up sets the error word of the control block.  Several workgroups per CU hide
+// have smaller ids: slices that wait on nothing, or the selecting slice of an
+// earlier unit.  By induction over units every awaited slice is dispatched
+// and every wait ends.  A wait is nevertheless bounded; giving up sets the
+// error word of the control block.  Several workgroups per CU hide
 // each task's serial latencies (table lookups, drains) behind the others'
 // streaming, and the unfolded tasks of early units overlap the gist slices of
 // later ones.  Data passed between workgroups is written and read with
@@ -324,9 +326,11 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         }
     }
     auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
-    // everything but the leading keys waits for every slice to be done
+    // everything but the leading keys waits for every other slice to be
+    // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
-        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)nA, sc.err);
+        drain();
+        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)(nA - 1), sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) wait_slices();
@@ -703,14 +707,61 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     return fast;
 }
 
+// The 4 wavefronts' online-softmax states combined into one partial held in
+// registers: pacc[j] is element threadIdx.x + j*kThreads of the G x D
+// accumulator, (pm, pl) the max (exp2 domain) and sum of head threadIdx.x < G.
+template <int D, int EJ, typename WA>
+__device__ __forceinline__ void combine_to_regs(WA& wa, float tl, int G, float* red, CombineSmem& cs,
+                                                float (&pacc)[EJ], float& pm, float& pl) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    float l = wa.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lg == 0) {
+        cs.wm[w][lr] = wa.m;
+        cs.wl[w][lr] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * lg + r;
+        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
+        const float sc = (cs.wm[w][h] == -INFINITY) ? 0.f : exp2f((cs.wm[w][h] - M) * tl);
+        if (h < G) {
+#pragma unroll
+            for (int db = 0; db < WA::DB; ++db) red[((size_t)w * G + h) * D + 16 * db + lr] = wa.o[db][r] * sc;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+        const int e = threadIdx.x + j * kThreads;
+        pacc[j] = e < G * D ? red[e] + red[G * D + e] + red[2 * G * D + e] + red[3 * G * D + e] : 0.f;
+    }
+    if (threadIdx.x < (unsigned)G) {
+        const int h = threadIdx.x;
+        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
+        float L = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (cs.wm[i][h] != -INFINITY) L += cs.wl[i][h] * exp2f((cs.wm[i][h] - M) * tl);
+        pm = M * tl;
+        pl = L;
+    }
+    __syncthreads();
+}
+
 // One slice (TA rows) of a scored list of unit u: the gists (flat GSA), the
 // meta-gists or the candidate gists (H-GSA).  Scores the rows (routing keys),
 // attends them when the set needs them (all gists, all meta-gists), publishes
-// the keys sorted by bucket and its partial; the next-to-last slice of the
-// list to finish runs the list's select.
-template <int D, int KIND>
+// the keys sorted by bucket and its partial.  The list's last slice runs the
+// list's select as soon as its own keys are sorted: it combines its
+// wavefronts' softmax states into registers first and publishes that partial
+// only after the select.
+template <int D, int EJ, int KIND>
 __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
-                                            unsigned char* smem, CombineSmem& cs, int* wsum, int* s_flag) {
+                                            unsigned char* smem, CombineSmem& cs, int* wsum) {
     constexpr int kind = KIND;
     constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -789,6 +840,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             }
     }
     const bool attn = meta || (kind == kListGists && !(a.flags & kFlagSelectedGists));
+    const bool selector = idx == nA - 1;
+    const size_t pbase = ((size_t)u * a.NS + idx) * G;  // this slice's partial slot
+    float pacc[EJ];  // the selecting slice's partial, held across the select
+    float pm = -INFINITY, pl = 0.f;
     float* keys = meta ? a.mkeys + (size_t)u * a.max_meta
                 : cand ? a.ckeys + (size_t)u * a.cand_stride : a.keys + (size_t)u * a.key_stride;
 
@@ -841,8 +896,9 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                                : a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
         uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
         bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
-        if (attn) {
-            const size_t pbase = ((size_t)u * a.NS + idx) * G;
+        if (attn && selector) {
+            combine_to_regs<D, EJ>(wa, a.tau_log2e, G, (float*)smem, cs, pacc, pm, pl);
+        } else if (attn) {
             combine_waves<D>(
                 wa, a.tau_log2e, G, (float*)smem, cs,
                 [&](int h, int d, float v) { st_dev(a.part_acc + (pbase + h) * D + d, v); },
@@ -853,17 +909,16 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                 });
         }
     }
-    drain();
-    __syncthreads();
-    // the next-to-last slice to finish selects (the only one with nA == 1):
-    // it polls the last slice's leading keys instead of waiting for its count
-    if (threadIdx.x == 0)
-        *s_flag = add_dev(cand ? unit_cntC(a, u) : unit_cntA(a, u), 1u) == (unsigned)(nA >= 2 ? nA - 2 : 0);
-    __syncthreads();
-    if (!*s_flag) return;
+    if (!selector) {
+        drain();
+        __syncthreads();
+        if (threadIdx.x == 0) add_dev(cand ? unit_cntC(a, u) : unit_cntA(a, u), 1u);
+        return;
+    }
 
     // select and publish (ahead of the streaming workgroups sharing this CU:
-    // everything of the unit waits for it)
+    // everything of the unit waits for it); the other slices' leading keys
+    // are polled
     __builtin_amdgcn_s_setprio(2);
     if (kind == kListGists)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
@@ -877,11 +932,28 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             if (i - sl * kFSelL < min(kFusedTA, n - sl * kFusedTA)) st_dev(lead + i, 0ull);
         }
     }
-    // the record entries this select wrote or cleared are in place: the
+    // this slice's partial
+    if (attn && cnt > 0) {
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) {
+            const int e = threadIdx.x + j * kThreads;
+            if (e < G * D) st_dev(a.part_acc + pbase * D + e, pacc[j]);
+        }
+        if (threadIdx.x < (unsigned)G) {
+            float* p = (float*)(a.part_ml + pbase + threadIdx.x);
+            st_dev(p, pm);
+            st_dev(p + 1, pl);
+        }
+    }
+    // the partial and the record entries this select wrote or cleared are in
+    // place: an unfolded task folds the partial after this count, and the
     // unit's merging task resets the record only after every select says so
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
+    if (threadIdx.x == 0) {
+        if (attn && cnt > 0) add_dev(unit_cntP(a, u), 1u);
+        add_dev(unit_cntS(a, u), 1u);
+    }
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
@@ -974,6 +1046,10 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     const int nAt = max(1, (n1 + s.TA - 1) / s.TA);   // its slice tasks
     const int nA = attn ? (n1 + s.TA - 1) / s.TA : 0;  // slices that wrote a partial
     const int nf = idx < nA ? (nA - idx + nB - 1) / nB : 0;
+    // the list's last slice (the selecting one) publishes its partial after
+    // the select: the task owning that slot folds it after its own stream
+    const bool owner = nA > 0 && (nA - 1) % nB == idx;
+    const int nf0 = nf - (owner ? 1 : 0);
     float gacc[EJ];
 #pragma unroll
     for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
@@ -981,10 +1057,10 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         fh.m[threadIdx.x] = -INFINITY;
         fh.l[threadIdx.x] = 0.f;
     }
-    if (nf > 0) {
-        wait_at_least<32>(unit_cntA(a, u), (unsigned)nAt, s.err);
+    if (nf0 > 0) {
+        wait_at_least<32>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
         __syncthreads();
-        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf, gacc, fh);
+        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf0, gacc, fh);
     }
     __builtin_amdgcn_s_setprio(1);  // the unit's result waits for this task
     WaveAttnL<D> wa;
@@ -1054,6 +1130,11 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
                               [](int, const f32x4_t*) {});
     }
     __syncthreads();
+    if (owner) {
+        wait_at_least<8>(unit_cntP(a, u), 1u, s.err);
+        __syncthreads();
+        fold_regs<EJ>(a, u, [&](int) { return nA - 1; }, 1, gacc, fh);
+    }
     combine_publish<D, EJ>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
     drain();
     __syncthreads();
@@ -1078,6 +1159,9 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     }
     __syncthreads();
     fold_regs<EJ>(a, u, [&](int i) { return s.S1 + i; }, nB, gacc, fh);
+    // the counts are compared only here: without this the compares move up
+    // to the loads and the fold's loads wait for their round trip
+    asm volatile("" : "+v"(seen[0]), "+v"(seen[1]), "+v"(seen[2])::"memory");
     __bf16* out = (__bf16*)a.out + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D;
 #pragma unroll
     for (int j = 0; j < EJ; ++j) {
@@ -1093,11 +1177,12 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     // record (long done in practice: nothing else orders them before this
     // point when the selection is empty), then return the record to zero
     if (threadIdx.x == 0) {
-        if (seen[0] < (unsigned)nAt) wait_at_least<8>(unit_cntA(a, u), (unsigned)nAt, s.err);
+        // (the selecting slice's partial count is in: its folding task saw it)
+        if (seen[0] < (unsigned)(nAt - 1)) wait_at_least<8>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
         if (seen[1] < (hier ? 2u : 1u)) wait_at_least<8>(unit_cntS(a, u), hier ? 2u : 1u, s.err);
         if (hier) {
             const unsigned nCt = (unsigned)max(1, (c.ns1 * a.R + ninc + s.TA - 1) / s.TA);
-            if (seen[2] < nCt) wait_at_least<8>(unit_cntC(a, u), nCt, s.err);
+            if (seen[2] < nCt - 1) wait_at_least<8>(unit_cntC(a, u), nCt - 1, s.err);
         }
     }
     __syncthreads();
@@ -1108,6 +1193,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);
         st_dev(unit_cntS(a, u), 0u);
+        st_dev(unit_cntP(a, u), 0u);
         if (hier) st_dev(unit_cntC(a, u), 0u);
     }
 }
@@ -1123,10 +1209,10 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     const int t = blockIdx.x;
     if (t < nA) {
         const int u = t / s.S1;
-        task_slices<D, HIER ? kListMeta : kListGists>(a, s, u, t - u * s.S1, smem, cs, wsum, &s_flag);
+        task_slices<D, EJ, HIER ? kListMeta : kListGists>(a, s, u, t - u * s.S1, smem, cs, wsum);
     } else if (HIER && t < nA + nC) {
         const int u = (t - nA) / s.S3;
-        task_slices<D, kListCand>(a, s, u, t - nA - u * s.S3, smem, cs, wsum, &s_flag);
+        task_slices<D, EJ, kListCand>(a, s, u, t - nA - u * s.S3, smem, cs, wsum);
     } else {
         const int u = (t - nA - nC) / s.S2;
         task_unfolded<D, EJ, HIER>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);

@@ -124,8 +124,10 @@ constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks
 constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
 // Control record of one unit (words): the counts of finished gist (or
-// meta-gist) slices, unfolded tasks, candidate tasks and finished selects,
-// each in a 64-byte sector of its own; from word 64 the selection's row
+// meta-gist) slices and candidate tasks (the selecting one, the list's last,
+// not included), of finished unfolded tasks and of finished selects, each in
+// a 64-byte sector of its own (the selecting slice's published partial
+// shares the last one); from word 64 the selection's row
 // offsets (entry i: one plus the element offset of the i-th selected chunk's
 // first raw row, bit 62 set when the chunk lies past the last complete
 // meta-group); then the leading keys of every gist or meta-gist slice
@@ -151,6 +153,7 @@ __device__ inline unsigned* unit_cntA(const Args& a, int u) { return unit_rec(a,
 __device__ inline unsigned* unit_cntB(const Args& a, int u) { return unit_rec(a, u) + 16; }  // finished unfolded tasks
 __device__ inline unsigned* unit_cntC(const Args& a, int u) { return unit_rec(a, u) + 32; }  // finished candidate tasks
 __device__ inline unsigned* unit_cntS(const Args& a, int u) { return unit_rec(a, u) + 48; }  // selects done writing the record
+__device__ inline unsigned* unit_cntP(const Args& a, int u) { return unit_rec(a, u) + 56; }  // selecting slice's partial published
 __device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(unit_rec(a, u) + 64); }
 __device__ inline uint64_t* unit_lead(const Args& a, int u) { return (uint64_t*)(unit_rec(a, u) + 64 + 2 * kRecRowOffs); }
 __device__ inline uint64_t* unit_lead_c(const Args& a, int u) {
