@@ -8,11 +8,10 @@
 //                      leading ones also into the unit's record), and
 //                      (all-gists set) one softmax partial.  The unit's
 //                      last slice runs the top-k select over the sorted
-//                      slices as soon as its own keys are sorted, publishes
-//                      the selection, then its own partial.
+//                      slices as soon as its own keys and partial are
+//                      written, and publishes the selection.
 //   unfolded (u, j)    folds gist-slice partials i = j, j+nB, ... while the
-//                      select runs (the selecting slice's partial after its
-//                      own stream), polls its chunks' row offsets (written
+//                      select runs, polls its chunks' row offsets (written
 //                      by the select into the unit's record), attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
 //                      the selected chunks, raw tail, selected gists) and
@@ -293,9 +292,11 @@ __device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, in
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
-template <int KIND>
+// drained(): called by every thread once every wavefront's earlier stores
+// have completed (at most once; maybe not at all).
+template <int KIND, typename Drained>
 __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int n, int nA,
-                                             const float* keys, unsigned char* smem) {
+                                             const float* keys, unsigned char* smem, Drained drained) {
     constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
     constexpr int WPL = kFSelMaxN / 32 / 64;                 // 32-bit bitmap words per lane of wavefront 0
@@ -333,7 +334,10 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)(nA - 1), sc.err);
         __syncthreads();
     };
-    if (!fast && n > 0) wait_slices();
+    if (!fast && n > 0) {
+        wait_slices();
+        drained();
+    }
     // round trip 1: the slices' leading keys, polled (the last slice may
     // still be writing its own); 1 << 32 marks an unused slot
     uint64_t pv[KQ];
@@ -497,7 +501,9 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     };
     bool general = !fast;
     if (fast) {
+        drain();          // (the polls above have waited for nearly all of it)
         __syncthreads();  // every thread's part of the LDS state is clear
+        drained();
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
@@ -707,58 +713,12 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     return fast;
 }
 
-// The 4 wavefronts' online-softmax states combined into one partial held in
-// registers: pacc[j] is element threadIdx.x + j*kThreads of the G x D
-// accumulator, (pm, pl) the max (exp2 domain) and sum of head threadIdx.x < G.
-template <int D, int EJ, typename WA>
-__device__ __forceinline__ void combine_to_regs(WA& wa, float tl, int G, float* red, CombineSmem& cs,
-                                                float (&pacc)[EJ], float& pm, float& pl) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    float l = wa.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (lg == 0) {
-        cs.wm[w][lr] = wa.m;
-        cs.wl[w][lr] = l;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * lg + r;
-        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
-        const float sc = (cs.wm[w][h] == -INFINITY) ? 0.f : exp2f((cs.wm[w][h] - M) * tl);
-        if (h < G) {
-#pragma unroll
-            for (int db = 0; db < WA::DB; ++db) red[((size_t)w * G + h) * D + 16 * db + lr] = wa.o[db][r] * sc;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) {
-        const int e = threadIdx.x + j * kThreads;
-        pacc[j] = e < G * D ? red[e] + red[G * D + e] + red[2 * G * D + e] + red[3 * G * D + e] : 0.f;
-    }
-    if (threadIdx.x < (unsigned)G) {
-        const int h = threadIdx.x;
-        const float M = fmaxf(fmaxf(cs.wm[0][h], cs.wm[1][h]), fmaxf(cs.wm[2][h], cs.wm[3][h]));
-        float L = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (cs.wm[i][h] != -INFINITY) L += cs.wl[i][h] * exp2f((cs.wm[i][h] - M) * tl);
-        pm = M * tl;
-        pl = L;
-    }
-    __syncthreads();
-}
-
 // One slice (TA rows) of a scored list of unit u: the gists (flat GSA), the
 // meta-gists or the candidate gists (H-GSA).  Scores the rows (routing keys),
 // attends them when the set needs them (all gists, all meta-gists), publishes
 // the keys sorted by bucket and its partial.  The list's last slice runs the
-// list's select as soon as its own keys are sorted: it combines its
-// wavefronts' softmax states into registers first and publishes that partial
-// only after the select.
+// list's select as soon as its partial is written: it counts the partial in
+// at the select's first barrier, once its stores have completed anyway.
 template <int D, int EJ, int KIND>
 __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
                                             unsigned char* smem, CombineSmem& cs, int* wsum) {
@@ -841,9 +801,6 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     }
     const bool attn = meta || (kind == kListGists && !(a.flags & kFlagSelectedGists));
     const bool selector = idx == nA - 1;
-    const size_t pbase = ((size_t)u * a.NS + idx) * G;  // this slice's partial slot
-    float pacc[EJ];  // the selecting slice's partial, held across the select
-    float pm = -INFINITY, pl = 0.f;
     float* keys = meta ? a.mkeys + (size_t)u * a.max_meta
                 : cand ? a.ckeys + (size_t)u * a.cand_stride : a.keys + (size_t)u * a.key_stride;
 
@@ -896,9 +853,8 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                                : a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
         uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
         bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
-        if (attn && selector) {
-            combine_to_regs<D, EJ>(wa, a.tau_log2e, G, (float*)smem, cs, pacc, pm, pl);
-        } else if (attn) {
+        if (attn) {
+            const size_t pbase = ((size_t)u * a.NS + idx) * G;
             combine_waves<D>(
                 wa, a.tau_log2e, G, (float*)smem, cs,
                 [&](int h, int d, float v) { st_dev(a.part_acc + (pbase + h) * D + d, v); },
@@ -922,7 +878,14 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     __builtin_amdgcn_s_setprio(2);
     if (kind == kListGists)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    select_fused<KIND>(a, s, c, n, nA, keys, smem);
+    // the partial's count: by thread 0 once every wavefront has drained
+    const bool partial = attn && cnt > 0;
+    bool counted = false;
+    auto count_partial = [&]() {
+        if (partial && threadIdx.x == 0) add_dev(unit_cntP(a, u), 1u);
+        counted = true;
+    };
+    select_fused<KIND>(a, s, c, n, nA, keys, smem, count_partial);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
@@ -932,28 +895,12 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             if (i - sl * kFSelL < min(kFusedTA, n - sl * kFusedTA)) st_dev(lead + i, 0ull);
         }
     }
-    // this slice's partial
-    if (attn && cnt > 0) {
-#pragma unroll
-        for (int j = 0; j < EJ; ++j) {
-            const int e = threadIdx.x + j * kThreads;
-            if (e < G * D) st_dev(a.part_acc + pbase * D + e, pacc[j]);
-        }
-        if (threadIdx.x < (unsigned)G) {
-            float* p = (float*)(a.part_ml + pbase + threadIdx.x);
-            st_dev(p, pm);
-            st_dev(p + 1, pl);
-        }
-    }
-    // the partial and the record entries this select wrote or cleared are in
-    // place: an unfolded task folds the partial after this count, and the
+    // the record entries this select wrote or cleared are in place: the
     // unit's merging task resets the record only after every select says so
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        if (attn && cnt > 0) add_dev(unit_cntP(a, u), 1u);
-        add_dev(unit_cntS(a, u), 1u);
-    }
+    if (!counted) count_partial();
+    if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
@@ -1046,10 +993,9 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     const int nAt = max(1, (n1 + s.TA - 1) / s.TA);   // its slice tasks
     const int nA = attn ? (n1 + s.TA - 1) / s.TA : 0;  // slices that wrote a partial
     const int nf = idx < nA ? (nA - idx + nB - 1) / nB : 0;
-    // the list's last slice (the selecting one) publishes its partial after
-    // the select: the task owning that slot folds it after its own stream
+    // the list's last slice (the selecting one) counts its partial in apart
+    // from the others
     const bool owner = nA > 0 && (nA - 1) % nB == idx;
-    const int nf0 = nf - (owner ? 1 : 0);
     float gacc[EJ];
 #pragma unroll
     for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
@@ -1057,10 +1003,11 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         fh.m[threadIdx.x] = -INFINITY;
         fh.l[threadIdx.x] = 0.f;
     }
-    if (nf0 > 0) {
+    if (nf > 0) {
         wait_at_least<32>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
+        if (owner) wait_at_least<8>(unit_cntP(a, u), 1u, s.err);
         __syncthreads();
-        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf0, gacc, fh);
+        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf, gacc, fh);
     }
     __builtin_amdgcn_s_setprio(1);  // the unit's result waits for this task
     WaveAttnL<D> wa;
@@ -1130,11 +1077,6 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
                               [](int, const f32x4_t*) {});
     }
     __syncthreads();
-    if (owner) {
-        wait_at_least<8>(unit_cntP(a, u), 1u, s.err);
-        __syncthreads();
-        fold_regs<EJ>(a, u, [&](int) { return nA - 1; }, 1, gacc, fh);
-    }
     combine_publish<D, EJ>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
     drain();
     __syncthreads();
