@@ -92,6 +92,18 @@ __device__ inline unsigned add_dev(unsigned* p, unsigned v) {
 // wait until this thread's memory operations have completed
 __device__ inline void drain() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Buffer view of `bytes` bytes at p (raw, 32-bit data format word).  A load at
+// an offset at or past the end reads 0 and touches no memory: the folds use
+// that instead of a lane-masked branch around every load.
+__device__ inline __amdgpu_buffer_rsrc_t buf_view(const void* p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr unsigned kBufOut = 0x40000000u;  // an offset part that keeps a load past the end
+// 4-byte load with the cache policy of ld_dev (device scope: sc1)
+__device__ inline float ld_dev_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 16));
+}
+
 // Thread 0 waits until *p >= target (bounded; giving up sets the error word).
 // The caller synchronises the block afterwards.  Polls are spaced out
 // (SLEEP * 64 cycles): hundreds of waiting workgroups polling a few counter
@@ -154,39 +166,45 @@ struct Lds {
     }
 };
 
-// Fold partial slots slot_of(0..ns) of unit u into (acc, fh): acc[j] holds
+// Fold partial slots s0, s0 + st, ... (ns of them) of unit u into (acc, fh): acc[j] holds
 // element threadIdx.x + j*kThreads of the G x D accumulator.  Eight slots per
 // round, every load of a round in flight together.
-template <int EJ, typename SlotFn>
-__device__ __forceinline__ void fold_regs(const Args& a, int u, SlotFn slot_of, int ns, float (&acc)[EJ], FoldHdr& fh) {
+template <int EJ>
+__device__ __forceinline__ void fold_regs(const Args& a, int u, int s0, int st, int ns, float (&acc)[EJ], FoldHdr& fh) {
     const int G = a.G, GD = a.G * a.D;
     const size_t base = (size_t)u * a.NS;
+    const __amdgpu_buffer_rsrc_t racc = buf_view(a.part_acc + base * GD, 4u * a.NS * GD);
+    const __amdgpu_buffer_rsrc_t rml = buf_view(a.part_ml + base * G, 8u * a.NS * G);
     constexpr int NR = EJ >= 8 ? kFoldRound / 2 : kFoldRound;  // slots per round (registers)
     constexpr int HR = NR / 2;
     for (int r0 = 0; r0 < ns; r0 += NR) {
         const int nr = min(NR, ns - r0);
-        // two half-round arrays (kept in registers), every load issued up front
+        // two half-round arrays (kept in registers), every load issued up front;
+        // a slot past the round or an element past G x D reads 0 (offset past
+        // the unit's partials)
         float va[EJ][HR], vb[EJ][HR];
+        unsigned eo[EJ];
 #pragma unroll
         for (int j = 0; j < EJ; ++j) {
             const int e = threadIdx.x + j * kThreads;
+            eo[j] = e < GD ? 4u * e : kBufOut;
+        }
 #pragma unroll
-            for (int i = 0; i < HR; ++i) {
-                va[j][i] = (e < GD && i < nr) ? ld_dev(a.part_acc + (base + slot_of(r0 + i)) * GD + e) : 0.f;
-                vb[j][i] = (e < GD && HR + i < nr)
-                               ? ld_dev(a.part_acc + (base + slot_of(r0 + HR + i)) * GD + e)
-                               : 0.f;
+        for (int i = 0; i < HR; ++i) {
+            const unsigned oa = i < nr ? 4u * (unsigned)((s0 + (r0 + i) * st) * GD) : kBufOut;
+            const unsigned ob = HR + i < nr ? 4u * (unsigned)((s0 + (r0 + HR + i) * st) * GD) : kBufOut;
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) {
+                va[j][i] = ld_dev_buf(racc, eo[j] + oa);
+                vb[j][i] = ld_dev_buf(racc, eo[j] + ob);
             }
         }
         {
             // factors: the 16 lanes of row h hold slots 0..15 of head h
             const int h = threadIdx.x >> 4, i = threadIdx.x & 15;
-            float x = -INFINITY, y = 0.f;
-            if (h < G && i < nr) {
-                const float* p = (const float*)(a.part_ml + (base + slot_of(r0 + i)) * G + h);
-                x = ld_dev(p);
-                y = ld_dev(p + 1);
-            }
+            const unsigned om = h < G && i < nr ? 8u * (unsigned)((s0 + (r0 + i) * st) * G + h) : kBufOut;
+            float x = ld_dev_buf(rml, om), y = ld_dev_buf(rml, om + 4u);
+            x = h < G && i < nr ? x : -INFINITY;
             const float mold = h < G ? fh.m[h] : -INFINITY;
             const float lold = h < G ? fh.l[h] : 0.f;
             const float M = fmaxf(mold, rowmax16(x));
@@ -1007,7 +1025,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         wait_at_least<32>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
         if (owner) wait_at_least<8>(unit_cntP(a, u), 1u, s.err);
         __syncthreads();
-        fold_regs<EJ>(a, u, [&](int i) { return idx + i * nB; }, nf, gacc, fh);
+        fold_regs<EJ>(a, u, idx, nB, nf, gacc, fh);
     }
     __builtin_amdgcn_s_setprio(1);  // the unit's result waits for this task
     WaveAttnL<D> wa;
@@ -1100,7 +1118,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         fh.l[threadIdx.x] = 0.f;
     }
     __syncthreads();
-    fold_regs<EJ>(a, u, [&](int i) { return s.S1 + i; }, nB, gacc, fh);
+    fold_regs<EJ>(a, u, s.S1, 1, nB, gacc, fh);
     // the counts are compared only here: without this the compares move up
     // to the loads and the fold's loads wait for their round trip
     asm volatile("" : "+v"(seen[0]), "+v"(seen[1]), "+v"(seen[2])::"memory");
