@@ -130,6 +130,17 @@ struct __attribute__((aligned(16))) FoldHdr {
     float f[16][kFoldRound];  // [head][slot of the round]
 };
 
+constexpr int kFSelKQ = kFSelMaxSlices * kFSelL / kThreads;  // up-front keys per thread
+constexpr int kFSelKB = kFSelBt / kThreads;                   // block-table entries per thread
+
+// The unit's block-table row, loaded by the selecting slice as soon as its
+// own stream is done: the round trip overlaps its bucket sort and partial.
+// (Loading the other slices' leading keys that early finds many not yet
+// written and costs a poll more than it saves.)
+struct SelPre {
+    int bt[kFSelKB];
+};
+
 // LDS of the top-k select (last gist slice of a unit).
 struct FSelSmem {
     uint64_t selbits[kFSelMaxN / 64];  // selected chunk ids, one bit each
@@ -310,12 +321,41 @@ __device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, in
 // low 21 bits, resolves ties to the lower chunk id and writes the selection
 // ascending from the bitmap: a single wavefront needs no block barriers, and
 // the candidates are few.
+// Whether the bucketed select serves this list (else the general select),
+// and whether it keeps the block-table row in LDS.
+template <int KIND>
+__device__ inline void select_plan(const Args& a, int n, int nA, bool& fast, bool& btl) {
+    const int k = KIND == kListMeta ? a.top_k_meta : a.top_k, keff = min(k, n);
+    fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
+    btl = fast && KIND != kListMeta && a.max_pages <= kFSelBt;
+}
+
+// Issue the select's block-table loads (SelPre).
+template <int KIND>
+__device__ inline void select_prefetch(const Args& a, const ListCtx& c, int n, int nA, SelPre& pre) {
+    bool fast, btl;
+    select_plan<KIND>(a, n, nA, fast, btl);
+    const int tid = threadIdx.x;
+    if (btl) {
+        const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
+#pragma unroll
+        for (int j = 0; j < kFSelKB; ++j) {
+            const int i = tid + j * kThreads;
+            pre.bt[j] = i < a.max_pages ? btrow[i] : 0;
+        }
+    }
+}
+
 // drained(): called by every thread once every wavefront's earlier stores
-// have completed (at most once; maybe not at all).
+// have completed (at most once; maybe not at all).  pre: the block-table row
+// loaded by select_prefetch.  Slice `own` (the calling one) is not bucket
+// sorted: every thread brings its key (ownk: order key | list index << 32,
+// ownv: present), so that slice is complete among the candidates.
 template <int KIND, typename Drained>
 __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int n, int nA,
-                                             const float* keys, unsigned char* smem, Drained drained) {
-    constexpr int KQ = kFSelMaxSlices * kFSelL / kThreads;   // up-front keys per thread
+                                             const float* keys, unsigned char* smem, SelPre& pre, int own,
+                                             uint64_t ownk, bool ownv, Drained drained) {
+    constexpr int KQ = kFSelKQ;   // up-front keys per thread
     constexpr int KR = kFSelCand / kThreads;                 // second-round keys per thread
     constexpr int WPL = kFSelMaxN / 32 / 64;                 // 32-bit bitmap words per lane of wavefront 0
     static_assert(kBins == 64 * 32, "64 coarse buckets of 32");
@@ -331,8 +371,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     const uint64_t* pairs = cand ? a.spairs_c + (size_t)u * sc.S3 * kFusedTA : a.spairs + (size_t)u * sc.S1 * kFusedTA;
     const uint64_t* lead = cand ? unit_lead_c(a, u) : unit_lead(a, u);
     const int32_t* btrow = a.bt + (size_t)c.b * a.max_pages;
-    const bool fast = keff > 0 && keff < n && nA <= kFSelMaxSlices && n <= kFSelMaxN;
-    bool btl = fast && !meta && a.max_pages <= kFSelBt;
+    bool fast, btl;
+    select_plan<KIND>(a, n, nA, fast, btl);
     // candidate list index -> chunk id: the gists of the kept meta-groups,
     // then the gists past the last complete group (ascending either way)
     const int head = c.ns1 * a.R;
@@ -356,18 +396,21 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         wait_slices();
         drained();
     }
-    // round trip 1: the slices' leading keys, polled (the last slice may
-    // still be writing its own); 1 << 32 marks an unused slot
+    // round trip 1: the slices' leading keys, polled (a slice may still be
+    // writing its own); 1 << 32 marks an unused slot
     uint64_t pv[KQ];
     if (fast) {
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            pv[j] = (sl < nA && p < slice_n(sl)) ? ld_dev(lead + q) : (1ull << 32);
+            pv[j] = (sl < nA && sl != own && p < slice_n(sl)) ? ld_dev(lead + q) : (1ull << 32);
         }
     }
-    if (btl)
-        for (int i = tid; i < a.max_pages; i += kThreads) sh.bt[i] = btrow[i];
+    if (btl) {
+#pragma unroll
+        for (int j = 0; j < kFSelKB; ++j)
+            if (tid + j * kThreads < a.max_pages) sh.bt[tid + j * kThreads] = pre.bt[j];
+    }
     if (fast) {
         // clear the LDS state while the keys are in flight
         *(int4*)&sh.uh[8 * tid] = make_int4(0, 0, 0, 0);
@@ -489,16 +532,22 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     };
     // the up-front keys: one LDS atomic per wavefront reserves all their
     // candidate slots
+    // up-front key j of this thread (j == KQ: its key of slice `own`)
+    auto up_key = [&](int j) { return j < KQ ? pv[j] : ownk; };
+    auto up_valid = [&](int j) {
+        const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+        return j < KQ ? sl < nA && sl != own && p < slice_n(sl) : ownv;
+    };
     auto take_upfront = [&]() {
-        uint64_t cm[KQ];
+        uint64_t cm[KQ + 1];
         int wtot = 0;
 #pragma unroll
-        for (int j = 0; j < KQ; ++j) {
-            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            const bool valid = sl < nA && p < slice_n(sl);
-            const uint32_t bk = (uint32_t)pv[j] >> 21;
+        for (int j = 0; j <= KQ; ++j) {
+            const uint64_t x = up_key(j);
+            const bool valid = up_valid(j);
+            const uint32_t bk = (uint32_t)x >> 21;
             if (valid && bk > (uint32_t)b0) {
-                const int id = (int)(pv[j] >> 32);
+                const int id = (int)(x >> 32);
                 atomicOr((unsigned long long*)&sh.selbits[id >> 6], 1ull << (id & 63));
             }
             cm[j] = __ballot(valid && bk == (uint32_t)b0);
@@ -508,11 +557,12 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         if (lane == 0 && wtot) base = atomicAdd(&sh.ncand, wtot);
         base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
-        for (int j = 0; j < KQ; ++j) {
+        for (int j = 0; j <= KQ; ++j) {
+            const uint64_t x = up_key(j);
             const int ci = base + __popcll(cm[j] & ((1ull << lane) - 1ull));
             if (((cm[j] >> lane) & 1ull) && ci < kFSelCand) {
-                sh.ckey[ci] = (uint32_t)pv[j];
-                sh.cidx[ci] = (int)(pv[j] >> 32);
+                sh.ckey[ci] = (uint32_t)x;
+                sh.cidx[ci] = (int)(x >> 32);
             }
             base += __popcll(cm[j]);
         }
@@ -523,10 +573,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         __syncthreads();  // every thread's part of the LDS state is clear
         drained();
 #pragma unroll
-        for (int j = 0; j < KQ; ++j) {
-            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            if (sl < nA && p < slice_n(sl)) atomicAdd(&sh.uh[(uint32_t)pv[j] >> 21], 1);
-        }
+        for (int j = 0; j <= KQ; ++j)
+            if (up_valid(j)) atomicAdd(&sh.uh[(uint32_t)up_key(j) >> 21], 1);
         __syncthreads();
         find_boundary();  // bT: the bucket of the keff-th largest candidate
         // classify against bT; a slice whose kFSelL-th key is in a bucket >= bT
@@ -535,7 +583,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            if (p == kFSelL - 1 && sl < nA && slice_n(sl) > kFSelL && ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
+            if (p == kFSelL - 1 && sl < nA && sl != own && slice_n(sl) > kFSelL &&
+                ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
                 atomicOr((unsigned long long*)&sh.needmask, 1ull << sl);
         }
         __syncthreads();
@@ -819,6 +868,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     }
     const bool attn = meta || (kind == kListGists && !(a.flags & kFlagSelectedGists));
     const bool selector = idx == nA - 1;
+    SelPre pre;  // the selecting slice's block-table row
+    bool prefetched = false;
+    uint64_t ownk = 0;  // the selecting slice's key of this thread (not bucket sorted)
+    bool ownv = false;
     float* keys = meta ? a.mkeys + (size_t)u * a.max_meta
                 : cand ? a.ckeys + (size_t)u * a.cand_stride : a.keys + (size_t)u * a.key_stride;
 
@@ -859,6 +912,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                 // flight would hold up the next wait on this wavefront's loads)
                 if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kv;
             });
+        if (selector) {
+            select_prefetch<KIND>(a, c, n, nA, pre);
+            prefetched = true;
+        }
         // thread t takes key slot t % 64 of wavefront t / 64 (NBW * 32 == 64 slots)
         static_assert(NBW * 32 * 4 == kThreads, "one key slot per thread");
         __syncthreads();
@@ -870,7 +927,12 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         uint64_t* pairs = cand ? a.spairs_c + ((size_t)u * s.S3 + idx) * kFusedTA
                                : a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
         uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
-        bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+        if (!selector) {
+            bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+        } else {  // the select takes this slice's keys as they are
+            ownk = (uint64_t)order_key(kv) | ((uint64_t)(uint32_t)(p0 + kpos) << 32);
+            ownv = kpos < cnt;
+        }
         if (attn) {
             const size_t pbase = ((size_t)u * a.NS + idx) * G;
             combine_waves<D>(
@@ -903,7 +965,8 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         if (partial && threadIdx.x == 0) add_dev(unit_cntP(a, u), 1u);
         counted = true;
     };
-    select_fused<KIND>(a, s, c, n, nA, keys, smem, count_partial);
+    if (!prefetched) select_prefetch<KIND>(a, c, n, nA, pre);
+    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, count_partial);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
