@@ -397,13 +397,18 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         drained();
     }
     // round trip 1: the slices' leading keys, polled (a slice may still be
-    // writing its own); 1 << 32 marks an unused slot
+    // writing its own); 1 << 32 marks an unused slot.  Key slots j >= JQ
+    // belong to no slice of this list: skipped with one scalar branch each.
+    const int JQ = min(KQ, (nA * kFSelL + kThreads - 1) / kThreads);
     uint64_t pv[KQ];
     if (fast) {
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
-            const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            pv[j] = (sl < nA && sl != own && p < slice_n(sl)) ? ld_dev(lead + q) : (1ull << 32);
+            pv[j] = 1ull << 32;
+            if (j < JQ) {
+                const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
+                if (sl < nA && sl != own && p < slice_n(sl)) pv[j] = ld_dev(lead + q);
+            }
         }
     }
     if (btl) {
@@ -436,7 +441,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             __builtin_amdgcn_s_sleep(8);
 #pragma unroll
             for (int j = 0; j < KQ; ++j)
-                if (pv[j] == 0ull) pv[j] = ld_dev(lead + tid + j * kThreads);
+                if (j < JQ && pv[j] == 0ull) pv[j] = ld_dev(lead + tid + j * kThreads);
         }
 #pragma unroll
         for (int j = 0; j < KQ; ++j) pv[j] -= 1ull << 32;
@@ -538,11 +543,14 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
         return j < KQ ? sl < nA && sl != own && p < slice_n(sl) : ownv;
     };
+    auto up_used = [&](int j) { return j == KQ || j < JQ; };  // uniform
     auto take_upfront = [&]() {
         uint64_t cm[KQ + 1];
         int wtot = 0;
 #pragma unroll
         for (int j = 0; j <= KQ; ++j) {
+            cm[j] = 0ull;
+            if (!up_used(j)) continue;
             const uint64_t x = up_key(j);
             const bool valid = up_valid(j);
             const uint32_t bk = (uint32_t)x >> 21;
@@ -558,6 +566,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
         for (int j = 0; j <= KQ; ++j) {
+            if (!up_used(j)) continue;
             const uint64_t x = up_key(j);
             const int ci = base + __popcll(cm[j] & ((1ull << lane) - 1ull));
             if (((cm[j] >> lane) & 1ull) && ci < kFSelCand) {
@@ -574,19 +583,25 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         drained();
 #pragma unroll
         for (int j = 0; j <= KQ; ++j)
-            if (up_valid(j)) atomicAdd(&sh.uh[(uint32_t)up_key(j) >> 21], 1);
+            if (up_used(j) && up_valid(j)) atomicAdd(&sh.uh[(uint32_t)up_key(j) >> 21], 1);
         __syncthreads();
         find_boundary();  // bT: the bucket of the keff-th largest candidate
         // classify against bT; a slice whose kFSelL-th key is in a bucket >= bT
         // may hold more such keys: then a second round, and classify again
         take_upfront();
+        // lanes 31 and 63 of wavefront w hold the last up-front key of slices
+        // 8j + 2w and 8j + 2w + 1: one ballot per key slot, one LDS atomic
+        static_assert(kThreads == 256 && kFSelL == 32, "slice of a lane");
+        uint64_t wneed = 0ull;
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
+            if (j >= JQ) continue;
             const int q = tid + j * kThreads, sl = q / kFSelL, p = q - sl * kFSelL;
-            if (p == kFSelL - 1 && sl < nA && sl != own && slice_n(sl) > kFSelL &&
-                ((uint32_t)pv[j] >> 21) >= (uint32_t)b0)
-                atomicOr((unsigned long long*)&sh.needmask, 1ull << sl);
+            const uint64_t bm = __ballot(p == kFSelL - 1 && sl < nA && sl != own && slice_n(sl) > kFSelL &&
+                                         ((uint32_t)pv[j] >> 21) >= (uint32_t)b0);
+            wneed |= (((bm >> 31) & 1ull) << (8 * j + 2 * w)) | (((bm >> 63) & 1ull) << (8 * j + 2 * w + 1));
         }
+        if (lane == 0 && wneed) atomicOr((unsigned long long*)&sh.needmask, wneed);
         __syncthreads();
         const uint64_t needmask = sh.needmask;
         if (needmask) {
