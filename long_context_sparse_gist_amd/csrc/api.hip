@@ -128,7 +128,11 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         a.recs_per_unit = pl.hier ? 2 : 1;
     }
     const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
-    const int TB = pl.fused ? gsa::kFusedTB : pl.TB;
+    // unfolded tasks: one block per wavefront, or (flat GSA) two when a
+    // launch would hold more than 2048 of them (per-task work then outweighs
+    // the tail)
+    int TB = pl.fused ? gsa::kFusedTB : pl.TB;
+    if (pl.fused && !pl.hier && units * ((cap2 + TB - 1) / TB) > 2048) TB = 2 * gsa::kFusedTB;
     pl.S1 = (int)((cap1 + TA - 1) / TA);
     pl.Sc = (int)((pl.cand_cap + TA - 1) / TA);
     pl.S2 = (int)((cap2 + TB - 1) / TB);

@@ -1059,7 +1059,7 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
 }
 
 // EJ: accumulator elements per thread, EJ * kThreads >= G * D.
-template <int D, int EJ, bool HIER>
+template <int D, int EJ, bool HIER, int NBB>
 __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                               CombineSmem& cs, FoldHdr& fh, int* s_flag) {
     const int G = a.G, C = a.C;
@@ -1113,63 +1113,83 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         // whose offset the wavefront polls in the unit's record until the
         // select has written it (one plus the offset; 0 before)
         const int64_t* ro = unit_rowoff(a, u);
-        size_t off[1][2];
-        int nval[1];
-        int jr[2];      // selection entry of the row, -1 for a known row
-        int64_t o[2];   // one plus the base offset (H-GSA: past-groups flag), 0 while unknown
-        int64_t add[2]; // offset of the row from that base
-        bool gsec[2];   // the row is a selected chunk's gist
+        // NBB 32-token blocks per wavefront (tasks of 128 NBB tokens): block j
+        // of wavefront w is the task's block w + 4j
+        constexpr int nbb = NBB;
+        size_t off[NBB][2];
+        int nval[NBB];
+        int jr[NBB][2];      // selection entry of the row, -1 for a known row
+        int64_t o[NBB][2];   // one plus the base offset (H-GSA: past-groups flag), 0 while unknown
+        int64_t add[NBB][2]; // offset of the row from that base
+        bool gsec[NBB][2];   // the row is a selected chunk's gist
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            // a token past the end reads the task's first row (in range)
-            const int rel = 32 * w + 16 * t + lr;
-            const int p = p0 + (rel < cnt ? rel : 0);
-            gsec[t] = false;
-            if (p < raw) {
-                jr[t] = p / C;
-                add[t] = (int64_t)(p - jr[t] * C) * D;
-            } else if (p < raw + c.tail) {
-                jr[t] = -1;
-                add[t] = 0;
-                o[t] = tail_off + (int64_t)(p - raw) * D + 1;
-            } else if (p < raw + c.tail + ninc) {
-                jr[t] = -1;
-                add[t] = 0;
-                const int m = c.nm * a.R + (p - raw - c.tail);
-                o[t] = (int64_t)slot_offset(a, c.b, c.g, m * (C + 1) + C) + 1;
-            } else {
-                jr[t] = p - raw - c.tail - ninc;
-                add[t] = (int64_t)C * D;
-                gsec[t] = true;
+        for (int j = 0; j < NBB; ++j)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // a token past the end reads the task's first row (in range)
+                const int rel = 32 * (w + 4 * j) + 16 * t + lr;
+                const int p = p0 + (rel < cnt ? rel : 0);
+                gsec[j][t] = false;
+                jr[j][t] = -1;
+                add[j][t] = 0;
+                o[j][t] = 1;
+                if (j >= nbb) continue;
+                if (p < raw) {
+                    jr[j][t] = p / C;
+                    add[j][t] = (int64_t)(p - jr[j][t] * C) * D;
+                } else if (p < raw + c.tail) {
+                    o[j][t] = tail_off + (int64_t)(p - raw) * D + 1;
+                } else if (p < raw + c.tail + ninc) {
+                    const int m = c.nm * a.R + (p - raw - c.tail);
+                    o[j][t] = (int64_t)slot_offset(a, c.b, c.g, m * (C + 1) + C) + 1;
+                } else {
+                    jr[j][t] = p - raw - c.tail - ninc;
+                    add[j][t] = (int64_t)C * D;
+                    gsec[j][t] = true;
+                }
+                if (jr[j][t] >= 0) o[j][t] = ld_dev(ro + jr[j][t]);
             }
-            if (jr[t] >= 0) o[t] = ld_dev(ro + jr[t]);
-        }
-        for (unsigned it = 0; __ballot(o[0] == 0 || o[1] == 0); ++it) {
+        for (unsigned it = 0;; ++it) {
+            bool miss = false;
+#pragma unroll
+            for (int j = 0; j < NBB; ++j) miss |= o[j][0] == 0 || o[j][1] == 0;
+            if (!__ballot(miss)) break;
             if (it >= kSpinLimit) {  // never expected: report, read a row in range
                 if (lane == 0) st_dev(s.err, 1u);
-                o[0] = o[0] == 0 ? 1 : o[0];
-                o[1] = o[1] == 0 ? 1 : o[1];
+#pragma unroll
+                for (int j = 0; j < NBB; ++j)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) o[j][t] = o[j][t] == 0 ? 1 : o[j][t];
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (o[t] == 0) o[t] = ld_dev(ro + jr[t]);
-        }
-        // rows this block attends: before the end, and (H-GSA) a selected
-        // chunk's gist only inside a complete group; they form a prefix of
-        // the block, so their count is the block's length
-        int nv = 0;
+            for (int j = 0; j < NBB; ++j)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bool valid = 32 * w + 16 * t + lr < cnt && !(gsec[t] && (o[t] & (int64_t)kRowPastGroups));
-            nv += __popcll(__ballot(valid && lg == 0));
-            off[0][t] = (size_t)((o[t] & ~(int64_t)kRowPastGroups) - 1 + add[t]);
+                for (int t = 0; t < 2; ++t)
+                    if (o[j][t] == 0) o[j][t] = ld_dev(ro + jr[j][t]);
         }
-        nval[0] = nv;
+        // rows a block attends: before the end, and (H-GSA) a selected
+        // chunk's gist only inside a complete group; they form a prefix of
+        // the task's list, so a block's count is its length and a wavefront's
+        // blocks with rows come first
+        int nbw = 0;
+#pragma unroll
+        for (int j = 0; j < NBB; ++j) {
+            int nv = 0;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bool valid = j < nbb && 32 * (w + 4 * j) + 16 * t + lr < cnt &&
+                                   !(gsec[j][t] && (o[j][t] & (int64_t)kRowPastGroups));
+                nv += __popcll(__ballot(valid && lg == 0));
+                off[j][t] = (size_t)((o[j][t] & ~(int64_t)kRowPastGroups) - 1 + add[j][t]);
+            }
+            nval[j] = nv;
+            nbw += nv > 0 ? 1 : 0;
+        }
         unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
-        wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval,
-                              nval[0] > 0 ? 1 : 0, true, a.tau_log2e, lr, lg, tile,
+        wa.template stream<NBB>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, true, a.tau_log2e,
+                                lr, lg, tile,
                               [](int, const f32x4_t*) {});
     }
     __syncthreads();
@@ -1236,7 +1256,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     }
 }
 
-template <int D, int EJ, bool HIER>
+template <int D, int EJ, bool HIER, int NBB>
 __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ CombineSmem cs;
@@ -1253,7 +1273,7 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
         task_slices<D, EJ, kListCand>(a, s, u, t - nA - u * s.S3, smem, cs, wsum);
     } else {
         const int u = (t - nA - nC) / s.S2;
-        task_unfolded<D, EJ, HIER>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);
+        task_unfolded<D, EJ, HIER, NBB>(a, s, u, t - nA - nC - u * s.S2, smem, cs, fh, &s_flag);
     }
 }
 
@@ -1263,9 +1283,11 @@ namespace {
 template <int D, int EJ>
 void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
     if (s.hier)
-        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    else if (s.TB == 2 * kFusedTB)
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 2>), dim3(s.total), dim3(kThreads), lds, st, a, s);
     else
-        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
 }
 }  // namespace
 

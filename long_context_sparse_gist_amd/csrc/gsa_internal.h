@@ -121,7 +121,8 @@ struct Sched {
 };
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
-constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront)
+constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront; twice
+                               // that for launches with many unfolded tasks)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
 // Control record of one unit (words): the counts of finished gist (or
 // meta-gist) slices and candidate tasks (the selecting one, the list's last,

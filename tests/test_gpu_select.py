@@ -202,3 +202,23 @@ def test_full_workload_every_unit_exact(gpu, name):
         check_exact(wl, sel, sc, wl.top_k)
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seq_mode", ["full", "ragged"])
+def test_two_block_unfolded_tasks(gpu, seq_mode):
+    # 512 units with 6 unfolded 128-token tasks each exceed the launch's
+    # 2048-task limit, so the unfolded tasks take 256 tokens (two blocks per
+    # wavefront); ragged lengths leave tasks with one block, a partial second
+    # block, or a partial first block only
+    wl = gi.Workload("two-block", gi.BF16, 64, 8, 8, 64, 16, 300, 40, 16)
+    lens = None
+    if seq_mode == "ragged":
+        gen = torch.Generator().manual_seed(611)
+        lens = torch.randint(40 * 16, 300 * 16 + 15, (wl.batch,), generator=gen).tolist()
+    inp = gi.make_inputs(wl, 610 + (seq_mode == "ragged"), seq_lens=lens)
+    units = wl.batch * wl.num_kv_heads
+    assert units * -(-(wl.top_k * wl.chunk_size + wl.chunk_size - 1) // 128) > 2048
+    say(f"[select] two-block unfolded tasks ({seq_mode})")
+    res = GU.run_gpu(GU.to(inp, gpu))
+    check_exact(wl, res[1], res[2], wl.top_k, lens=lens)
+    GU.check_gsa(inp, res, units=[(b, g) for b in range(0, wl.batch, 7) for g in range(wl.num_kv_heads)])
