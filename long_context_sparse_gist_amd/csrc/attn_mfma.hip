@@ -180,8 +180,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (rel_of(blk, t, r) < count) mx = fmaxf(mx, s[blk][t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows4_max(mx);
     if (lg == 0) s_max[w][lr] = mx;
     __syncthreads();
     float mh = s_max[0][lr];
@@ -203,8 +202,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
                 lsum += (float)pb;
                 P[blk][4 * t + r] = pb;
             }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = rows4_sum(lsum);
 
     f32x4_t o[DB];
 #pragma unroll

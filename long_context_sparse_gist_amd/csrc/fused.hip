@@ -1009,8 +1009,7 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
     const int G = a.G, GD = a.G * D;
     const float tl = a.tau_log2e;
     float l = wa.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     if (lg == 0) {
         cs.wm[w][lr] = wa.m;
         cs.wl[w][lr] = l;

@@ -95,6 +95,24 @@ __device__ inline uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Sum / max over the four 16-lane rows at one column (lanes l, l^16, l^32,
+// l^48); every one of them gets the result.  A lane swap between the wave's
+// halves, then between the rows of each half (VALU, no LDS round trip): with
+// both operands the same value, the two results of a swap hold the lane's
+// value and its partner's.
+__device__ inline float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ inline float rows4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Number of unfolded (non-"all gists") list tokens of a sequence with `ns`
 // selected chunks and `tail` raw tokens after its last gist.
 __device__ inline int unfolded_len(const Args& a, int ns, int tail) {

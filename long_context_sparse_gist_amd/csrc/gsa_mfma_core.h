@@ -124,8 +124,7 @@ struct WaveAttn {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * t + 4 * lg + r < nvalid) bm = fmaxf(bm, s[t][r]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = rows4_max(bm);
         const float mnew = fmaxf(m, bm);  // finite: the block has a real token
         const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on the first block
         const float mb = mnew * tau_log2e;
@@ -254,8 +253,7 @@ __device__ inline void combine_waves(WA& wa, float tau_log2e, int G, float* red,
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     float l = wa.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = rows4_sum(l);
     if (lg == 0) {
         cs.wm[w][lr] = wa.m;
         cs.wl[w][lr] = l;
@@ -374,8 +372,7 @@ struct WaveAttnL {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * t + 4 * lg + r < nvalid) bm = fmaxf(bm, s[t][r]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = rows4_max(bm);
         const float mnew = fmaxf(m, bm);  // finite: the block has a real token
         const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on the first block
         const float mb = mnew * tau_log2e;
