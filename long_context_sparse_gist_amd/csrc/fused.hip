@@ -1000,9 +1000,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
-// (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u.
-template <int D, int EJ, typename WA>
-__device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, int slot, const float (&gacc)[EJ],
+// (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u,
+// or (LOCAL) leave it in (gacc, fh.m, fh.l) for a fold to continue from.
+template <int D, int EJ, bool LOCAL, typename WA>
+__device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, int slot, float (&gacc)[EJ],
                                 FoldHdr& fh, float* red, CombineSmem& cs) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -1040,9 +1041,15 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
         const float fb = mb == -INFINITY ? 0.f : exp2f(mb - Mt);
         fh.fg[h] = fg;
         fh.fb[h] = fb;
-        float* p = (float*)(a.part_ml + pbase + h);
-        st_dev(p, Mt);
-        st_dev(p + 1, fh.l[h] * fg + Lb * fb);
+        const float L = fh.l[h] * fg + Lb * fb;
+        if (LOCAL) {
+            fh.m[h] = Mt;
+            fh.l[h] = L;
+        } else {
+            float* p = (float*)(a.part_ml + pbase + h);
+            st_dev(p, Mt);
+            st_dev(p + 1, L);
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -1052,7 +1059,11 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
             const int h = e / D, d = e - h * D;
             const float bs = red[(size_t)h * D + d] + red[((size_t)G + h) * D + d] +
                              red[((size_t)2 * G + h) * D + d] + red[((size_t)3 * G + h) * D + d];
-            st_dev(a.part_acc + pbase * D + e, gacc[j] * fh.fg[h] + bs * fh.fb[h]);
+            const float v = gacc[j] * fh.fg[h] + bs * fh.fb[h];
+            if (LOCAL)
+                gacc[j] = v;
+            else
+                st_dev(a.part_acc + pbase * D + e, v);
         }
     }
 }
@@ -1192,30 +1203,30 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
                               [](int, const f32x4_t*) {});
     }
     __syncthreads();
-    combine_publish<D, EJ>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
-    drain();
-    __syncthreads();
-    if (threadIdx.x == 0) *s_flag = add_dev(unit_cntB(a, u), 1u) == (unsigned)(nB - 1);
-    __syncthreads();
-    if (!*s_flag) return;
+    // the unit's last unfolded task (the last one dispatched) merges; the
+    // others publish their partials and count themselves in
+    if (idx != nB - 1) {
+        combine_publish<D, EJ, false>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
+        drain();
+        __syncthreads();
+        if (threadIdx.x == 0) add_dev(unit_cntB(a, u), 1u);
+        return;
+    }
 
-    // the last unfolded task of the unit: merge, write the output, return the
-    // unit's record to zero.  The reset needs every slice, candidate task and
-    // select counted in: read the counts now, the fold hides the round trip.
+    // merge: this task's own partial stays in registers, the others' are
+    // folded into it; then write the output and return the unit's record to
+    // zero.  The reset needs every slice, candidate task and select counted
+    // in: read the counts now, the fold hides the round trip.
+    combine_publish<D, EJ, true>(wa, a, u, s.S1 + idx, gacc, fh, (float*)smem, cs);
     unsigned seen[3] = {0u, 0u, 0u};
     if (threadIdx.x == 0) {
         seen[0] = ld_dev(unit_cntA(a, u));
         seen[1] = ld_dev(unit_cntS(a, u));
         if (hier) seen[2] = ld_dev(unit_cntC(a, u));
-    }
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
-    if (threadIdx.x < 16) {
-        fh.m[threadIdx.x] = -INFINITY;
-        fh.l[threadIdx.x] = 0.f;
+        wait_at_least<8>(unit_cntB(a, u), (unsigned)(nB - 1), s.err);
     }
     __syncthreads();
-    fold_regs<EJ>(a, u, s.S1, 1, nB, gacc, fh);
+    fold_regs<EJ>(a, u, s.S1, 1, nB - 1, gacc, fh);
     // the counts are compared only here: without this the compares move up
     // to the loads and the fold's loads wait for their round trip
     asm volatile("" : "+v"(seen[0]), "+v"(seen[1]), "+v"(seen[2])::"memory");
