@@ -122,6 +122,25 @@ __device__ inline void wait_at_least(const unsigned* p, unsigned target, unsigne
     }
 }
 
+// As wait_at_least, polling every SLEEP * 64 cycles while more than two counts
+// are missing and every 128 cycles after: many waiting workgroups poll
+// rarely, the ones about to proceed see the last counts soon.
+template <int SLEEP>
+__device__ inline void wait_at_least_close(const unsigned* p, unsigned target, unsigned* err) {
+    if (threadIdx.x != 0) return;
+    unsigned it = 0;
+    for (unsigned v = ld_dev(p); v < target; v = ld_dev(p)) {
+        if (v + 2u < target)
+            __builtin_amdgcn_s_sleep(SLEEP);
+        else
+            __builtin_amdgcn_s_sleep(2);
+        if (++it >= kSpinLimit) {
+            st_dev(err, 1u);
+            break;
+        }
+    }
+}
+
 // Folding state of one partial: per-head running max (exp2 domain) and sum,
 // and the factors of the round being folded.
 constexpr int kFoldRound = 16;  // partials folded per round
@@ -1110,7 +1129,7 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
         fh.l[threadIdx.x] = 0.f;
     }
     if (nf > 0) {
-        wait_at_least<32>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
+        wait_at_least_close<32>(unit_cntA(a, u), (unsigned)(nAt - 1), s.err);
         if (owner) wait_at_least<8>(unit_cntP(a, u), 1u, s.err);
         __syncthreads();
         fold_regs<EJ>(a, u, idx, nB, nf, gacc, fh);
