@@ -279,3 +279,41 @@ def test_prepared_call_matches(gpu):
         call()
         torch.cuda.synchronize()
         assert torch.equal(call.out, want)
+
+
+@pytest.mark.parametrize("batch", [32, 33])
+def test_unit_limits(gpu, batch):
+    """H-GSA at 256 units (the single launch's limit: two control records per
+    unit, the last ones at the end of the control block) and at 264 (the
+    multi-launch path), flat GSA at the same batches (512 and 528 units, the
+    flat limit and past it): the first and the last units against the oracle,
+    and the control block zero afterwards."""
+    say(f"[parity] unit limits batch={batch}")
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=gpu)
+    wl = gi.Workload(f"h-limit-b{batch}", gi.BF16, batch, 8, 8, 64, 4, 96, 6, 16,
+                     plant="align_meta", plant_count=2, gists_per_meta=4, top_k_meta=3)
+    inp = gi.make_inputs(wl, 700 + batch, seq_lens=lens_for(wl, "ragged", 30 + batch))
+    g = GU.to(inp, gpu)
+    B, H = wl.batch, wl.num_kv_heads
+    s1 = torch.full((B, H, wl.top_k_meta), -7, dtype=torch.int32, device=gpu)
+    s2 = torch.full((B, H, wl.top_k), -7, dtype=torch.int32, device=gpu)
+    out = gsa.hgsa_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.k_meta, g.v_meta,
+                          num_chunks=wl.num_chunks, chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                          gists_per_meta=wl.gists_per_meta, top_k_meta=wl.top_k_meta, top_k=wl.top_k,
+                          sel_meta=s1, sel_idx=s2, ws=ws)
+    torch.cuda.synchronize()
+    ends = [(0, 0), (B // 2, 3), (B - 1, H - 2), (B - 1, H - 1)]
+    GU.check_hgsa(inp, (out.float().cpu().numpy(), s1.cpu().numpy(), s2.cpu().numpy()), units=ends)
+    assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
+    wl = gi.Workload(f"limit-b{batch}", gi.BF16, batch, 16, 16, 64, 4, 96, 6, 16)
+    inp = gi.make_inputs(wl, 800 + batch, seq_lens=lens_for(wl, "ragged", 40 + batch))
+    g = GU.to(inp, gpu)
+    B, H = wl.batch, wl.num_kv_heads
+    sel = torch.full((B, H, wl.top_k), -7, dtype=torch.int32, device=gpu)
+    out = gsa.gsa_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                         num_chunks=wl.num_chunks, chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                         top_k=wl.top_k, sel_idx=sel, ws=ws)
+    torch.cuda.synchronize()
+    ends = [(0, 0), (B // 2, 7), (B - 1, H - 2), (B - 1, H - 1)]
+    GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None), units=ends)
+    assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
