@@ -15,16 +15,18 @@
 //                      by the select into the unit's record), attends tokens
 //                      [j*TB, (j+1)*TB) of the unfolded list (raw tokens of
 //                      the selected chunks, raw tail, selected gists) and
-//                      writes one partial.  The unit's last one to finish
-//                      merges them into the output and returns the unit's
-//                      record to zero.
-// Waits: unfolded tasks on gist slices (smaller workgroup ids), and the
-// selecting slice of a unit (its last) on the unit's other slices.  The device
-// dispatches each XCD's workgroups in id order, and ids run gist slices
-// first, unit by unit, so the workgroups queued ahead of an awaited slice
-// have smaller ids: slices that wait on nothing, or the selecting slice of an
-// earlier unit.  By induction over units every awaited slice is dispatched
-// and every wait ends.  A wait is nevertheless bounded; giving up sets the
+//                      writes one partial.  The unit's last unfolded task
+//                      keeps its own partial in registers, waits for the
+//                      others' partials, merges them into the output and
+//                      returns the unit's record to zero.
+// Waits: unfolded tasks on gist slices, the merging task on the unit's other
+// unfolded tasks (all of them smaller workgroup ids), and the selecting slice
+// of a unit (its last) on the unit's other slices: every task waits only on
+// tasks with smaller workgroup ids.  The device dispatches each XCD's
+// workgroups in id order, so while the smallest unfinished task is not yet
+// running, every workgroup ahead of it on its XCD has finished and freed its
+// slot; it is then dispatched, and everything it waits on has finished.  By
+// induction every task runs and every wait ends.  A wait is nevertheless bounded; giving up sets the
 // error word of the control block.  Several workgroups per CU hide
 // each task's serial latencies (table lookups, drains) behind the others'
 // streaming, and the unfolded tasks of early units overlap the gist slices of
@@ -52,8 +54,8 @@ constexpr int kThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 24;
 constexpr int kFSelMaxSlices = kRecSlices;  // slices the bucketed select merges
 constexpr int kFSelMaxN = 16384;     // gists per unit the bucketed select handles
-constexpr int kFSelBt = 1024;        // block-table entries the select keeps in LDS
-constexpr int kFSelCand = 2048;      // largest boundary bucket (else the general select)
+constexpr int kFSelBt = 768;         // block-table entries the select keeps in LDS
+constexpr int kFSelCand = 1024;      // largest boundary bucket (else the general select)
 constexpr int kFSelL = kRecLead;     // keys per slice the select reads up front
 
 __device__ inline void st_dev(float* p, float v) {

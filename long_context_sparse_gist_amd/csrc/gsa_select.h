@@ -15,9 +15,9 @@
 
 namespace gsa {
 
-constexpr int kSelCache = 6144;   // general path: keys kept in LDS; longer lists are re-read
+constexpr int kSelCache = 4096;   // general path: keys kept in LDS; longer lists are re-read
 constexpr int kSelFast = 8192;    // fast path: longest list
-constexpr int kSelCandCap = 2048;    // fast path: largest boundary bucket
+constexpr int kSelCandCap = 1536;    // fast path: largest boundary bucket
 
 
 template <int NT>
