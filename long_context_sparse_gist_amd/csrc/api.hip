@@ -127,7 +127,9 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
                    kmeta <= gsa::kRecMeta;
         a.recs_per_unit = pl.hier ? 2 : 1;
     }
-    const int TA = pl.fused ? gsa::kFusedTA : pl.TB;
+    // H-GSA's meta slices and candidate tasks take half as many rows: its
+    // launch is a chain of latency-bound steps, not a bandwidth-bound stream
+    const int TA = pl.fused ? (pl.hier ? gsa::kFusedTAH : gsa::kFusedTA) : pl.TB;
     // unfolded tasks: one block per wavefront, or (flat GSA) two when a
     // launch would hold more than 2048 of them (per-task work then outweighs
     // the tail)

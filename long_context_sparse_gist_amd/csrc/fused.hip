@@ -405,7 +405,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             kept[j] = i < c.ns1 ? ld_dev(mo + i) : 1u;
         }
     }
-    auto slice_n = [&](int sl) { return min(kFusedTA, n - sl * kFusedTA); };
+    auto slice_n = [&](int sl) { return min(sc.TA, n - sl * sc.TA); };
     // everything but the leading keys waits for every other slice to be
     // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
@@ -826,7 +826,8 @@ template <int D, int EJ, int KIND>
 __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
                                             unsigned char* smem, CombineSmem& cs, int* wsum) {
     constexpr int kind = KIND;
-    constexpr int NBW = kFusedTA / 128;  // 32-token blocks per wavefront
+    // 32-token blocks per wavefront: rows per task / 128 (H-GSA's lists: 1)
+    constexpr int NBW = (KIND == kListMeta || KIND == kListCand ? kFusedTAH : kFusedTA) / 128;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int G = a.G, C = a.C;
@@ -952,8 +953,9 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             select_prefetch<KIND>(a, c, n, nA, pre);
             prefetched = true;
         }
-        // thread t takes key slot t % 64 of wavefront t / 64 (NBW * 32 == 64 slots)
-        static_assert(NBW * 32 * 4 == kThreads, "one key slot per thread");
+        // thread t takes key slot t % 64 of wavefront t / 64 (slots past NBW * 32
+        // hold no row: kpos >= cnt there)
+        static_assert(NBW * 32 * 4 <= kThreads, "one key slot per thread");
         __syncthreads();
         const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
         const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
@@ -1009,7 +1011,7 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         uint64_t* lead = cand ? unit_lead_c(a, u) : unit_lead(a, u);
         for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
             const int sl = i / kFSelL;
-            if (i - sl * kFSelL < min(kFusedTA, n - sl * kFusedTA)) st_dev(lead + i, 0ull);
+            if (i - sl * kFSelL < min(s.TA, n - sl * s.TA)) st_dev(lead + i, 0ull);
         }
     }
     // the record entries this select wrote or cleared are in place: the

@@ -138,7 +138,9 @@ struct Sched {
     int hier;          // H-GSA
 };
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
-constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront)
+constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront);
+                               // also the sorted-key capacity of every slice
+constexpr int kFusedTAH = 128; // rows per meta slice or candidate task (H-GSA: one block per wavefront)
 constexpr int kFusedTB = 128;  // tokens per unfolded task (one 32-token block per wavefront; twice
                                // that for launches with many unfolded tasks)
 constexpr int kBins = 2048;    // buckets of a routing key's top 11 bits
