@@ -862,7 +862,19 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             }
     } else if (cand && cnt > 0) {
         // the gists of the kept meta-groups (the meta select's entries in the
-        // unit's record, polled), then the gists past the last complete group
+        // unit's record, polled), then the gists past the last complete group.
+        // The sequence's block-table row goes into the (unused) V-tile LDS while
+        // the meta select runs, so the page lookups cost no round trip after it.
+        const bool btc = a.max_pages <= Lds::stash(D) / 4;
+        int* bl = (int*)smem;
+        if (btc) {
+            const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
+            for (int e0 = 64 * w; e0 < a.max_pages; e0 += 64 * 4) {
+                // lane l writes entry e0 + l (a lane past the row rereads its last entry)
+                const int e = min(e0 + lane, a.max_pages - 1);
+                __builtin_amdgcn_global_load_lds(btrow + e, (lds_void_t*)(smem + 4 * e0), 4, 0, 0);
+            }
+        }
         const unsigned* mo = unit_meta(a, u);
         const int head = c.ns1 * a.R;
         unsigned grp[NBW][2];
@@ -893,6 +905,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                 for (int t = 0; t < 2; ++t)
                     if (grp[j][t] == 0u) grp[j][t] = ld_dev(mo + min(row_p(j, t), n - 1) / a.R);
         }
+        if (btc) {  // every wavefront's row entries are in LDS
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
@@ -900,7 +916,9 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
                 const int p = min(row_p(j, t), n - 1);
                 const int r = p / a.R;
                 const int gist = p < head ? (int)(grp[j][t] - 1u) * a.R + (p - r * a.R) : c.nm * a.R + (p - head);
-                off[j][t] = slot_offset(a, b, g, gist * (C + 1) + C);
+                const int sl = gist * (C + 1) + C, lp = sl / a.spp;
+                const int phys = btc ? bl[lp] : a.bt[(size_t)b * a.max_pages + lp];
+                off[j][t] = (((size_t)phys * a.Hkv + g) * a.spp + (sl - lp * a.spp)) * (size_t)D;
             }
     }
     const bool attn = meta || (kind == kListGists && !(a.flags & kFlagSelectedGists));

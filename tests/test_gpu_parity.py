@@ -317,3 +317,38 @@ def test_unit_limits(gpu, batch):
     ends = [(0, 0), (B // 2, 7), (B - 1, H - 2), (B - 1, H - 1)]
     GU.check_gsa(inp, (out.float().cpu().numpy(), sel.cpu().numpy(), None), units=ends)
     assert int(ws[:gsa.WORKSPACE_CONTROL_BYTES].count_nonzero()) == 0
+
+
+# Block-table rows around the lengths the kernels keep in LDS: the flat select
+# keeps a row of up to 768 pages; H-GSA's candidate tasks keep a row of up to
+# 4096 pages (head_dim 64) or 8192 (head_dim 128).  One chunk per page: a row
+# holds num_chunks + 1 pages (chunk size 2) or num_chunks (chunk size 1).
+LONG_ROWS = {
+    "rows-flat-768": gi.Workload("rows-flat-768", gi.BF16, 2, 8, 2, 64, 2, 767, 20, 1,
+                                 plant="align", plant_count=3),
+    "rows-flat-1001": gi.Workload("rows-flat-1001", gi.BF16, 2, 8, 2, 64, 2, 1000, 20, 1,
+                                  plant="align", plant_count=3),
+    "rows-h-d64-4096": gi.Workload("rows-h-d64-4096", gi.BF16, 1, 8, 2, 64, 2, 4095, 16, 1,
+                                   plant="align_meta", plant_count=2, gists_per_meta=16,
+                                   top_k_meta=6),
+    "rows-h-d64-4201": gi.Workload("rows-h-d64-4201", gi.BF16, 1, 8, 2, 64, 2, 4200, 16, 1,
+                                   plant="align_meta", plant_count=2, gists_per_meta=16,
+                                   top_k_meta=6),
+    "rows-h-d128-8192": gi.Workload("rows-h-d128-8192", gi.BF16, 1, 4, 1, 128, 1, 8192, 16, 1,
+                                    plant="align_meta", plant_count=2, gists_per_meta=16,
+                                    top_k_meta=6),
+    "rows-h-d128-8300": gi.Workload("rows-h-d128-8300", gi.BF16, 1, 4, 1, 128, 1, 8300, 16, 1,
+                                    plant="align_meta", plant_count=2, gists_per_meta=16,
+                                    top_k_meta=6),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LONG_ROWS))
+def test_long_block_table_rows(gpu, name):
+    wl = LONG_ROWS[name]
+    say(f"[parity] {name} max_pages={wl.max_pages}")
+    inp = gi.make_inputs(wl, 300 + len(name), seq_lens=lens_for(wl, "ragged", 11))
+    if wl.hgsa:
+        GU.check_hgsa(inp, GU.run_gpu_h(GU.to(inp, gpu)))
+    else:
+        GU.check_gsa(inp, GU.run_gpu(GU.to(inp, gpu)))
