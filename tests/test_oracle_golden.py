@@ -1,0 +1,149 @@
+"""Hand-worked examples (tests/golden/hand_worked.txt): the oracle, and the GPU
+library through its C ABI, against outputs worked out by hand.
+
+The inputs make every softmax weight an integer (keys are logarithms, scale 1),
+so the expected selections, routing keys and outputs are exact fractions
+derived in the fixture's comments, independently of both implementations.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.txt")
+FILL_K, FILL_V = math.log(1000.0), 999.0  # slots no example may read
+
+
+def load_cases(path=GOLDEN):
+    cases, cur = {}, None
+    with open(path) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "case":
+                cur = {"name": tok[1], "slots": {}, "meta": {}}
+            elif tok[0] == "end":
+                cases[cur["name"]] = cur
+                cur = None
+            elif tok[0] == "cite":
+                cur["cite"] = " ".join(tok[1:])
+            elif tok[0] == "config":
+                cur["cfg"] = {k: int(v) for k, v in (t.split("=") for t in tok[1:])}
+            elif tok[0] == "q":
+                cur["q"] = [float(x) for x in tok[1:]]
+            elif tok[0] == "slot":
+                cur["slots"][int(tok[1])] = [float(x) for x in tok[3:]]
+            elif tok[0] == "meta":
+                cur["meta"][int(tok[1])] = [float(x) for x in tok[2:]]
+            elif tok[0] in ("expect_sel", "expect_sel_meta"):
+                cur[tok[0]] = [int(x) for x in tok[1:]]
+            elif tok[0] in ("expect_scores", "expect_out"):
+                cur[tok[0]] = [float(x) for x in tok[1:]]
+            else:
+                raise ValueError(f"unknown fixture line: {line}")
+    return cases
+
+
+CASES = load_cases()
+
+
+def arrays(case, d):
+    """One page holding every slot, head dim d (the example's 2 dims, then 0)."""
+    c = case["cfg"]
+    C, P = c["chunk_size"], c["page_chunks"]
+    spp = P * (C + 1)
+    k = np.zeros((1, 1, spp, d), np.float32)
+    v = np.zeros((1, 1, spp, d), np.float32)
+    k[0, 0, :, 0], v[0, 0, :, 0], v[0, 0, :, 1] = FILL_K, FILL_V, FILL_V
+    for s, (k0, k1, v0, v1) in case["slots"].items():
+        k[0, 0, s, :2] = (k0, k1)
+        v[0, 0, s, :2] = (v0, v1)
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, :2] = case["q"]
+    km = vm = None
+    if case["meta"]:
+        mm = c["max_meta"]
+        km = np.zeros((1, 1, mm, d), np.float32)
+        vm = np.zeros((1, 1, mm, d), np.float32)
+        for r, (k0, k1, v0, v1) in case["meta"].items():
+            km[0, 0, r, :2] = (k0, k1)
+            vm[0, 0, r, :2] = (v0, v1)
+    bt = np.zeros((1, 1), np.int32)
+    sl = np.array([c["seq_len"]], np.int32)
+    return q, k, v, bt, sl, km, vm
+
+
+def oracle_cfg(case, d):
+    c = case["cfg"]
+    cfg = dict(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=d, top_k=c["top_k"],
+               sm_scale=1.0, dtype=0, flags=0, num_chunks=c["num_chunks"],
+               chunk_size=c["chunk_size"], page_chunks=c["page_chunks"], num_pages=1,
+               max_pages=1)
+    if case["meta"]:
+        cfg.update(gists_per_meta=c["gists_per_meta"], top_k_meta=c["top_k_meta"],
+                   max_meta=c["max_meta"])
+    return cfg
+
+
+def test_fixture_is_complete():
+    assert set(CASES) == {"gsa-k1", "gsa-k2", "hgsa-k1", "hgsa-k2"}
+    for case in CASES.values():
+        assert case["cite"] and case["expect_out"] and case["expect_sel"]
+
+
+@pytest.mark.parametrize("name", sorted(n for n in CASES if not CASES[n]["meta"]))
+def test_oracle_gsa_hand_worked(name):
+    case = CASES[name]
+    q, k, v, bt, sl, _, _ = arrays(case, 2)
+    out, sel, sc = oracle.gsa_decode(oracle_cfg(case, 2), q, k, v, bt, sl)
+    assert sel[0, 0].tolist() == case["expect_sel"]
+    np.testing.assert_allclose(sc[0, 0], case["expect_scores"], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(out[0, 0, :2], case["expect_out"], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", sorted(n for n in CASES if CASES[n]["meta"]))
+def test_oracle_hgsa_hand_worked(name):
+    case = CASES[name]
+    q, k, v, bt, sl, km, vm = arrays(case, 2)
+    out, s1, s2, _, _ = oracle.hgsa_decode(oracle_cfg(case, 2), q, k, v, bt, sl, km, vm)
+    assert s1[0, 0].tolist() == case["expect_sel_meta"]
+    assert s2[0, 0].tolist() == case["expect_sel"]
+    np.testing.assert_allclose(out[0, 0, :2], case["expect_out"], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_gpu_hand_worked(gpu, name):
+    """The library (fp32 kernels, head_dim 64: the example padded with zeros)."""
+    import torch
+    import long_context_sparse_gist_amd as gsa
+    case = CASES[name]
+    c = case["cfg"]
+    print(f"[golden] {name}", flush=True)
+    q, k, v, bt, sl, km, vm = (None if x is None else torch.from_numpy(x).to(gpu)
+                               for x in arrays(case, 64))
+    sel = torch.full((1, 1, c["top_k"]), -7, dtype=torch.int32, device=gpu)
+    if case["meta"]:
+        sm = torch.full((1, 1, c["top_k_meta"]), -7, dtype=torch.int32, device=gpu)
+        out = gsa.hgsa_decode(q, k, v, bt, sl, km, vm, num_chunks=c["num_chunks"],
+                              chunk_size=c["chunk_size"], page_chunks=c["page_chunks"],
+                              gists_per_meta=c["gists_per_meta"], top_k_meta=c["top_k_meta"],
+                              top_k=c["top_k"], sm_scale=1.0, sel_meta=sm, sel_idx=sel)
+        torch.cuda.synchronize()
+        assert sm[0, 0].tolist() == case["expect_sel_meta"]
+    else:
+        sc = torch.full((1, 1, c["num_chunks"]), 7.0, dtype=torch.float32, device=gpu)
+        out = gsa.gsa_decode(q, k, v, bt, sl, num_chunks=c["num_chunks"],
+                             chunk_size=c["chunk_size"], page_chunks=c["page_chunks"],
+                             top_k=c["top_k"], sm_scale=1.0, sel_idx=sel, scores=sc)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(sc[0, 0].cpu().numpy(), case["expect_scores"], rtol=0, atol=1e-5)
+    assert sel[0, 0].tolist() == case["expect_sel"]
+    o = out[0, 0].cpu().numpy()
+    np.testing.assert_allclose(o[:2], case["expect_out"], rtol=1e-5, atol=1e-4)
+    assert np.all(o[2:] == 0.0)
