@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=gi.QWEN7B_128K.name, choices=sorted(gi.BY_NAME))
+    ap.add_argument("--score", default="sum_logits", choices=["sum_logits", "sum_probs"],
+                    help="group routing key (flat GSA): sum of the heads' logits, or of their "
+                         "softmax probabilities over the gists (multi-launch kernels)")
     ap.add_argument("--copies", type=int, default=6,
                     help="cache copies rotated between calls (defeats the Infinity Cache)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -87,7 +90,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(inp, seconds: float):
+def cpu_baseline(inp, seconds: float, flags: int = 0):
     """The oracle, as it stands, on the host cores: the whole batch, repeated
     until `seconds` of wall time (at least one run)."""
     import oracle
@@ -98,7 +101,7 @@ def cpu_baseline(inp, seconds: float):
     vc = U.np_raw(inp.v_cache)
     bt = U.np_raw(inp.block_table)
     sl = U.np_raw(inp.seq_lens)
-    cfg = U.cfg_of(inp)
+    cfg = U.cfg_of(inp, flags=flags)
     threads = oracle.max_threads()
     times = []
     t_end = time.perf_counter() + seconds
@@ -125,6 +128,14 @@ def main():
               f"no multi-GPU mode in this build", file=sys.stderr)
         sys.exit(2)
     wl = gi.BY_NAME[args.workload]
+    flags = 0
+    if args.score == "sum_probs":
+        if wl.hgsa or wl.dtype != gi.BF16:
+            print("--score sum_probs applies to the flat bf16 workloads", file=sys.stderr)
+            sys.exit(2)
+        flags = gsa.GSA_SCORE_SUM_PROBS
+    # one launch per call (the bf16 default key); else the multi-launch kernels
+    single = wl.dtype == gi.BF16 and flags == 0
     idx = gi.WORKLOADS.index(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -152,7 +163,7 @@ def main():
         return gsa.prepare_gsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
                                       num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
                                       page_chunks=wl.page_chunks, top_k=wl.top_k, out=out,
-                                      stream=stream)
+                                      flags=flags, stream=stream)
     calls = [prepare(c) for c in copies]
 
     def step(i):
@@ -218,23 +229,24 @@ def main():
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "context_tokens": wl.raw_tokens, "chunk_size": wl.chunk_size,
                    "top_k": wl.top_k, "page_chunks": wl.page_chunks,
-                   "cache_copies": len(copies)},
+                   "score": args.score, "cache_copies": len(copies)},
         "hbm_gbps_alg": achieved,
         "launch_us": mean_call_s * 1e6,
         "single_launch_us": {"mean": statistics.fmean(call_ms) * 1e3,
                     "median": statistics.median(call_ms) * 1e3,
                     "p10": float(np.percentile(call_ms, 10)) * 1e3,
                     "p90": float(np.percentile(call_ms, 90)) * 1e3},
-        "roofline": {"bound": "hbm", "kernel": KERNEL if not wl.hgsa else "hgsa_decode launches",
+        "roofline": {"bound": "hbm", "kernel": KERNEL if single else
+                     ("hgsa_decode launches" if wl.hgsa else "gsa_decode launches (multi-launch)"),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(wl.name) if not wl.hgsa else None,
+                     "traffic": measured_traffic(wl.name) if single and not wl.hgsa else None,
                      "alg_bytes_per_launch": nbytes, "kernel_hash": kernel_hash()},
     }
     if args.cpu_baseline:
         del copies, calls
         torch.cuda.empty_cache()
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, flags)
     print(json.dumps(res), flush=True)
 
 

@@ -60,7 +60,9 @@ typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype_t;
 /* Routing key shared by the query heads of one GQA group (one selection per
  * (batch, kv-head)).  Default: the sum over the group of the scaled logits
  * sm_scale * q_h . k_gist.  SUM_PROBS: the sum over the group of each head's
- * softmax probability of the gist, the softmax taken over the gists. */
+ * softmax probability of the gist, the softmax taken over the sequence's gists
+ * (gsa_decode only; it needs every gist's logits before any key, so the call
+ * runs the multi-launch kernels). */
 #define GSA_SCORE_SUM_LOGITS 0x0u
 #define GSA_SCORE_SUM_PROBS 0x1u
 /* Attention set.  Default: every gist plus the raw tokens of the selected
@@ -157,7 +159,8 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
  * the gists of the kept groups (plus the gists after the last complete
  * group), keep the top_k of those, and attend over every meta-gist, the kept
  * gists, the gists after the last complete group, the raw tokens of the kept
- * chunks and the raw tokens after the last gist.  flags: GSA_SCORE_* only.
+ * chunks and the raw tokens after the last gist.  flags: 0 (the default key
+ * and set) or GSA_PATH_PORTABLE; other flags return GSA_ERR_BAD_FLAGS.
  *   sel_meta : NULL, or int32 [batch][num_kv_heads][top_k_meta] ascending, -1 padded
  *   sel_idx  : NULL, or int32 [batch][num_kv_heads][top_k] ascending, -1 padded */
 gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv,

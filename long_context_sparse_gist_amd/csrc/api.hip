@@ -38,7 +38,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, off_spairs_c, total;
+        off_spairs, off_spairs_c, off_hlog, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -52,7 +52,6 @@ gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
     if (!(p->sm_scale == p->sm_scale) || isinf(p->sm_scale)) return GSA_ERR_BAD_SHAPE;
     const unsigned known = GSA_SCORE_SUM_PROBS | GSA_SET_SELECTED_GISTS | gsa::kFlagPortable;
     if (p->flags & ~known) return GSA_ERR_BAD_FLAGS;
-    if (p->flags & GSA_SCORE_SUM_PROBS) return GSA_ERR_BAD_FLAGS;  // not provided by this build
     if (kv->chunk_size < 1 || kv->page_chunks < 1 || kv->num_chunks < 0) return GSA_ERR_BAD_SHAPE;
     if (kv->num_pages < 1 || kv->max_pages < 1) return GSA_ERR_BAD_SHAPE;
     long spp = (long)kv->page_chunks * (kv->chunk_size + 1);
@@ -70,6 +69,7 @@ gsa_status_t check_meta(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_me
     if (m->max_meta < kv->num_chunks / m->gists_per_meta) return GSA_ERR_BAD_SHAPE;
     if ((long)p->batch * p->num_kv_heads * (long)m->max_meta > (1L << 40)) return GSA_ERR_BAD_SHAPE;
     if (p->flags & GSA_SET_SELECTED_GISTS) return GSA_ERR_BAD_FLAGS;
+    if (p->flags & GSA_SCORE_SUM_PROBS) return GSA_ERR_BAD_FLAGS;  // flat GSA only
     return GSA_OK;
 }
 
@@ -123,8 +123,10 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         const long kc = pl.hier ? pl.cand_cap : M;
         const long ksel = p->top_k < kc ? p->top_k : kc;
         const long kmeta = pl.hier ? (m->top_k_meta < cap1 ? m->top_k_meta : cap1) : 0;
+        // (the sum-of-probabilities key needs every gist's logits before any key:
+        // multi-launch path)
         pl.fused = pl.mfma && units * (pl.hier ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
-                   kmeta <= gsa::kRecMeta;
+                   kmeta <= gsa::kRecMeta && !(p->flags & GSA_SCORE_SUM_PROBS);
         a.recs_per_unit = pl.hier ? 2 : 1;
     }
     // H-GSA's meta slices and candidate tasks take half as many rows: its
@@ -170,6 +172,8 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     const size_t fslices = pl.fused ? (size_t)units * pl.S1 : 0;
     pl.off_spairs = off; off += align_up(sizeof(uint64_t) * fslices * gsa::kFusedTA);
     pl.off_spairs_c = off; off += align_up(sizeof(uint64_t) * (size_t)units * pl.sc.S3 * gsa::kFusedTA);
+    const bool probs = !pl.hier && (p->flags & GSA_SCORE_SUM_PROBS);
+    pl.off_hlog = off;  off += align_up(sizeof(float) * (probs ? (size_t)units * a.G * M : 0));
     pl.total = off;
 }
 
@@ -244,6 +248,7 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     a.seq_lens = kv->seq_lens;
     a.keys = scores ? scores : (float*)(ws + pl.off_keys);
     a.sel = sel_idx ? sel_idx : (int32_t*)(ws + pl.off_sel);
+    a.hlog = (p->flags & GSA_SCORE_SUM_PROBS) ? (float*)(ws + pl.off_hlog) : nullptr;
     a.part_ml = (float2*)(ws + pl.off_ml);
     a.part_acc = (float*)(ws + pl.off_acc);
     a.out = out;

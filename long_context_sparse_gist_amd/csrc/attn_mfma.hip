@@ -157,6 +157,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
                     int v = blk * 8 + t * 4 + r;
                     if (v == lr) { kv = x; krel = rel_of(blk, t, r); }
                 }
+        if (kind == kListGists && a.hlog && lr < G) {
+            // per-head logits for the sum-of-probabilities key (this lane: head lr)
+            float* hl = a.hlog + ((size_t)u * G + lr) * a.key_stride + p0;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (rel_of(blk, t, r) < count) hl[rel_of(blk, t, r)] = s[blk][t][r] * a.tau;
+        }
         if (krel >= 0 && krel < count) {
             int p = p0 + krel;
             if (kind == kListGists) {

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(256) void attn_portable_kernel(Args a, int kind, in
         for (int h = 0; h < G; ++h) S += z[h][tid];
         S *= a.tau;
         int p = p0 + tid;
+        if (kind == kListGists && a.hlog)  // per-head logits for the sum-of-probabilities key
+            for (int h = 0; h < G; ++h) a.hlog[((size_t)u * G + h) * a.key_stride + p] = z[h][tid] * a.tau;
         if (kind == kListGists) {
             a.keys[(size_t)u * a.key_stride + p] = S;
         } else if (kind == kListMeta) {

@@ -36,6 +36,7 @@ struct Args {
     // work buffers
     float* keys;      // [units][key_stride] routing keys
     int key_stride;
+    float* hlog;      // [units][G][key_stride] per-head gist logits (sum-of-probabilities key), else null
     int32_t* sel;     // [units][top_k] selected chunk ids, ascending, -1 padded
     int32_t* sel_meta;   // [units][top_k_meta] (H-GSA)
     float* mkeys;     // [units][max_meta] meta routing keys (H-GSA)

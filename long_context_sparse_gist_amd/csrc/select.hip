@@ -8,14 +8,49 @@ namespace {
 
 constexpr int kThreads = 512;
 
+// Block-wide max / sum of one value per thread (every thread gets the result).
+__device__ inline float block_reduce(float x, bool is_max, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    __syncthreads();  // the previous use of red is over
+    if (lane == 0) red[w] = x;
+    __syncthreads();
+    x = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) x = is_max ? fmaxf(x, red[i]) : x + red[i];
+    return x;
+}
+
+// Sum-of-probabilities routing key of the unit's n gists: for each head of the
+// group, the softmax of its logits over the gists; the key of a gist is the sum
+// of its probabilities over the heads.  Overwrites the sum-of-logits keys.
+__device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* red) {
+    for (int h = 0; h < a.G; ++h) {
+        const float* z = a.hlog + ((size_t)u * a.G + h) * a.key_stride;
+        float m = -INFINITY;
+        for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, z[i]);
+        m = block_reduce(m, true, red);
+        float l = 0.f;
+        for (int i = threadIdx.x; i < n; i += kThreads) l += expf(z[i] - m);
+        l = block_reduce(l, false, red);
+        // each thread updates only the entries it owns: no barrier between heads
+        for (int i = threadIdx.x; i < n; i += kThreads) kw[i] = (h ? kw[i] : 0.f) + expf(z[i] - m) / l;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
     __shared__ SelectSmem<kThreads> sh;
+    __shared__ float red[kThreads / 64];
     const int u = blockIdx.x;
     ListCtx c;
     make_ctx(a, mode == kSelCand ? kListCand : kListGists, u, mode != kSelGists, c);
     if (mode == kSelGists) {
         // scores past the sequence's gists read -inf
         float* kw = a.keys + (size_t)u * a.key_stride;
+        if (a.hlog) sum_probs_keys(a, u, c.n, kw, red);
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) kw[i] = -INFINITY;
         block_topk<kThreads>(a.keys + (size_t)u * a.key_stride, nullptr, c.n, a.top_k,
                              a.sel + (size_t)u * a.top_k, false, sh);

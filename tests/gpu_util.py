@@ -21,6 +21,9 @@ from tests import _util as U
 GAP = 1e-3
 TOL = {gi.BF16: (2e-2, 1e-2), gi.F32: (1e-4, 1e-4)}   # (atol, rtol)
 KEY_TOL = (1e-3, 1e-4)
+# sum-of-probabilities keys are probabilities: relative tolerance, and the gap
+# rule applies to the keys divided by the unit's largest key
+KEY_TOL_PROBS = (1e-7, 1e-3)
 
 
 def to(inp, device):
@@ -132,14 +135,17 @@ def check_gsa(inp, gpu_res, units=None, top_k=None, flags=0, sm_scale=0.0):
         sub = to(unit_inputs(inp, b, g), "cpu")
         o_out, o_sel, o_sc = U.run_oracle(sub, top_k=k, flags=flags, sm_scale=sm_scale)
         n = int(sub.seq_lens[0]) // wl.chunk_size
+        probs = bool(flags & gsa.GSA_SCORE_SUM_PROBS)
         if sc is not None:
-            if not (flags & gsa.GSA_SCORE_SUM_PROBS):
-                assert np.all(np.isneginf(sc[b, g, n:]))
-            atol, rtol = KEY_TOL
+            assert np.all(np.isneginf(sc[b, g, n:]))
+            atol, rtol = KEY_TOL_PROBS if probs else KEY_TOL
             d = np.abs(sc[b, g, :n].astype(np.float64) - o_sc[0, 0, :n])
             assert np.all(d <= atol + rtol * np.abs(o_sc[0, 0, :n])), \
                 f"unit {(b, g)}: key error {d.max():.3g}"
-        same = check_set(sel[b, g], o_sc[0, 0, :n], k)
+        gk = o_sc[0, 0, :n].astype(np.float64)
+        if probs and n:
+            gk = gk / max(float(np.max(gk)), 1e-30)
+        same = check_set(sel[b, g], gk, k)
         if not same:
             differ += 1
             o_out, _, _ = U.run_oracle(sub, top_k=k, flags=flags, sm_scale=sm_scale,

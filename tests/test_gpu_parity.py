@@ -83,6 +83,52 @@ def test_small_selected_gists_set(gpu, name):
     GU.check_gsa(inp, res, flags=flags)
 
 
+@pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16", "b2-g16-d64-c4", "f32-b2-g3-d64"])
+@pytest.mark.parametrize("lens", ["full", "edge"])
+def test_small_sum_probs_key(gpu, name, lens):
+    wl = SMALL[name]
+    say(f"[parity] {name} sum-of-probabilities key lens={lens}")
+    inp = gi.make_inputs(wl, 21, seq_lens=lens_for(wl, lens, 6))
+    flags = gsa.GSA_SCORE_SUM_PROBS
+    res = GU.run_gpu(GU.to(inp, gpu), flags=flags)
+    GU.check_gsa(inp, res, flags=flags)
+
+
+@pytest.mark.parametrize("extra", ["selected-gists", "portable"])
+def test_sum_probs_key_combined(gpu, extra):
+    wl = SMALL["b2-g7-d128-c16"]
+    say(f"[parity] sum-of-probabilities key + {extra}")
+    inp = gi.make_inputs(wl, 23, seq_lens=lens_for(wl, "ragged", 7))
+    flags = gsa.GSA_SCORE_SUM_PROBS | (gsa.GSA_SET_SELECTED_GISTS if extra == "selected-gists"
+                                       else gsa.GSA_PATH_PORTABLE)
+    res = GU.run_gpu(GU.to(inp, gpu), flags=flags)
+    GU.check_gsa(inp, res, flags=flags & ~gsa.GSA_PATH_PORTABLE)
+
+
+def test_sum_probs_key_full_workload_sampled_units(gpu):
+    wl = gi.QWEN7B_128K
+    say(f"[parity] full {wl.name} sum-of-probabilities key")
+    inp = gi.make_inputs(wl, gi.seed_of(2), device=gpu)
+    flags = gsa.GSA_SCORE_SUM_PROBS
+    res = GU.run_gpu(inp, flags=flags)
+    rng = random.Random(12)
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    GU.check_gsa(inp, res, units=rng.sample(units, 3), flags=flags)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_sum_probs_key_rejected_by_hgsa(gpu):
+    wl = SMALL_H["h-b2-g4-d64-r4"]
+    inp = GU.to(gi.make_inputs(wl, 3), gpu)
+    with pytest.raises(gsa.GsaError):
+        gsa.hgsa_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens,
+                        inp.k_meta, inp.v_meta, num_chunks=wl.num_chunks,
+                        chunk_size=wl.chunk_size, page_chunks=wl.page_chunks,
+                        gists_per_meta=wl.gists_per_meta, top_k_meta=wl.top_k_meta,
+                        top_k=wl.top_k, flags=gsa.GSA_SCORE_SUM_PROBS)
+
+
 @pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16"])
 def test_portable_path_on_bf16(gpu, name):
     wl = SMALL[name]
