@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--score", default="sum_logits", choices=["sum_logits", "sum_probs"],
                     help="group routing key (flat GSA): sum of the heads' logits, or of their "
                          "softmax probabilities over the gists (multi-launch kernels)")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="top-p selection with this probability mass, top_k as its cap "
+                         "(flat GSA, multi-launch kernels); 0: top-k")
     ap.add_argument("--copies", type=int, default=6,
                     help="cache copies rotated between calls (defeats the Infinity Cache)")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -90,7 +93,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(inp, seconds: float, flags: int = 0):
+def cpu_baseline(inp, seconds: float, flags: int = 0, top_p: float = 0.0):
     """The oracle, as it stands, on the host cores: the whole batch, repeated
     until `seconds` of wall time (at least one run)."""
     import oracle
@@ -101,7 +104,7 @@ def cpu_baseline(inp, seconds: float, flags: int = 0):
     vc = U.np_raw(inp.v_cache)
     bt = U.np_raw(inp.block_table)
     sl = U.np_raw(inp.seq_lens)
-    cfg = U.cfg_of(inp, flags=flags)
+    cfg = U.cfg_of(inp, flags=flags | (oracle.SELECT_TOP_P if top_p > 0.0 else 0), top_p=top_p)
     threads = oracle.max_threads()
     times = []
     t_end = time.perf_counter() + seconds
@@ -134,8 +137,11 @@ def main():
             print("--score sum_probs applies to the flat bf16 workloads", file=sys.stderr)
             sys.exit(2)
         flags = gsa.GSA_SCORE_SUM_PROBS
-    # one launch per call (the bf16 default key); else the multi-launch kernels
-    single = wl.dtype == gi.BF16 and flags == 0
+    if args.top_p > 0.0 and (wl.hgsa or flags):
+        print("--top-p applies to the flat workloads with the default key", file=sys.stderr)
+        sys.exit(2)
+    # one launch per call (the bf16 default key, top-k); else the multi-launch kernels
+    single = wl.dtype == gi.BF16 and flags == 0 and args.top_p == 0.0
     idx = gi.WORKLOADS.index(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -163,7 +169,7 @@ def main():
         return gsa.prepare_gsa_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
                                       num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
                                       page_chunks=wl.page_chunks, top_k=wl.top_k, out=out,
-                                      flags=flags, stream=stream)
+                                      flags=flags, top_p=args.top_p, stream=stream)
     calls = [prepare(c) for c in copies]
 
     def step(i):
@@ -209,6 +215,16 @@ def main():
 
     queries = wl.batch * wl.num_q_heads
     nbytes = alg_bytes(wl)
+    if args.top_p > 0.0:
+        # top-p keeps a different number of chunks per unit: count them
+        sel = torch.full((wl.batch, wl.num_kv_heads, wl.top_k), -1, dtype=torch.int32, device=dev)
+        gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens,
+                       num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                       page_chunks=wl.page_chunks, top_k=wl.top_k, top_p=args.top_p, sel_idx=sel)
+        kept = int((sel >= 0).sum().item())
+        units = wl.batch * wl.num_kv_heads
+        e, d, G = wl.elem_bytes, wl.head_dim, wl.group
+        nbytes = units * (e * d * 2 * wl.num_chunks + 2 * G * d * e) + kept * 2 * wl.chunk_size * d * e
     ms_per_step = wall / args.steps * 1e3
     value = queries * args.steps / wall
     achieved = nbytes / mean_call_s / 1e9
@@ -229,7 +245,8 @@ def main():
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "context_tokens": wl.raw_tokens, "chunk_size": wl.chunk_size,
                    "top_k": wl.top_k, "page_chunks": wl.page_chunks,
-                   "score": args.score, "cache_copies": len(copies)},
+                   "score": args.score, "top_p": args.top_p or None,
+                   "cache_copies": len(copies)},
         "hbm_gbps_alg": achieved,
         "launch_us": mean_call_s * 1e6,
         "single_launch_us": {"mean": statistics.fmean(call_ms) * 1e3,
@@ -246,7 +263,7 @@ def main():
     if args.cpu_baseline:
         del copies, calls
         torch.cuda.empty_cache()
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, flags)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, flags, args.top_p)
     print(json.dumps(res), flush=True)
 
 

@@ -70,6 +70,17 @@ typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype_t;
  * tokens (the "SG+SR" rule of the ja page's ablation, section 4). */
 #define GSA_SET_ALL_GISTS 0x0u
 #define GSA_SET_SELECTED_GISTS 0x2u
+/* Selection rule.  Default: the top_k largest keys.  SELECT_TOP_P: top-p
+ * (nucleus) selection, the alternative the ja page's ablation (section 4) and
+ * the nl page's results ("Stabiliteit") compare with top-k: the chunks in key
+ * order (largest first, ties to the lower index, NaN last) up to and including
+ * the first at which the running sum of their selection probabilities reaches
+ * top_p, at most top_k of them (top_k <= 2048 then).  A chunk's selection
+ * probability is the softmax of its key over the sequence's gists (NaN keys:
+ * 0); with no finite largest key the first min(top_k, n) are taken.  Default
+ * key only; gsa_decode only; runs the multi-launch kernels.  sel_idx then holds
+ * a variable number of ids per (batch, kv-head), -1 padded. */
+#define GSA_SELECT_TOP_P 0x4u
 /* Run the portable fp32-VALU kernels instead of the MFMA kernels (the fp32
  * dtype always uses them); a cross-check of the bf16 MFMA path. */
 #define GSA_PATH_PORTABLE 0x100u
@@ -84,7 +95,9 @@ typedef struct {
                               For hgsa_decode: k2, the gist-level top-k. */
     float sm_scale;        /* softmax scale tau; <= 0 selects 1/sqrt(d) */
     int32_t dtype;         /* gsa_dtype_t of q, caches, meta caches and out */
-    uint32_t flags;        /* GSA_SCORE_* | GSA_SET_* */
+    uint32_t flags;        /* GSA_SCORE_* | GSA_SET_* | GSA_SELECT_* | GSA_PATH_* */
+    float top_p;           /* with GSA_SELECT_TOP_P: probability mass to keep, in (0, 1];
+                              ignored otherwise */
 } gsa_params_t;
 
 /* Paged interleaved raw+gist KV cache.

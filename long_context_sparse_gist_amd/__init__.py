@@ -25,6 +25,7 @@ GSA_SCORE_SUM_LOGITS = 0x0
 GSA_SCORE_SUM_PROBS = 0x1
 GSA_SET_ALL_GISTS = 0x0
 GSA_SET_SELECTED_GISTS = 0x2
+GSA_SELECT_TOP_P = 0x4
 GSA_PATH_PORTABLE = 0x100
 # bytes at the start of every workspace that must be zero between calls
 WORKSPACE_CONTROL_BYTES = 16384 + 512 * 25088
@@ -38,7 +39,7 @@ class GsaParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("top_p", ctypes.c_float)]
 
 
 class GsaKV(ctypes.Structure):
@@ -112,9 +113,12 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_params(q: torch.Tensor, num_kv_heads: int, top_k: int, sm_scale: float = 0.0,
-                flags: int = 0) -> GsaParams:
+                flags: int = 0, top_p: float = 0.0) -> GsaParams:
+    """top_p > 0 selects top-p selection (GSA_SELECT_TOP_P), top_k its cap."""
     B, Hq, d = q.shape
-    return GsaParams(B, Hq, num_kv_heads, d, top_k, sm_scale, _dtype_code(q), flags)
+    if top_p > 0.0:
+        flags |= GSA_SELECT_TOP_P
+    return GsaParams(B, Hq, num_kv_heads, d, top_k, sm_scale, _dtype_code(q), flags, top_p)
 
 
 def make_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -187,13 +191,13 @@ class PreparedCall:
 
 def prepare_gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
                        chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
-                       flags: int = 0, out=None, sel_idx=None, scores=None, ws=None,
-                       stream=None) -> PreparedCall:
+                       flags: int = 0, top_p: float = 0.0, out=None, sel_idx=None, scores=None,
+                       ws=None, stream=None) -> PreparedCall:
     """gsa_decode's arguments marshalled into a PreparedCall; `out` is
     allocated here if not given and can be read back as `.out`."""
     _check(q, k_cache, v_cache, block_table, seq_lens)
     Hkv = k_cache.shape[1]
-    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    p = make_params(q, Hkv, top_k, sm_scale, flags, top_p)
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     if out is None:
         out = torch.empty_like(q)
@@ -241,15 +245,17 @@ def prepare_hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_me
 
 def gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
                chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
-               flags: int = 0, out=None, sel_idx=None, scores=None, ws=None, stream=None):
+               flags: int = 0, top_p: float = 0.0, out=None, sel_idx=None, scores=None,
+               ws=None, stream=None):
     """One GSA decode step (see gsa_decode in include/gsa.h).
 
     q [B][Hq][d]; k_cache, v_cache [num_pages][Hkv][page_chunks*(C+1)][d];
-    block_table int32 [B][max_pages]; seq_lens int32 [B] or None.
+    block_table int32 [B][max_pages]; seq_lens int32 [B] or None.  top_p > 0:
+    top-p selection with top_k as its cap.
     Returns out [B][Hq][d] (allocated if not given)."""
     _check(q, k_cache, v_cache, block_table, seq_lens)
     Hkv = k_cache.shape[1]
-    p = make_params(q, Hkv, top_k, sm_scale, flags)
+    p = make_params(q, Hkv, top_k, sm_scale, flags, top_p)
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     if out is None:
         out = torch.empty_like(q)

@@ -38,7 +38,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, off_spairs_c, off_hlog, total;
+        off_spairs, off_spairs_c, off_hlog, off_nsel, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -50,8 +50,13 @@ gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
     if (p->head_dim != 64 && p->head_dim != 128) return GSA_ERR_BAD_SHAPE;
     if (p->top_k < 0 || p->top_k > kMaxTopK) return GSA_ERR_BAD_SHAPE;
     if (!(p->sm_scale == p->sm_scale) || isinf(p->sm_scale)) return GSA_ERR_BAD_SHAPE;
-    const unsigned known = GSA_SCORE_SUM_PROBS | GSA_SET_SELECTED_GISTS | gsa::kFlagPortable;
+    const unsigned known = GSA_SCORE_SUM_PROBS | GSA_SET_SELECTED_GISTS | GSA_SELECT_TOP_P | gsa::kFlagPortable;
     if (p->flags & ~known) return GSA_ERR_BAD_FLAGS;
+    if (p->flags & GSA_SELECT_TOP_P) {
+        if (p->flags & GSA_SCORE_SUM_PROBS) return GSA_ERR_BAD_FLAGS;  // default key only
+        if (!(p->top_p > 0.0f && p->top_p <= 1.0f)) return GSA_ERR_BAD_SHAPE;
+        if (p->top_k > gsa::kTopPMaxK) return GSA_ERR_BAD_SHAPE;
+    }
     if (kv->chunk_size < 1 || kv->page_chunks < 1 || kv->num_chunks < 0) return GSA_ERR_BAD_SHAPE;
     if (kv->num_pages < 1 || kv->max_pages < 1) return GSA_ERR_BAD_SHAPE;
     long spp = (long)kv->page_chunks * (kv->chunk_size + 1);
@@ -69,7 +74,7 @@ gsa_status_t check_meta(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_me
     if (m->max_meta < kv->num_chunks / m->gists_per_meta) return GSA_ERR_BAD_SHAPE;
     if ((long)p->batch * p->num_kv_heads * (long)m->max_meta > (1L << 40)) return GSA_ERR_BAD_SHAPE;
     if (p->flags & GSA_SET_SELECTED_GISTS) return GSA_ERR_BAD_FLAGS;
-    if (p->flags & GSA_SCORE_SUM_PROBS) return GSA_ERR_BAD_FLAGS;  // flat GSA only
+    if (p->flags & (GSA_SCORE_SUM_PROBS | GSA_SELECT_TOP_P)) return GSA_ERR_BAD_FLAGS;  // flat GSA only
     return GSA_OK;
 }
 
@@ -126,7 +131,7 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         // (the sum-of-probabilities key needs every gist's logits before any key:
         // multi-launch path)
         pl.fused = pl.mfma && units * (pl.hier ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
-                   kmeta <= gsa::kRecMeta && !(p->flags & GSA_SCORE_SUM_PROBS);
+                   kmeta <= gsa::kRecMeta && !(p->flags & (GSA_SCORE_SUM_PROBS | GSA_SELECT_TOP_P));
         a.recs_per_unit = pl.hier ? 2 : 1;
     }
     // H-GSA's meta slices and candidate tasks take half as many rows: its
@@ -174,6 +179,8 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_spairs_c = off; off += align_up(sizeof(uint64_t) * (size_t)units * pl.sc.S3 * gsa::kFusedTA);
     const bool probs = !pl.hier && (p->flags & GSA_SCORE_SUM_PROBS);
     pl.off_hlog = off;  off += align_up(sizeof(float) * (probs ? (size_t)units * a.G * M : 0));
+    const bool topp = !pl.hier && (p->flags & GSA_SELECT_TOP_P);
+    pl.off_nsel = off;  off += align_up(sizeof(int32_t) * (topp ? (size_t)units : 0));
     pl.total = off;
 }
 
@@ -249,6 +256,8 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     a.keys = scores ? scores : (float*)(ws + pl.off_keys);
     a.sel = sel_idx ? sel_idx : (int32_t*)(ws + pl.off_sel);
     a.hlog = (p->flags & GSA_SCORE_SUM_PROBS) ? (float*)(ws + pl.off_hlog) : nullptr;
+    a.top_p = (p->flags & GSA_SELECT_TOP_P) ? p->top_p : 0.f;
+    a.nsel = nullptr;  // set once the top-p counts are written
     a.part_ml = (float2*)(ws + pl.off_ml);
     a.part_acc = (float*)(ws + pl.off_acc);
     a.out = out;
@@ -264,6 +273,10 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     }
     if ((s = run_attn(pl, gsa::kListGists, pl.S1, st)) != GSA_OK) return s;
     GSA_LAUNCH(gsa::launch_select(a, gsa::kSelGists, st));
+    if (p->flags & GSA_SELECT_TOP_P) {
+        a.nsel = (int32_t*)(ws + pl.off_nsel);
+        GSA_LAUNCH(gsa::launch_topp_trim(a, st));
+    }
     if ((s = run_attn(pl, gsa::kListUnfolded, pl.S2, st)) != GSA_OK) return s;
     GSA_LAUNCH(gsa::launch_merge(a, 0, st));
     return GSA_OK;

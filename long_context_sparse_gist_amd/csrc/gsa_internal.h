@@ -10,6 +10,7 @@ namespace gsa {
 
 constexpr unsigned kFlagSumProbs = 0x1u;
 constexpr unsigned kFlagSelectedGists = 0x2u;
+constexpr unsigned kFlagTopP = 0x4u;
 constexpr unsigned kFlagPortable = 0x100u;
 
 // Everything a kernel needs to walk one decode call.  Built once on the host,
@@ -37,6 +38,8 @@ struct Args {
     float* keys;      // [units][key_stride] routing keys
     int key_stride;
     float* hlog;      // [units][G][key_stride] per-head gist logits (sum-of-probabilities key), else null
+    float top_p;      // top-p selection: probability mass to keep
+    int32_t* nsel;    // [units] selected chunks per unit (top-p), else null: min(top_k, n)
     int32_t* sel;     // [units][top_k] selected chunk ids, ascending, -1 padded
     int32_t* sel_meta;   // [units][top_k_meta] (H-GSA)
     float* mkeys;     // [units][max_meta] meta routing keys (H-GSA)
@@ -185,6 +188,8 @@ __device__ inline unsigned* unit_meta(const Args& a, int u) { return unit_rec(a,
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
+hipError_t launch_topp_trim(const Args& a, hipStream_t st);
+constexpr int kTopPMaxK = 2048;  // largest top_k (the cap) with top-p selection
 hipError_t launch_merge(const Args& a, int hier, hipStream_t st);
 hipError_t launch_cand_keys(const Args& a, hipStream_t st);
 

@@ -56,6 +56,7 @@ __device__ inline void make_ctx(const Args& a, int kind, int u, bool hier, ListC
         c.ns = min(a.top_k, nc);
     } else {
         c.ns = min(a.top_k, c.n);
+        if (a.nsel) c.ns = min(c.ns, a.nsel[u]);  // top-p: the unit's own count
     }
     c.e1 = 0;
     if (hier && kind == kListUnfolded) {

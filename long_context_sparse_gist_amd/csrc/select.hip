@@ -64,7 +64,82 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
     }
 }
 
+// Top-p: trims the unit's top-k selection (k = top_k, the cap; ascending ids,
+// -1 padded) to the shortest prefix of key order (largest first, ties to the
+// lower id, NaN last) whose selection probabilities reach top_p, rewrites it
+// ascending and stores its length in nsel.  A chunk's selection probability
+// is the softmax of its key over the sequence's gists (NaN: 0).  The prefix
+// is summed in key order, one entry after another.
+__global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
+    __shared__ uint32_t okey[kTopPMaxK];
+    __shared__ int oid[kTopPMaxK];
+    __shared__ float wr[kTopPMaxK];  // selection weights in key order
+    __shared__ int rk[kTopPMaxK];    // key-order rank of selection entry i
+    __shared__ float red[kThreads / 64];
+    __shared__ int s_need;
+    const int u = blockIdx.x, tid = threadIdx.x;
+    int n, tail;
+    seq_shape(a, u / a.Hkv, n, tail);
+    const int kk = min(a.top_k, n);
+    const float* kw = a.keys + (size_t)u * a.key_stride;
+    int32_t* sel = a.sel + (size_t)u * a.top_k;
+    float m = -INFINITY;
+    for (int i = tid; i < n; i += kThreads)
+        if (!isnan(kw[i])) m = fmaxf(m, kw[i]);
+    m = block_reduce(m, true, red);
+    const bool usable = isfinite(m);
+    float z = 0.f;
+    if (usable)
+        for (int i = tid; i < n; i += kThreads) z += isnan(kw[i]) ? 0.f : expf(kw[i] - m);
+    z = block_reduce(z, false, red);
+    for (int i = tid; i < kk; i += kThreads) {
+        const int id = sel[i];
+        oid[i] = id;
+        okey[i] = order_key(kw[id]);
+    }
+    __syncthreads();
+    for (int i = tid; i < kk; i += kThreads) {
+        int r = 0;
+        for (int j = 0; j < kk; ++j) r += okey[j] > okey[i] || (okey[j] == okey[i] && oid[j] < oid[i]);
+        rk[i] = r;
+        const float key = kw[oid[i]];
+        wr[r] = (usable && !isnan(key)) ? expf(key - m) : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int need = kk;
+        if (usable) {
+            const float target = a.top_p * z;
+            float cum = 0.f;
+            for (int r = 0; r < kk; ++r) {
+                cum += wr[r];
+                if (cum >= target) {
+                    need = r + 1;
+                    break;
+                }
+            }
+        }
+        s_need = need;
+        a.nsel[u] = need;
+    }
+    __syncthreads();
+    const int need = s_need;
+    // keep the entries ranked below `need`, in their (ascending id) order
+    for (int i = tid; i < kk; i += kThreads) {
+        if (rk[i] >= need) continue;
+        int pos = 0;
+        for (int j = 0; j < i; ++j) pos += rk[j] < need;
+        sel[pos] = oid[i];
+    }
+    for (int i = need + tid; i < a.top_k; i += kThreads) sel[i] = -1;
+}
+
 }  // namespace
+
+hipError_t launch_topp_trim(const Args& a, hipStream_t st) {
+    hipLaunchKernelGGL(topp_trim_kernel, dim3(a.B * a.Hkv), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const Args& a, int mode, hipStream_t st) {
     hipLaunchKernelGGL(select_kernel, dim3(a.B * a.Hkv), dim3(kThreads), 0, st, a, mode);

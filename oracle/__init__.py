@@ -18,6 +18,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 SCORE_SUM_PROBS = 0x1
 SET_SELECTED_GISTS = 0x2
+SELECT_TOP_P = 0x4
 
 
 class OracleCfg(ctypes.Structure):
@@ -25,7 +26,8 @@ class OracleCfg(ctypes.Structure):
                 ("batch", "num_q_heads", "num_kv_heads", "head_dim", "top_k")] + [
         ("sm_scale", ctypes.c_float)] + [(n, ctypes.c_int) for n in
         ("dtype", "flags", "num_chunks", "chunk_size", "page_chunks", "num_pages",
-         "max_pages", "gists_per_meta", "top_k_meta", "max_meta")]
+         "max_pages", "gists_per_meta", "top_k_meta", "max_meta")] + [
+        ("top_p", ctypes.c_float)]
 
 
 def build(force: bool = True) -> str:

@@ -19,6 +19,11 @@
  *              float keys, the precision the GPU path decides in.
  *   O2 select  top-k chunks by score (ja page, section 2.1 item 3; nl page,
  *              "Selectie"); ties go to the lower chunk index; NaN keys last.
+ *              With ORACLE_SELECT_TOP_P: the top-p (nucleus) alternative the
+ *              ja page's ablation (section 4) and the nl page's results
+ *              ("Stabiliteit") compare against top-k: the shortest prefix of
+ *              that order whose selection probabilities (softmax of the keys)
+ *              reach top_p, top_k at most.
  *   O3 set     all gist tokens plus the raw tokens of the selected chunks
  *              (ja page, 2.1 items 3-4; nl page, "Selectieve Ontvouwing"),
  *              plus the raw tokens after the last gist (not yet compressed).
@@ -46,6 +51,7 @@
 
 #define ORACLE_SCORE_SUM_PROBS 0x1
 #define ORACLE_SET_SELECTED_GISTS 0x2
+#define ORACLE_SELECT_TOP_P 0x4
 
 typedef struct {
     int batch, num_q_heads, num_kv_heads, head_dim;
@@ -55,6 +61,7 @@ typedef struct {
     int flags;
     int num_chunks, chunk_size, page_chunks, num_pages, max_pages;
     int gists_per_meta, top_k_meta, max_meta; /* H-GSA only */
+    float top_p;        /* with ORACLE_SELECT_TOP_P: probability mass to keep, (0, 1] */
 } oracle_cfg;
 
 /* ---- element access (bf16 -> float widening is exact) ---------------- */
@@ -169,6 +176,39 @@ static int topk(const float *S, const int *ids, int n, int k, int *out) {
     return kk;
 }
 
+/* ---- O2': top-p (nucleus) selection ----------------------------------- */
+
+/* The chunks in key order (largest first, ties to the lower index, NaN last)
+ * up to and including the first at which the running sum of their selection
+ * probabilities reaches p; at most k of them.  A chunk's selection
+ * probability is the softmax of its key over the n candidates (a NaN key:
+ * probability 0).  Without a usable softmax (no finite largest key) the first
+ * min(k, n) are taken.  Writes them ascending to out; returns the count. */
+static int topp(const float *S, const int *ids, int n, int k, double p, int *out) {
+    keyed *v = (keyed *)malloc(sizeof(keyed) * (size_t)(n > 0 ? n : 1));
+    for (int r = 0; r < n; r++) { v[r].s = S[r]; v[r].id = ids[r]; }
+    qsort(v, (size_t)n, sizeof(keyed), cmp_keyed);
+    int kk = k < n ? k : n;
+    double mx = -INFINITY;
+    for (int r = 0; r < n; r++)
+        if (!isnan(v[r].s) && v[r].s > mx) mx = v[r].s;
+    if (isfinite(mx)) {
+        double z = 0.0;
+        for (int r = 0; r < n; r++) z += isnan(v[r].s) ? 0.0 : exp(v[r].s - mx);
+        double cum = 0.0;
+        int need = kk;
+        for (int r = 0; r < kk; r++) {
+            cum += isnan(v[r].s) ? 0.0 : exp(v[r].s - mx);
+            if (cum >= p * z) { need = r + 1; break; }
+        }
+        kk = need;
+    }
+    for (int i = 0; i < kk; i++) out[i] = v[i].id;
+    qsort(out, (size_t)kk, sizeof(int), cmp_int);
+    free(v);
+    return kk;
+}
+
 /* ---- O4: softmax attention of the G heads over a token list ------------ */
 
 typedef struct {
@@ -211,7 +251,11 @@ static int check_cfg(const oracle_cfg *c, int hier) {
     if (c->max_pages < 1 || c->num_pages < 1) return 2;
     if ((long)c->max_pages * c->page_chunks < c->num_chunks) return 2;
     if (c->dtype != 0 && c->dtype != 1) return 3;
-    if (c->flags & ~(ORACLE_SCORE_SUM_PROBS | ORACLE_SET_SELECTED_GISTS)) return 4;
+    if (c->flags & ~(ORACLE_SCORE_SUM_PROBS | ORACLE_SET_SELECTED_GISTS | ORACLE_SELECT_TOP_P)) return 4;
+    if (c->flags & ORACLE_SELECT_TOP_P) {
+        if (hier || (c->flags & ORACLE_SCORE_SUM_PROBS)) return 4;
+        if (!(c->top_p > 0.0f && c->top_p <= 1.0f)) return 2;
+    }
     if (hier) {
         if (c->gists_per_meta < 1 || c->top_k_meta < 0) return 2;
         if (c->max_meta < c->num_chunks / c->gists_per_meta) return 2;
@@ -261,6 +305,8 @@ static void gsa_unit(const oracle_cfg *c, const void *q, const void *kc, const v
         for (int i = 0; i < c->top_k; i++)
             if (ext_sel[i] >= 0 && ext_sel[i] < n) sel[ns++] = ext_sel[i];
         qsort(sel, (size_t)ns, sizeof(int), cmp_int);
+    } else if (c->flags & ORACLE_SELECT_TOP_P) {
+        ns = topp(S, ids, n, c->top_k, (double)c->top_p, sel);
     } else {
         ns = topk(S, ids, n, c->top_k, sel);
     }

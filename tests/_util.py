@@ -24,9 +24,9 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 
 
-def cfg_of(inp, top_k=None, flags=0, sm_scale=0.0, top_k_meta=None) -> dict:
+def cfg_of(inp, top_k=None, flags=0, sm_scale=0.0, top_k_meta=None, top_p=0.0) -> dict:
     wl = inp.wl
-    c = dict(batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+    c = dict(top_p=top_p, batch=wl.batch, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
              head_dim=wl.head_dim, top_k=wl.top_k if top_k is None else top_k,
              sm_scale=sm_scale, dtype=wl.dtype, flags=flags, num_chunks=wl.num_chunks,
              chunk_size=wl.chunk_size, page_chunks=wl.page_chunks, num_pages=inp.num_pages,

@@ -34,7 +34,7 @@ def to(inp, device):
     return gi.GsaInputs(**f)
 
 
-def run_gpu(inp, top_k=None, flags=0, sm_scale=0.0, want_scores=True):
+def run_gpu(inp, top_k=None, flags=0, sm_scale=0.0, want_scores=True, top_p=0.0):
     wl = inp.wl
     k = wl.top_k if top_k is None else top_k
     B, Hkv = wl.batch, wl.num_kv_heads
@@ -45,6 +45,7 @@ def run_gpu(inp, top_k=None, flags=0, sm_scale=0.0, want_scores=True):
     out = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens,
                          num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
                          page_chunks=wl.page_chunks, top_k=k, sm_scale=sm_scale, flags=flags,
+                         top_p=top_p,
                          sel_idx=sel, scores=sc)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), sel.cpu().numpy(),
@@ -152,6 +153,48 @@ def check_gsa(inp, gpu_res, units=None, top_k=None, flags=0, sm_scale=0.0):
                                        ext_sel=sel[b:b + 1, g:g + 1])
         assert_close(out[b, g * G:(g + 1) * G], o_out[0], wl.dtype, f"unit {(b, g)}")
     return differ
+
+
+TOL_P = 1e-4  # top-p: running sums within this of p may fall either way
+
+
+def check_gsa_topp(inp, gpu_res, p, cap, units=None):
+    """Top-p: the GPU's count must be a valid cut of the oracle's running sum
+    of selection probabilities (exactly the oracle's where p is clear of the
+    sums on both sides), its set the top entries by key (gap rule), and the
+    output the oracle's on the GPU's set."""
+    import oracle
+    wl = inp.wl
+    out, sel, sc = gpu_res
+    G = wl.group
+    if units is None:
+        units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    for b, g in units:
+        sub = to(unit_inputs(inp, b, g), "cpu")
+        _, o_sel, o_sc = U.run_oracle(sub, top_k=cap, flags=oracle.SELECT_TOP_P, top_p=p)
+        n = int(sub.seq_lens[0]) // wl.chunk_size
+        kk = min(cap, n)
+        got = [int(x) for x in sel[b, g] if x >= 0]
+        N = len(got)
+        assert np.all(sel[b, g][N:] == -1), f"unit {(b, g)}: -1 padding"
+        keys = o_sc[0, 0, :n].astype(np.float64)
+        if n:
+            order = sorted(range(n), key=lambda i: (-keys[i], i))
+            w = np.exp(keys - keys.max())
+            cum = np.cumsum(w[order] / w.sum())
+            assert 1 <= N <= kk, f"unit {(b, g)}: count {N}"
+            assert N == 1 or cum[N - 2] < p + TOL_P, f"unit {(b, g)}: kept past p"
+            assert cum[N - 1] >= p - TOL_P or N == kk, f"unit {(b, g)}: stopped before p"
+            want = [int(x) for x in o_sel[0, 0] if x >= 0]
+            lo = cum[len(want) - 2] if len(want) >= 2 else 0.0
+            clear = (p - lo > TOL_P) and (cum[len(want) - 1] - p > TOL_P or len(want) == kk)
+            if clear:
+                assert N == len(want), f"unit {(b, g)}: count {N}, oracle {len(want)}"
+            check_set(np.array(got, np.int32), keys, N)
+        else:
+            assert N == 0
+        o_out, _, _ = U.run_oracle(sub, top_k=cap, ext_sel=sel[b:b + 1, g:g + 1])
+        assert_close(out[b, g * G:(g + 1) * G], o_out[0], wl.dtype, f"unit {(b, g)}")
 
 
 def check_hgsa(inp, gpu_res, units=None, top_k=None, top_k_meta=None):

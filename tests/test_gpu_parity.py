@@ -118,6 +118,71 @@ def test_sum_probs_key_full_workload_sampled_units(gpu):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["b3-g4-d64-c8", "b2-g7-d128-c16", "f32-b2-g3-d64"])
+@pytest.mark.parametrize("p", [0.3, 0.9])
+@pytest.mark.parametrize("lens", ["full", "edge"])
+def test_small_top_p(gpu, name, p, lens):
+    wl = SMALL[name]
+    say(f"[parity] {name} top-p {p} lens={lens}")
+    inp = gi.make_inputs(wl, 41, seq_lens=lens_for(wl, lens, 9))
+    res = GU.run_gpu(GU.to(inp, gpu), top_p=p)
+    GU.check_gsa_topp(inp, res, p, wl.top_k)
+
+
+@pytest.mark.parametrize("extra", ["selected-gists", "portable"])
+def test_top_p_combined(gpu, extra):
+    wl = SMALL["b2-g7-d128-c16"]
+    say(f"[parity] top-p + {extra}")
+    inp = gi.make_inputs(wl, 43, seq_lens=lens_for(wl, "ragged", 3))
+    flags = gsa.GSA_SET_SELECTED_GISTS if extra == "selected-gists" else gsa.GSA_PATH_PORTABLE
+    res = GU.run_gpu(GU.to(inp, gpu), top_p=0.8, flags=flags)
+    if extra == "selected-gists":
+        # the set rule changes the output only: the oracle on the GPU's set,
+        # with the same rule (the cut itself is checked by the other cases)
+        out, sel, _ = res
+        for b in range(wl.batch):
+            for g in range(wl.num_kv_heads):
+                sub = GU.to(GU.unit_inputs(inp, b, g), "cpu")
+                o_out, _, _ = GU.U.run_oracle(sub, top_k=wl.top_k, flags=flags,
+                                              ext_sel=sel[b:b + 1, g:g + 1])
+                GU.assert_close(out[b, g * wl.group:(g + 1) * wl.group], o_out[0], wl.dtype,
+                                f"unit {(b, g)}")
+    else:
+        GU.check_gsa_topp(inp, res, 0.8, wl.top_k)
+
+
+def test_top_p_full_workload_sampled_units(gpu):
+    wl = gi.QWEN7B_128K
+    say(f"[parity] full {wl.name} top-p 0.9")
+    inp = gi.make_inputs(wl, gi.seed_of(2), device=gpu)
+    res = GU.run_gpu(inp, top_p=0.9)
+    rng = random.Random(13)
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    GU.check_gsa_topp(inp, res, 0.9, wl.top_k, units=rng.sample(units, 3))
+    del inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("flags,top_p", [(0, 0.0), (0, 1.5), (1, 0.5)])
+def test_top_p_rejected(gpu, flags, top_p):
+    """top-p needs 0 < p <= 1 and the default key; H-GSA does not take it."""
+    wl = SMALL["b3-g4-d64-c8"]
+    inp = GU.to(gi.make_inputs(wl, 3), gpu)
+    p = gsa.make_params(inp.q, wl.num_kv_heads, wl.top_k, 0.0, flags | gsa.GSA_SELECT_TOP_P, 0.0)
+    p.top_p = top_p
+    kv = gsa.make_kv(inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens, wl.num_chunks,
+                     wl.chunk_size, wl.page_chunks)
+    assert gsa.gsa_workspace_size(p, kv) == 0
+    wh = SMALL_H["h-b2-g4-d64-r4"]
+    ih = GU.to(gi.make_inputs(wh, 3), gpu)
+    with pytest.raises(gsa.GsaError):
+        gsa.hgsa_decode(ih.q, ih.k_cache, ih.v_cache, ih.block_table, ih.seq_lens,
+                        ih.k_meta, ih.v_meta, num_chunks=wh.num_chunks,
+                        chunk_size=wh.chunk_size, page_chunks=wh.page_chunks,
+                        gists_per_meta=wh.gists_per_meta, top_k_meta=wh.top_k_meta,
+                        top_k=wh.top_k, flags=gsa.GSA_SELECT_TOP_P)
+
+
 def test_sum_probs_key_rejected_by_hgsa(gpu):
     wl = SMALL_H["h-b2-g4-d64-r4"]
     inp = GU.to(gi.make_inputs(wl, 3), gpu)

@@ -33,7 +33,8 @@ def load_cases(path=GOLDEN):
             elif tok[0] == "cite":
                 cur["cite"] = " ".join(tok[1:])
             elif tok[0] == "config":
-                cur["cfg"] = {k: int(v) for k, v in (t.split("=") for t in tok[1:])}
+                cur["cfg"] = {k: (float(v) if "." in v else int(v))
+                              for k, v in (t.split("=") for t in tok[1:])}
             elif tok[0] == "q":
                 cur["q"] = [float(x) for x in tok[1:]]
             elif tok[0] == "slot":
@@ -87,11 +88,14 @@ def oracle_cfg(case, d):
     if case["meta"]:
         cfg.update(gists_per_meta=c["gists_per_meta"], top_k_meta=c["top_k_meta"],
                    max_meta=c["max_meta"])
+    if "top_p" in c:
+        cfg.update(flags=oracle.SELECT_TOP_P, top_p=c["top_p"])
     return cfg
 
 
 def test_fixture_is_complete():
-    assert set(CASES) == {"gsa-k1", "gsa-k2", "hgsa-k1", "hgsa-k2"}
+    assert set(CASES) == {"gsa-k1", "gsa-k2", "hgsa-k1", "hgsa-k2", "gsa-topp-0.5",
+                          "gsa-topp-0.6", "gsa-topp-0.9", "gsa-topp-cap"}
     for case in CASES.values():
         assert case["cite"] and case["expect_out"] and case["expect_sel"]
 
@@ -101,7 +105,8 @@ def test_oracle_gsa_hand_worked(name):
     case = CASES[name]
     q, k, v, bt, sl, _, _ = arrays(case, 2)
     out, sel, sc = oracle.gsa_decode(oracle_cfg(case, 2), q, k, v, bt, sl)
-    assert sel[0, 0].tolist() == case["expect_sel"]
+    want = case["expect_sel"]
+    assert sel[0, 0].tolist() == want + [-1] * (case["cfg"]["top_k"] - len(want))
     np.testing.assert_allclose(sc[0, 0], case["expect_scores"], rtol=0, atol=1e-6)
     np.testing.assert_allclose(out[0, 0, :2], case["expect_out"], rtol=1e-6, atol=1e-6)
 
@@ -140,10 +145,12 @@ def test_gpu_hand_worked(gpu, name):
         sc = torch.full((1, 1, c["num_chunks"]), 7.0, dtype=torch.float32, device=gpu)
         out = gsa.gsa_decode(q, k, v, bt, sl, num_chunks=c["num_chunks"],
                              chunk_size=c["chunk_size"], page_chunks=c["page_chunks"],
-                             top_k=c["top_k"], sm_scale=1.0, sel_idx=sel, scores=sc)
+                             top_k=c["top_k"], sm_scale=1.0, top_p=c.get("top_p", 0.0),
+                             sel_idx=sel, scores=sc)
         torch.cuda.synchronize()
         np.testing.assert_allclose(sc[0, 0].cpu().numpy(), case["expect_scores"], rtol=0, atol=1e-5)
-    assert sel[0, 0].tolist() == case["expect_sel"]
+    want = case["expect_sel"]
+    assert sel[0, 0].tolist() == want + [-1] * (c["top_k"] - len(want))
     o = out[0, 0].cpu().numpy()
     np.testing.assert_allclose(o[:2], case["expect_out"], rtol=1e-5, atol=1e-4)
     assert np.all(o[2:] == 0.0)

@@ -324,3 +324,55 @@ def test_oracle_rejects_bad_config():
             oracle.gsa_decode(bad, U.np_raw(inp.q), U.np_raw(inp.k_cache),
                               U.np_raw(inp.v_cache), U.np_raw(inp.block_table),
                               U.np_raw(inp.seq_lens))
+
+
+def _np_topp_count(keys, p, cap):
+    """Top-p by brute force in fp64: key order (largest first, ties to the
+    lower index), selection probabilities softmax(keys); the shortest prefix
+    whose running sum reaches p, at most cap long.  Also returns the margin
+    between p and the running sums on either side of the cut."""
+    keys = np.asarray(keys, np.float64)
+    n = len(keys)
+    order = sorted(range(n), key=lambda i: (-keys[i], i))
+    w = np.exp(keys - keys.max())
+    prob = w[order] / w.sum()
+    cum = np.cumsum(prob)
+    kk = min(cap, n)
+    reached = [r for r in range(kk) if cum[r] >= p]
+    if reached:
+        need = reached[0] + 1
+        margin = min(cum[need - 1] - p, p - (cum[need - 2] if need >= 2 else 0.0))
+    else:  # the cap decides
+        need = kk
+        margin = p - cum[kk - 1]
+    return sorted(order[:need]), margin
+
+
+@pytest.mark.parametrize("p", [0.05, 0.3, 0.7, 0.95])
+def test_pj_top_p_matches_brute_force(p):
+    """P-j: top-p selection against fp64 brute force on the oracle's own keys
+    (planted chunks make the probability mass uneven)."""
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 31, seq_lens=ragged(wl, 5))
+    cap = wl.top_k
+    _, sel, sc = U.run_oracle(inp, flags=oracle.SELECT_TOP_P, top_p=p)
+    n, _ = U.shapes(inp)
+    checked = 0
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            want, margin = _np_topp_count(sc[b, g, :n[b]], p, cap)
+            got = [int(x) for x in sel[b, g] if x >= 0]
+            if margin > 1e-6:
+                assert got == want, (b, g, p)
+                checked += 1
+            assert all(x == -1 for x in sel[b, g][len(got):])
+    assert checked > 0
+
+
+def test_pj_top_p_full_mass_is_top_k():
+    """p = 1 with a cap below the gist count: the cap decides, as top-k."""
+    wl = SMALL_BF16
+    inp = gi.make_inputs(wl, 32)
+    _, a, _ = U.run_oracle(inp)
+    _, b_, _ = U.run_oracle(inp, flags=oracle.SELECT_TOP_P, top_p=1.0)
+    assert np.array_equal(a, b_)
