@@ -23,27 +23,71 @@ __device__ inline float block_reduce(float x, bool is_max, float* red) {
     return x;
 }
 
+// Block-wide max / sum of 16 values per thread at once (every thread gets the
+// results).  red: [kThreads / 64][16].
+__device__ inline void block_reduce16(float (&x)[16], bool is_max, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(x[h], o);
+            x[h] = is_max ? fmaxf(x[h], y) : x[h] + y;
+        }
+    __syncthreads();  // the previous use of red is over
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h == lane) red[16 * w + h] = x[h];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        float v = red[h];
+        for (int i = 1; i < kThreads / 64; ++i) v = is_max ? fmaxf(v, red[16 * i + h]) : v + red[16 * i + h];
+        x[h] = v;
+    }
+}
+
 // Sum-of-probabilities routing key of the unit's n gists: for each head of the
 // group, the softmax of its logits over the gists; the key of a gist is the sum
-// of its probabilities over the heads.  Overwrites the sum-of-logits keys.
+// of its probabilities over the heads.  Overwrites the sum-of-logits keys.  All
+// heads go through each pass together, so a thread's loads of one gist are in
+// flight at once.
 __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* red) {
-    for (int h = 0; h < a.G; ++h) {
-        const float* z = a.hlog + ((size_t)u * a.G + h) * a.key_stride;
-        float m = -INFINITY;
-        for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, z[i]);
-        m = block_reduce(m, true, red);
-        float l = 0.f;
-        for (int i = threadIdx.x; i < n; i += kThreads) l += expf(z[i] - m);
-        l = block_reduce(l, false, red);
-        // each thread updates only the entries it owns: no barrier between heads
-        for (int i = threadIdx.x; i < n; i += kThreads) kw[i] = (h ? kw[i] : 0.f) + expf(z[i] - m) / l;
+    const int G = a.G;  // <= 16
+    const size_t hs = a.key_stride;
+    const float* z = a.hlog + (size_t)u * G * hs;
+    float m[16], l[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+    }
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
+    }
+    block_reduce16(m, true, red);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
+    }
+    block_reduce16(l, false, red);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        float key = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) key += expf(z[h * hs + i] - m[h]) / l[h];
+        kw[i] = key;
     }
     __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
     __shared__ SelectSmem<kThreads> sh;
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[16 * (kThreads / 64)];
     const int u = blockIdx.x;
     ListCtx c;
     make_ctx(a, mode == kSelCand ? kListCand : kListGists, u, mode != kSelGists, c);
