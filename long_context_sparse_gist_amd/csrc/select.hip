@@ -63,18 +63,21 @@ __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* re
         m[h] = -INFINITY;
         l[h] = 0.f;
     }
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kThreads) {
 #pragma unroll
         for (int h = 0; h < 16; ++h)
             if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
     }
     block_reduce16(m, true, red);
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kThreads) {
 #pragma unroll
         for (int h = 0; h < 16; ++h)
             if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
     }
     block_reduce16(l, false, red);
+#pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kThreads) {
         float key = 0.f;
 #pragma unroll
