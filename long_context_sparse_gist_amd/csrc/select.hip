@@ -51,8 +51,10 @@ __device__ inline void block_reduce16(float (&x)[16], bool is_max, float* red) {
 // Sum-of-probabilities routing key of the unit's n gists: for each head of the
 // group, the softmax of its logits over the gists; the key of a gist is the sum
 // of its probabilities over the heads.  Overwrites the sum-of-logits keys.  All
-// heads go through each pass together, so a thread's loads of one gist are in
-// flight at once.
+// heads go through each pass together and four gists per thread are unrolled,
+// so a pass takes a few load round trips (one workgroup per unit).  With the
+// all-gists set, each head's maximum and normaliser come from the gist
+// attention partials, and one pass over the logits remains.
 __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* red) {
     const int G = a.G;  // <= 16
     const size_t hs = a.key_stride;
@@ -63,20 +65,41 @@ __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* re
         m[h] = -INFINITY;
         l[h] = 0.f;
     }
-#pragma unroll 4
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+    if (!(a.flags & kFlagSelectedGists)) {
+        // the gist attention partials already hold each head's softmax maximum
+        // and normaliser over every split of the gists (base-2 domain): fold them
+        const int ns = (n + a.SL - 1) / a.SL;
+        const float2* ml = a.part_ml + (size_t)u * a.NS * G;
+        for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
 #pragma unroll
-        for (int h = 0; h < 16; ++h)
-            if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
-    }
-    block_reduce16(m, true, red);
-#pragma unroll 4
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+            for (int h = 0; h < 16; ++h)
+                if (h < G) m[h] = fmaxf(m[h], ml[(size_t)sp * G + h].x);
+        }
+        block_reduce16(m, true, red);
+        for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
 #pragma unroll
-        for (int h = 0; h < 16; ++h)
-            if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
+            for (int h = 0; h < 16; ++h)
+                if (h < G) l[h] += ml[(size_t)sp * G + h].y * exp2f(ml[(size_t)sp * G + h].x - m[h]);
+        }
+        block_reduce16(l, false, red);
+#pragma unroll
+        for (int h = 0; h < 16; ++h) m[h] *= 0.69314718055994531f;  // to the natural-log domain
+    } else {
+#pragma unroll 4
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+#pragma unroll
+            for (int h = 0; h < 16; ++h)
+                if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
+        }
+        block_reduce16(m, true, red);
+#pragma unroll 4
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+#pragma unroll
+            for (int h = 0; h < 16; ++h)
+                if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
+        }
+        block_reduce16(l, false, red);
     }
-    block_reduce16(l, false, red);
 #pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kThreads) {
         float key = 0.f;
