@@ -272,6 +272,8 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
         return GSA_OK;
     }
     if ((s = run_attn(pl, gsa::kListGists, pl.S1, st)) != GSA_OK) return s;
+    if ((p->flags & GSA_SCORE_SUM_PROBS) && !(p->flags & GSA_SET_SELECTED_GISTS) && pl.S1 > 0)
+        GSA_LAUNCH(gsa::launch_probs_keys(a, st));  // (the selected-gists set: in the select)
     GSA_LAUNCH(gsa::launch_select(a, gsa::kSelGists, st));
     if (p->flags & GSA_SELECT_TOP_P) {
         a.nsel = (int32_t*)(ws + pl.off_nsel);

@@ -189,6 +189,7 @@ __device__ inline unsigned* unit_meta(const Args& a, int u) { return unit_rec(a,
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
 hipError_t launch_topp_trim(const Args& a, hipStream_t st);
+hipError_t launch_probs_keys(const Args& a, hipStream_t st);
 constexpr int kTopPMaxK = 2048;  // largest top_k (the cap) with top-p selection
 hipError_t launch_merge(const Args& a, int hier, hipStream_t st);
 hipError_t launch_cand_keys(const Args& a, hipStream_t st);

@@ -7,6 +7,7 @@ namespace gsa {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kKeyParts = 8;  // workgroups per unit making sum-of-probabilities keys
 
 // Block-wide max / sum of one value per thread (every thread gets the result).
 __device__ inline float block_reduce(float x, bool is_max, float* red) {
@@ -52,9 +53,8 @@ __device__ inline void block_reduce16(float (&x)[16], bool is_max, float* red) {
 // group, the softmax of its logits over the gists; the key of a gist is the sum
 // of its probabilities over the heads.  Overwrites the sum-of-logits keys.  All
 // heads go through each pass together and four gists per thread are unrolled,
-// so a pass takes a few load round trips (one workgroup per unit).  With the
-// all-gists set, each head's maximum and normaliser come from the gist
-// attention partials, and one pass over the logits remains.
+// so a pass takes a few load round trips.  Used with the selected-gists set
+// (no gist attention partials); otherwise probs_keys_kernel makes the keys.
 __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* red) {
     const int G = a.G;  // <= 16
     const size_t hs = a.key_stride;
@@ -65,41 +65,20 @@ __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* re
         m[h] = -INFINITY;
         l[h] = 0.f;
     }
-    if (!(a.flags & kFlagSelectedGists)) {
-        // the gist attention partials already hold each head's softmax maximum
-        // and normaliser over every split of the gists (base-2 domain): fold them
-        const int ns = (n + a.SL - 1) / a.SL;
-        const float2* ml = a.part_ml + (size_t)u * a.NS * G;
-        for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (h < G) m[h] = fmaxf(m[h], ml[(size_t)sp * G + h].x);
-        }
-        block_reduce16(m, true, red);
-        for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (h < G) l[h] += ml[(size_t)sp * G + h].y * exp2f(ml[(size_t)sp * G + h].x - m[h]);
-        }
-        block_reduce16(l, false, red);
-#pragma unroll
-        for (int h = 0; h < 16; ++h) m[h] *= 0.69314718055994531f;  // to the natural-log domain
-    } else {
 #pragma unroll 4
-        for (int i = threadIdx.x; i < n; i += kThreads) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
 #pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
-        }
-        block_reduce16(m, true, red);
-#pragma unroll 4
-        for (int i = threadIdx.x; i < n; i += kThreads) {
-#pragma unroll
-            for (int h = 0; h < 16; ++h)
-                if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
-        }
-        block_reduce16(l, false, red);
+        for (int h = 0; h < 16; ++h)
+            if (h < G) m[h] = fmaxf(m[h], z[h * hs + i]);
     }
+    block_reduce16(m, true, red);
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) l[h] += expf(z[h * hs + i] - m[h]);
+    }
+    block_reduce16(l, false, red);
 #pragma unroll 4
     for (int i = threadIdx.x; i < n; i += kThreads) {
         float key = 0.f;
@@ -111,6 +90,52 @@ __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* re
     __syncthreads();
 }
 
+// Sum-of-probabilities keys with the all-gists set (grid: kKeyParts x units):
+// each workgroup folds its unit's gist attention partials into every head's
+// softmax maximum and normaliser (base-2 domain) and writes the keys of its
+// part of the gists.  A few parts per unit: the fold is repeated per part.
+__global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
+    __shared__ float red[16 * (kThreads / 64)];
+    const int u = blockIdx.y;
+    int n, tail;
+    seq_shape(a, u / a.Hkv, n, tail);
+    const int per = (n + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int p0 = blockIdx.x * per;
+    if (p0 >= n) return;  // block-uniform
+    const int G = a.G;    // <= 16
+    const int ns = (n + a.SL - 1) / a.SL;
+    const float2* ml = a.part_ml + (size_t)u * a.NS * G;
+    float m[16], l[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+    }
+    for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) m[h] = fmaxf(m[h], ml[(size_t)sp * G + h].x);
+    }
+    block_reduce16(m, true, red);
+    for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) l[h] += ml[(size_t)sp * G + h].y * exp2f(ml[(size_t)sp * G + h].x - m[h]);
+    }
+    block_reduce16(l, false, red);
+    const size_t hs = a.key_stride;
+    const float* z = a.hlog + (size_t)u * G * hs;
+    float* kw = a.keys + (size_t)u * hs;
+    const int end = min(n, p0 + per);
+    for (int i = p0 + threadIdx.x; i < end; i += kThreads) {
+        float key = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) key += exp2f(z[h * hs + i] * 1.4426950408889634f - m[h]) / l[h];
+        kw[i] = key;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
     __shared__ SelectSmem<kThreads> sh;
     __shared__ float red[16 * (kThreads / 64)];
@@ -120,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
     if (mode == kSelGists) {
         // scores past the sequence's gists read -inf
         float* kw = a.keys + (size_t)u * a.key_stride;
-        if (a.hlog) sum_probs_keys(a, u, c.n, kw, red);
+        if (a.hlog && (a.flags & kFlagSelectedGists)) sum_probs_keys(a, u, c.n, kw, red);  // (else done by probs_keys_kernel)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) kw[i] = -INFINITY;
         block_topk<kThreads>(a.keys + (size_t)u * a.key_stride, nullptr, c.n, a.top_k,
                              a.sel + (size_t)u * a.top_k, false, sh);
@@ -205,6 +230,11 @@ __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
 }
 
 }  // namespace
+
+hipError_t launch_probs_keys(const Args& a, hipStream_t st) {
+    hipLaunchKernelGGL(probs_keys_kernel, dim3(kKeyParts, a.B * a.Hkv), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_topp_trim(const Args& a, hipStream_t st) {
     hipLaunchKernelGGL(topp_trim_kernel, dim3(a.B * a.Hkv), dim3(kThreads), 0, st, a);
