@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
 // lower id, NaN last) whose selection probabilities reach top_p, rewrites it
 // ascending and stores its length in nsel.  A chunk's selection probability
 // is the softmax of its key over the sequence's gists (NaN: 0).  The prefix
-// is summed in key order, one entry after another.
+// is summed in key order (chunks of ranks per lane, then a prefix over lanes).
 __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
     __shared__ uint32_t okey[kTopPMaxK];
     __shared__ int oid[kTopPMaxK];
@@ -179,13 +179,16 @@ __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
     const float* kw = a.keys + (size_t)u * a.key_stride;
     int32_t* sel = a.sel + (size_t)u * a.top_k;
     float m = -INFINITY;
+#pragma unroll 4
     for (int i = tid; i < n; i += kThreads)
         if (!isnan(kw[i])) m = fmaxf(m, kw[i]);
     m = block_reduce(m, true, red);
     const bool usable = isfinite(m);
     float z = 0.f;
-    if (usable)
+    if (usable) {
+#pragma unroll 4
         for (int i = tid; i < n; i += kThreads) z += isnan(kw[i]) ? 0.f : expf(kw[i] - m);
+    }
     z = block_reduce(z, false, red);
     for (int i = tid; i < kk; i += kThreads) {
         const int id = sel[i];
@@ -201,21 +204,38 @@ __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
         wr[r] = (usable && !isnan(key)) ? expf(key - m) : 0.f;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < 64) {
+        // wavefront 0: lane l sums ranks [l*per, (l+1)*per), a prefix over the
+        // lanes finds the chunk where the running sum reaches the target, and
+        // that lane walks its chunk to the cut
+        const int per = (kk + 63) / 64, b0 = tid * per, e0 = min(kk, b0 + per);
+        float cs = 0.f;
+        for (int r = b0; r < e0; ++r) cs += wr[r];
+        float incl = cs;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(incl, o);
+            if (tid >= o) incl += y;
+        }
+        const float target = a.top_p * z;
+        const uint64_t hit = __ballot(usable && b0 < e0 && incl >= target);
         int need = kk;
-        if (usable) {
-            const float target = a.top_p * z;
-            float cum = 0.f;
-            for (int r = 0; r < kk; ++r) {
+        if (hit) {
+            const int lc = __ffsll((unsigned long long)hit) - 1;
+            int nl = e0;  // (rounding: the chunk's end if the walk falls short)
+            float cum = incl - cs;
+            for (int r = b0; r < e0; ++r) {
                 cum += wr[r];
                 if (cum >= target) {
-                    need = r + 1;
+                    nl = r + 1;
                     break;
                 }
             }
+            need = __shfl(nl, lc);
         }
-        s_need = need;
-        a.nsel[u] = need;
+        if (tid == 0) {
+            s_need = need;
+            a.nsel[u] = need;
+        }
     }
     __syncthreads();
     const int need = s_need;
