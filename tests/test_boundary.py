@@ -94,6 +94,10 @@ BAD_PARAMS = [
     (dict(num_q_heads=7), 2), (dict(num_q_heads=34), 2), (dict(head_dim=96), 2),
     (dict(top_k=-1), 2), (dict(sm_scale=float("nan")), 2), (dict(sm_scale=float("inf")), 2),
     (dict(dtype=2), 3), (dict(flags=0x40), 4),
+    # top-p: 0 < top_p <= 1, the default key only, a cap of at most 2048
+    (dict(flags=0x4, top_p=0.0), 2), (dict(flags=0x4, top_p=1.5), 2),
+    (dict(flags=0x4, top_p=float("nan")), 2), (dict(flags=0x5, top_p=0.5), 4),
+    (dict(flags=0x4, top_p=0.5, top_k=4096), 2),
 ]
 BAD_KV = [
     (dict(chunk_size=0), 2), (dict(page_chunks=0), 2), (dict(num_chunks=-1), 2),
@@ -153,6 +157,8 @@ def test_hgsa_validation(lib):
     assert call_h(lib, p, kv, meta(top_k_meta=-1)) == 2
     assert call_h(lib, p, kv, meta(max_meta=3)) == 2
     assert call_h(lib, params(flags=gsa.GSA_SET_SELECTED_GISTS), kv, meta()) == 4
+    assert call_h(lib, params(flags=gsa.GSA_SCORE_SUM_PROBS), kv, meta()) == 4  # flat GSA only
+    assert call_h(lib, params(flags=gsa.GSA_SELECT_TOP_P, top_p=0.5), kv, meta()) == 4
     assert call_h(lib, params(head_dim=32), kv, meta()) == 2
     need = lib.hgsa_workspace_size(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(meta()))
     assert call_h(lib, p, kv, meta(), ws_bytes=need - 1) == 5
@@ -182,3 +188,28 @@ def test_control_block_size_matches_header():
 def test_workspace_covers_control_block(lib):
     p, kv = params(), kvs()
     assert lib.gsa_workspace_size(ctypes.byref(p), ctypes.byref(kv)) > gsa.WORKSPACE_CONTROL_BYTES
+
+
+def test_params_layout_matches_header(tmp_path):
+    """The binding's gsa_params_t / gsa_kv_t / hgsa_meta_t match the header's
+    layout (sizes and field offsets, from a C program built with gcc)."""
+    structs = {"gsa_params_t": gsa.GsaParams, "gsa_kv_t": gsa.GsaKV, "hgsa_meta_t": gsa.HgsaMeta}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gsa.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'    printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'    printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n"):
+        if ln:
+            cname, what, val = ln.split()
+            got[(cname, what)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
