@@ -35,7 +35,11 @@
  *              Uitbreiding"): score meta-gists, keep top-k1, score the gists of
  *              the kept groups, keep top-k2, unfold their raw tokens; attend to
  *              all meta-gists, the kept gists and their raw tokens.
- *   O6         O3-O5 with the selection supplied by the caller.
+ *   O6         O3-O5 with the selection supplied by the caller: its ids that
+ *              lie in the sequence (chunk ids in [0, n), meta-group ids in
+ *              [0, n/R)) in place of the top-k at that level, in any order;
+ *              -1 and other ids are ignored.  H-GSA's candidates follow the
+ *              caller's meta-groups.
  *
  * Parity pins (tests/test_oracle_*.py) check this file against numpy fp64
  * brute force, closed forms and invariants; see the tests for which pin

@@ -46,6 +46,11 @@ MUTANTS = {
     "candidates_wrong_group": ("cids[nc++] = sel1[i] * R + j;", "cids[nc++] = sel1[i] + j * nm;"),
     "tail_gists_not_candidates": ("for (int m = nm * R; m < n; m++) cids[nc++] = m;",
                                   "for (int m = nm * R; m < nm * R; m++) cids[nc++] = m;"),
+    "ext_sel_ignored": ("    if (ext_sel) {\n        ns = 0;", "    if (0) {\n        ns = 0;"),
+    "ext_sel_range_unchecked": ("if (ext_sel[i] >= 0 && ext_sel[i] < n) sel[ns++]",
+                                "if (ext_sel[i] >= 0 && ext_sel[i] < c->num_chunks) sel[ns++]"),
+    "ext1_ignored": ("    if (ext1) {", "    if (0) {"),
+    "ext2_ignored": ("    if (ext2) {", "    if (0) {"),
     "meta_gists_not_attended": ("for (int r = 0; r < nm; r++) { T[nT].arr_k = km;",
                                 "for (int r = 0; r < 0; r++) { T[nT].arr_k = km;"),
 }
@@ -69,6 +74,10 @@ def pin_battery():
             ("h_full", lambda: P.test_hgsa_matches_brute_force("full")),
             ("h_ragged", lambda: P.test_hgsa_matches_brute_force("ragged")),
             ("sum_probs", P.test_sum_of_probs_keys)]
+    for fl in (0, oracle.SET_SELECTED_GISTS):
+        out.append((f"o6_flat/{fl}", lambda fl=fl: P.test_o6_external_selection_flat(fl)))
+    for which in ("meta", "gist", "both"):
+        out.append((f"o6_h/{which}", lambda which=which: P.test_o6_external_selection_hgsa(which)))
     for wl in (P.SMALL_BF16, P.SMALL_F32):
         out.append((f"pi/{wl.name}", lambda wl=wl: P.test_pi_convex_hull(wl)))
     return out

@@ -226,8 +226,10 @@ def test_pa_hierarchy_all_kept_is_dense_over_meta_and_sequence():
                                rtol=1e-10, atol=1e-12)
 
 
-def _np_hgsa(inp, k1, k2):
-    """Two-level selection and attention, numpy brute force."""
+def _np_hgsa(inp, k1, k2, ext1=None, ext2=None):
+    """Two-level selection and attention, numpy brute force.  ext1 / ext2:
+    caller selections ([B][Hkv][k1] / [B][Hkv][k2], entries outside the
+    sequence's meta-groups / gists ignored) replacing the top-k at that level."""
     wl = inp.wl
     R, C, G = wl.gists_per_meta, wl.chunk_size, wl.group
     tau = U.tau_of(wl.head_dim)
@@ -243,10 +245,14 @@ def _np_hgsa(inp, k1, k2):
             qg = q[b, g * G:(g + 1) * G]
             SM = (tau * km[b, g, :nm] @ qg.T).sum(1).astype(np.float32)
             s1 = U.np_topk(SM, k1)
+            if ext1 is not None:
+                s1 = np.array(sorted(int(r) for r in ext1[b][g] if 0 <= r < nm), np.int64)
             cand = np.concatenate([np.arange(r * R, r * R + R) for r in s1] +
                                   [np.arange(nm * R, n[b])]).astype(np.int64)
             SC = (tau * K[b, g, cand * (C + 1) + C] @ qg.T).sum(1).astype(np.float32)
             s2 = U.np_topk(SC, k2, ids=cand)
+            if ext2 is not None:
+                s2 = np.array(sorted(int(m) for m in ext2[b][g] if 0 <= m < n[b]), np.int64)
             m = U.gsa_mask(n[b], tail[b], C, s2, K.shape[2], all_gists=False)
             m[np.arange(nm * R, n[b]) * (C + 1) + C] = True
             Kall = np.concatenate([km[b, g, :nm], K[b, g][m]])
@@ -376,3 +382,96 @@ def test_pj_top_p_full_mass_is_top_k():
     _, a, _ = U.run_oracle(inp)
     _, b_, _ = U.run_oracle(inp, flags=oracle.SELECT_TOP_P, top_p=1.0)
     assert np.array_equal(a, b_)
+
+
+# ---------------- O6: the caller's selection ----------------
+# The gap rule of the GPU parity tests reruns the oracle with the GPU's set
+# whenever the two selections differ, so O6 must follow the caller's set and
+# nothing else: checked here with sets that are far from the top-k (the
+# lowest keys), padded with -1, holding ids past the sequence, unordered.
+
+def _bottom_sets(keys_by_unit, counts, k, rng, pad_bad=True):
+    """Per unit: the lowest-key ids (as far from the top-k as possible),
+    shuffled, with -1 padding and ids outside [0, count) mixed in."""
+    out = []
+    for row, crow in zip(keys_by_unit, counts):
+        rr = []
+        for S, n in zip(row, crow):
+            low = [int(i) for i in np.argsort(S, kind="stable")[:max(0, min(k - 2, n))]]
+            extra = [-1, n + 2] if pad_bad else []
+            ids = (low + extra + [-1] * k)[:k]
+            rng.shuffle(ids)
+            rr.append(ids)
+        out.append(rr)
+    return np.array(out, np.int32)
+
+
+@pytest.mark.parametrize("flags", [0, oracle.SET_SELECTED_GISTS])
+def test_o6_external_selection_flat(flags):
+    """O6 (flat): the set is the caller's ids that lie in [0, n), whatever
+    their keys or order; the output is masked dense attention over it."""
+    wl = SMALL_BF16.replace(top_k=6)
+    lens = ragged(wl, 14)
+    inp = gi.make_inputs(wl, 61, seq_lens=lens)
+    _, own, sc = U.run_oracle(inp, flags=flags)
+    n, _ = U.shapes(inp)
+    keys = [[sc[b, g, :n[b]] for g in range(wl.num_kv_heads)] for b in range(wl.batch)]
+    counts = [[int(n[b])] * wl.num_kv_heads for b in range(wl.batch)]
+    ext = _bottom_sets(keys, counts, wl.top_k, np.random.default_rng(3))
+    # an id past this sequence but inside the cache capacity (ragged rows)
+    for b in range(wl.batch):
+        if n[b] < wl.num_chunks:
+            ext[b, 0, -1] = n[b]
+    out, sel, _ = U.run_oracle(inp, ext_sel=ext, flags=flags)
+    want = [[sorted(int(m) for m in ext[b, g] if 0 <= m < n[b]) for g in range(wl.num_kv_heads)]
+            for b in range(wl.batch)]
+    differs = 0
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            got = [int(x) for x in sel[b, g] if x >= 0]
+            assert got == want[b][g]
+            differs += got != [int(x) for x in own[b, g] if x >= 0]
+    assert differs == wl.batch * wl.num_kv_heads  # every unit away from its top-k
+    ref = U.np_gsa_out(inp, want, all_gists=not flags)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+    # an empty caller set: gists (and raw tail) only
+    empty = np.full_like(ext, -1)
+    out0, _, _ = U.run_oracle(inp, ext_sel=empty, flags=flags)
+    none = [[[] for _ in range(wl.num_kv_heads)] for _ in range(wl.batch)]
+    assert np.allclose(out0, U.np_gsa_out(inp, none, all_gists=not flags), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["meta", "gist", "both"])
+def test_o6_external_selection_hgsa(which):
+    """O6 (H-GSA): a caller's meta-group set replaces the meta top-k (the
+    candidates follow it), a caller's gist set replaces the gist top-k (any
+    gist of the sequence), or both."""
+    wl = SMALL_H
+    inp = gi.make_inputs(wl, 67, seq_lens=[230, 170])
+    _, o1, o2, ms, gs = U.run_oracle_h(inp)
+    n, _ = U.shapes(inp)
+    R = wl.gists_per_meta
+    rng = np.random.default_rng(5)
+    e1 = e2 = None
+    if which in ("meta", "both"):
+        keys = [[ms[b, g, :n[b] // R] for g in range(wl.num_kv_heads)] for b in range(wl.batch)]
+        counts = [[int(n[b] // R)] * wl.num_kv_heads for b in range(wl.batch)]
+        e1 = _bottom_sets(keys, counts, wl.top_k_meta, rng)
+    if which in ("gist", "both"):
+        keys = [[gs[b, g, :n[b]] for g in range(wl.num_kv_heads)] for b in range(wl.batch)]
+        counts = [[int(n[b])] * wl.num_kv_heads for b in range(wl.batch)]
+        e2 = _bottom_sets(keys, counts, wl.top_k, rng)
+    out, s1, s2, _, _ = U.run_oracle_h(inp, ext_sel_meta=e1, ext_sel=e2)
+    ref, sels = _np_hgsa(inp, wl.top_k_meta, wl.top_k, ext1=e1, ext2=e2)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+    i = 0
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            a1, a2 = sels[i]
+            i += 1
+            assert np.array_equal(s1[b, g][s1[b, g] >= 0], a1)
+            assert np.array_equal(s2[b, g][s2[b, g] >= 0], a2)
+            if e1 is not None and len(a1):
+                assert not np.array_equal(a1, o1[b, g][o1[b, g] >= 0])
+            if e2 is not None and len(a2):
+                assert not np.array_equal(a2, o2[b, g][o2[b, g] >= 0])
