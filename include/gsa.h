@@ -51,8 +51,10 @@ typedef enum {
     GSA_ERR_BAD_DTYPE = 3,  /* dtype not GSA_F32 / GSA_BF16 */
     GSA_ERR_BAD_FLAGS = 4,  /* unknown or unsupported flag bits */
     GSA_ERR_WORKSPACE = 5,  /* workspace NULL, too small or misaligned */
-    GSA_ERR_DEVICE = 6,     /* no usable HIP device / not a gfx950 device */
-    GSA_ERR_LAUNCH = 7      /* a kernel launch failed */
+    GSA_ERR_DEVICE = 6,     /* no usable HIP device / the current device is not gfx950 */
+    GSA_ERR_LAUNCH = 7,     /* a kernel launch failed */
+    GSA_ERR_WAIT = 8        /* gsa_workspace_status: a bounded wait inside the
+                               single-launch kernel gave up (see below) */
 } gsa_status_t;
 
 typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype_t;
@@ -141,6 +143,15 @@ typedef struct {
 /* Size of the control block at the start of every workspace: an error word
  * and the per-(batch, kv-head) counters of the single-launch path. */
 #define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 25088)
+/* Byte offset (in the control block) of the 32-bit error word.  The
+ * single-launch kernel's workgroups hand data to each other through the
+ * control block and wait for it with bounded polls; a wait that gives up
+ * (never expected: it would take a device that stops dispatching queued
+ * workgroups) sets this word to 1 and the kernel finishes with partial data.
+ * The call's outputs are then unreliable and the control block may be left
+ * non-zero.  gsa_workspace_status reads the word; gsa_workspace_reset clears
+ * the control block again, after which the workspace is usable. */
+#define GSA_WORKSPACE_ERROR_OFFSET ((size_t)8)
 
 /* Bytes of device workspace gsa_decode needs for these shapes (0 if the
  * shapes are invalid).  The workspace must be 256-byte aligned and its first
@@ -180,6 +191,19 @@ gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv,
                          const hgsa_meta_t* meta, const void* q, void* out,
                          int32_t* sel_meta, int32_t* sel_idx, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Waits for `stream` (a hipStream_t, NULL: the null stream), then reads the
+ * error word of `workspace`: GSA_OK if it is zero, GSA_ERR_WAIT if a wait of
+ * some call since the last reset gave up.  GSA_ERR_NULL_ARG / GSA_ERR_WORKSPACE
+ * for a NULL, misaligned or too-small (< GSA_WORKSPACE_CONTROL_BYTES)
+ * workspace; GSA_ERR_DEVICE if the wait or the read fails. */
+gsa_status_t gsa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Enqueues on `stream` the zeroing of the control block of `workspace` (a
+ * fill kernel, so the call can be captured in a HIP graph): the recovery step
+ * after GSA_ERR_WAIT, or the first-use preparation of a fresh workspace.
+ * Must not overlap a decode call that uses the same workspace. */
+gsa_status_t gsa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status_t s);

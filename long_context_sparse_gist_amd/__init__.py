@@ -6,7 +6,14 @@ is loaded on first use and a missing or unloadable library raises; there is no
 fallback path.
 
 Names mirror the C ABI in include/gsa.h: gsa_decode, hgsa_decode,
-gsa_workspace_size, hgsa_workspace_size, gsa_status_string, gsa_version.
+gsa_workspace_size, hgsa_workspace_size, gsa_workspace_status,
+gsa_workspace_reset, gsa_status_string, gsa_version.
+
+Streams: a call runs on `stream` (default: the current stream of q's
+device).  The output and the cached workspace are allocated, and the
+workspace zero-filled, on that stream, and the workspace cache is kept per
+(device, stream), so calls on different streams never share a control block
+and every allocation is ordered before the kernels that use it.
 """
 from __future__ import annotations
 
@@ -29,10 +36,12 @@ GSA_SELECT_TOP_P = 0x4
 GSA_PATH_PORTABLE = 0x100
 # bytes at the start of every workspace that must be zero between calls
 WORKSPACE_CONTROL_BYTES = 16384 + 512 * 25088
+# byte offset of the control block's error word (nonzero: a wait gave up)
+WORKSPACE_ERROR_OFFSET = 8
 
 STATUS = {0: "GSA_OK", 1: "GSA_ERR_NULL_ARG", 2: "GSA_ERR_BAD_SHAPE", 3: "GSA_ERR_BAD_DTYPE",
           4: "GSA_ERR_BAD_FLAGS", 5: "GSA_ERR_WORKSPACE", 6: "GSA_ERR_DEVICE",
-          7: "GSA_ERR_LAUNCH"}
+          7: "GSA_ERR_LAUNCH", 8: "GSA_ERR_WAIT"}
 
 
 class GsaParams(ctypes.Structure):
@@ -85,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.hgsa_decode.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
                                   ctypes.POINTER(HgsaMeta), P, P, P, P, P, ctypes.c_size_t, P]
         L.hgsa_decode.restype = ctypes.c_int
+        L.gsa_workspace_status.argtypes = [P, ctypes.c_size_t, P]
+        L.gsa_workspace_status.restype = ctypes.c_int
+        L.gsa_workspace_reset.argtypes = [P, ctypes.c_size_t, P]
+        L.gsa_workspace_reset.restype = ctypes.c_int
         L.gsa_status_string.argtypes = [ctypes.c_int]
         L.gsa_status_string.restype = ctypes.c_char_p
         L.gsa_version.restype = ctypes.c_int
@@ -144,16 +157,46 @@ def hgsa_workspace_size(params: GsaParams, kv: GsaKV, meta: HgsaMeta) -> int:
 _ws_cache: dict = {}
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes on `device`, reused across
-    calls (calls on one device must not overlap when they share it)."""
+def _stream_of(stream, device) -> "torch.cuda.Stream":
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes on `device` for calls on
+    `stream` (default: the device's current stream), reused across calls on
+    that stream.  It is allocated and zero-filled on that stream, so the fill
+    is ordered before the calls; a replaced one returns to the allocator's
+    pool for that stream, whose later users are ordered after the calls that
+    used it."""
     dev = torch.device(device)
-    key = (dev.type, dev.index)
+    s = _stream_of(stream, dev)
+    key = (dev.type, dev.index, s.cuda_stream)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = t
     return t
+
+
+def gsa_workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """Wait for `stream`, then read the workspace's error word: 0 (GSA_OK) or
+    8 (GSA_ERR_WAIT, a wait in the single-launch kernel gave up)."""
+    return lib().gsa_workspace_status(_ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream_ptr(stream, ws.device))
+
+
+def gsa_workspace_reset(ws: torch.Tensor, stream=None) -> None:
+    """Enqueue the zeroing of the workspace's control block on `stream`."""
+    st = lib().gsa_workspace_reset(_ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream_ptr(stream, ws.device))
+    if st != 0:
+        raise GsaError(st, "gsa_workspace_reset")
+
+
+def _alloc_out(q: torch.Tensor, stream) -> torch.Tensor:
+    with torch.cuda.stream(_stream_of(stream, q.device)):
+        return torch.empty_like(q)
 
 
 def _check(q, k_cache, v_cache, block_table, seq_lens):
@@ -169,8 +212,7 @@ def _check(q, k_cache, v_cache, block_table, seq_lens):
 
 
 def _stream_ptr(stream, device):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_of(stream, device).cuda_stream)
 
 
 class PreparedCall:
@@ -200,12 +242,12 @@ def prepare_gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks
     p = make_params(q, Hkv, top_k, sm_scale, flags, top_p)
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_out(q, stream)
     nbytes = gsa_workspace_size(p, kv)
     if nbytes == 0:
         raise GsaError(2, "gsa_workspace_size")
     if ws is None:
-        ws = workspace(nbytes, q.device)
+        ws = workspace(nbytes, q.device, stream)
     args = (ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(sel_idx), _ptr(scores),
             _ptr(ws), ws.numel() * ws.element_size(), _stream_ptr(stream, q.device))
     call = PreparedCall(lib().gsa_decode, args,
@@ -227,12 +269,12 @@ def prepare_hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_me
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     m = make_meta(k_meta, v_meta, gists_per_meta, top_k_meta)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_out(q, stream)
     nbytes = hgsa_workspace_size(p, kv, m)
     if nbytes == 0:
         raise GsaError(2, "hgsa_workspace_size")
     if ws is None:
-        ws = workspace(nbytes, q.device)
+        ws = workspace(nbytes, q.device, stream)
     args = (ctypes.byref(p), ctypes.byref(kv), ctypes.byref(m), _ptr(q), _ptr(out),
             _ptr(sel_meta), _ptr(sel_idx), _ptr(ws), ws.numel() * ws.element_size(),
             _stream_ptr(stream, q.device))
@@ -258,12 +300,12 @@ def gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
     p = make_params(q, Hkv, top_k, sm_scale, flags, top_p)
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_out(q, stream)
     nbytes = gsa_workspace_size(p, kv)
     if nbytes == 0:
         raise GsaError(2, "gsa_workspace_size")
     if ws is None:
-        ws = workspace(nbytes, q.device)
+        ws = workspace(nbytes, q.device, stream)
     st = lib().gsa_decode(ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(sel_idx),
                           _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream_ptr(stream, q.device))
@@ -287,12 +329,12 @@ def hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_meta, *, n
     kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
     m = make_meta(k_meta, v_meta, gists_per_meta, top_k_meta)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_out(q, stream)
     nbytes = hgsa_workspace_size(p, kv, m)
     if nbytes == 0:
         raise GsaError(2, "hgsa_workspace_size")
     if ws is None:
-        ws = workspace(nbytes, q.device)
+        ws = workspace(nbytes, q.device, stream)
     st = lib().hgsa_decode(ctypes.byref(p), ctypes.byref(kv), ctypes.byref(m), _ptr(q), _ptr(out),
                            _ptr(sel_meta), _ptr(sel_idx), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream_ptr(stream, q.device))

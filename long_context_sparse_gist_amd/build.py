@@ -34,16 +34,33 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libgsa.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed to build libgsa.so")
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source (one hipcc per file, in parallel) and link
+    libgsa.so; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = os.path.join(PKG, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    compile_flags = [f for f in flags() if f != "-shared"]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc()] + compile_flags + ["-c", "-o", obj, os.path.join(CSRC, src)])
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)), 8)
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+
 #include "gsa.h"
 #include "gsa_internal.h"
 
@@ -184,18 +185,30 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.total = off;
 }
 
+// The current device exists and is a gfx950 (compute capability 9.5): the
+// code object holds gfx950 kernels only.
 gsa_status_t check_device() {
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
         (void)hipGetLastError();
         return GSA_ERR_DEVICE;
     }
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    int dev = -1, major = 0, minor = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 ||
+        hipDeviceGetAttribute(&major, hipDeviceAttributeComputeCapabilityMajor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&minor, hipDeviceAttributeComputeCapabilityMinor, dev) != hipSuccess) {
         (void)hipGetLastError();
         return GSA_ERR_DEVICE;
     }
+    if (major != 9 || minor != 5) return GSA_ERR_DEVICE;
     return GSA_OK;
+}
+
+// Zero `words` 32-bit words at p (the control block).
+__global__ void clear_words_kernel(unsigned* p, size_t words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 gsa_status_t check_workspace(const Plan& pl, void* ws, size_t bytes) {
@@ -235,17 +248,15 @@ size_t hgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa
     return pl.total;
 }
 
-gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q, void* out,
-                        int32_t* sel_idx, float* scores, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-    gsa_status_t s = check_params(p, kv);
-    if (s != GSA_OK) return s;
-    if (!q || !out || !kv->k_cache || !kv->v_cache || !kv->block_table) return GSA_ERR_NULL_ARG;
-    Plan pl;
-    make_plan(p, kv, nullptr, pl);
-    if ((s = check_workspace(pl, workspace, workspace_bytes)) != GSA_OK) return s;
-    if ((s = check_device()) != GSA_OK) return s;
+}  // extern "C"
 
+namespace {
+
+// Everything gsa_decode does after validating its workspace.
+gsa_status_t decode_flat(Plan& pl, const gsa_params_t* p, const gsa_kv_t* kv, const void* q,
+                         void* out, int32_t* sel_idx, float* scores, void* workspace,
+                         void* stream) {
+    gsa_status_t s;
     Args& a = pl.a;
     char* ws = (char*)workspace;
     a.q = q;
@@ -265,7 +276,7 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
 
     if (pl.fused) {
         unsigned* ctl = (unsigned*)(ws + pl.off_ctl);
-        pl.sc.err = ctl + 2;
+        pl.sc.err = ctl + GSA_WORKSPACE_ERROR_OFFSET / sizeof(unsigned);
         a.urec = ctl + kHdrWords;
         a.spairs = (uint64_t*)(ws + pl.off_spairs);
         GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
@@ -282,6 +293,23 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     if ((s = run_attn(pl, gsa::kListUnfolded, pl.S2, st)) != GSA_OK) return s;
     GSA_LAUNCH(gsa::launch_merge(a, 0, st));
     return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q, void* out,
+                        int32_t* sel_idx, float* scores, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    gsa_status_t s = check_params(p, kv);
+    if (s != GSA_OK) return s;
+    if (!q || !out || !kv->k_cache || !kv->v_cache || !kv->block_table) return GSA_ERR_NULL_ARG;
+    Plan pl;
+    make_plan(p, kv, nullptr, pl);
+    if ((s = check_workspace(pl, workspace, workspace_bytes)) != GSA_OK) return s;
+    if ((s = check_device()) != GSA_OK) return s;
+    return decode_flat(pl, p, kv, q, out, sel_idx, scores, workspace, stream);
 }
 
 gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m,
@@ -318,7 +346,7 @@ gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_m
 
     if (pl.fused) {
         unsigned* ctl = (unsigned*)(ws + pl.off_ctl);
-        pl.sc.err = ctl + 2;
+        pl.sc.err = ctl + GSA_WORKSPACE_ERROR_OFFSET / sizeof(unsigned);
         a.urec = ctl + kHdrWords;
         a.spairs = (uint64_t*)(ws + pl.off_spairs);
         a.spairs_c = (uint64_t*)(ws + pl.off_spairs_c);
@@ -334,6 +362,33 @@ gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_m
     return GSA_OK;
 }
 
+gsa_status_t gsa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return GSA_ERR_NULL_ARG;
+    if (((uintptr_t)workspace) % kAlign || workspace_bytes < GSA_WORKSPACE_CONTROL_BYTES)
+        return GSA_ERR_WORKSPACE;
+    gsa_status_t s = check_device();
+    if (s != GSA_OK) return s;
+    unsigned word = 0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+        hipMemcpy(&word, (const char*)workspace + GSA_WORKSPACE_ERROR_OFFSET, sizeof(word),
+                  hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return GSA_ERR_DEVICE;
+    }
+    return word ? GSA_ERR_WAIT : GSA_OK;
+}
+
+gsa_status_t gsa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return GSA_ERR_NULL_ARG;
+    if (((uintptr_t)workspace) % kAlign || workspace_bytes < GSA_WORKSPACE_CONTROL_BYTES)
+        return GSA_ERR_WORKSPACE;
+    gsa_status_t s = check_device();
+    if (s != GSA_OK) return s;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream,
+                       (unsigned*)workspace, kCtlWords);
+    return hipGetLastError() == hipSuccess ? GSA_OK : GSA_ERR_LAUNCH;
+}
+
 const char* gsa_status_string(gsa_status_t s) {
     switch (s) {
         case GSA_OK: return "ok";
@@ -342,8 +397,9 @@ const char* gsa_status_string(gsa_status_t s) {
         case GSA_ERR_BAD_DTYPE: return "unsupported dtype";
         case GSA_ERR_BAD_FLAGS: return "unknown or unsupported flags";
         case GSA_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
-        case GSA_ERR_DEVICE: return "no usable HIP device";
+        case GSA_ERR_DEVICE: return "no usable HIP device, or the current device is not a gfx950";
         case GSA_ERR_LAUNCH: return "kernel launch failed";
+        case GSA_ERR_WAIT: return "a wait in the single-launch kernel gave up: reset the workspace";
     }
     return "unknown status";
 }

@@ -39,7 +39,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gsa_workspace_size", "hgsa_workspace_size", "gsa_decode", "hgsa_decode",
-        "gsa_status_string", "gsa_version"])
+        "gsa_workspace_status", "gsa_workspace_reset", "gsa_status_string", "gsa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -168,6 +168,27 @@ def test_hgsa_validation(lib):
 def test_valid_call_without_device_reports_device_error(lib):
     assert call(lib, params(), kvs()) == 6
     assert call_h(lib, params(), kvs(), meta()) == 6
+
+
+def test_workspace_status_and_reset_validation(lib):
+    need = gsa.WORKSPACE_CONTROL_BYTES
+    for fn in (lib.gsa_workspace_status, lib.gsa_workspace_reset):
+        assert fn(None, need, None) == 1
+        assert fn(ctypes.c_void_p(FAKE + 16), need, None) == 5    # misaligned
+        assert fn(ctypes.c_void_p(FAKE), need - 1, None) == 5     # smaller than the control block
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible")
+def test_workspace_status_without_device_reports_device_error(lib):
+    need = gsa.WORKSPACE_CONTROL_BYTES
+    assert lib.gsa_workspace_status(ctypes.c_void_p(FAKE), need, None) == 6
+    assert lib.gsa_workspace_reset(ctypes.c_void_p(FAKE), need, None) == 6
+
+
+def test_error_word_offset_matches_header():
+    m = re.search(r"#define GSA_WORKSPACE_ERROR_OFFSET \(\(size_t\)(\d+)\)", open(HEADER).read())
+    assert m is not None and int(m[1]) == gsa.WORKSPACE_ERROR_OFFSET
+    assert gsa.STATUS[8] == "GSA_ERR_WAIT" and "GSA_ERR_WAIT = 8" in open(HEADER).read()
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
