@@ -179,6 +179,24 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
                         void* out, int32_t* sel_idx, float* scores,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the library-owned workspace of gsa_decode_noalloc (64 MiB per GPU). */
+#define GSA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* gsa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as gsa_decode, without the workspace: the call uses a
+ * library-owned device array of GSA_NOALLOC_WORKSPACE_BYTES that each GPU
+ * holds from the library's first use on it until the process ends, and calls
+ * no allocating routine.  Shapes whose gsa_workspace_size exceeds that size
+ * return GSA_ERR_WORKSPACE (nothing enqueued).  Each call first clears, with a
+ * fill kernel on `stream`, the part of the array's control block it uses, so
+ * it does not depend on earlier calls (a given-up wait is not reported).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must be serialised by the
+ * caller. */
+gsa_status_t gsa_decode_noalloc(const gsa_params_t* p, const gsa_kv_t* kv, const void* q,
+                                void* out, int32_t* sel_idx, float* scores, void* stream);
+
 /* One H-GSA decode step: keep the top_k_meta meta-gists by routing key, score
  * the gists of the kept groups (plus the gists after the last complete
  * group), keep the top_k of those, and attend over every meta-gist, the kept

@@ -6,8 +6,8 @@ is loaded on first use and a missing or unloadable library raises; there is no
 fallback path.
 
 Names mirror the C ABI in include/gsa.h: gsa_decode, hgsa_decode,
-gsa_workspace_size, hgsa_workspace_size, gsa_workspace_status,
-gsa_workspace_reset, gsa_status_string, gsa_version.
+gsa_decode_noalloc, gsa_workspace_size, hgsa_workspace_size,
+gsa_workspace_status, gsa_workspace_reset, gsa_status_string, gsa_version.
 
 Streams: a call runs on `stream` (default: the current stream of q's
 device).  The output and the cached workspace are allocated, and the
@@ -38,6 +38,8 @@ GSA_PATH_PORTABLE = 0x100
 WORKSPACE_CONTROL_BYTES = 16384 + 512 * 25088
 # byte offset of the control block's error word (nonzero: a wait gave up)
 WORKSPACE_ERROR_OFFSET = 8
+# the library-owned workspace of gsa_decode_noalloc
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 STATUS = {0: "GSA_OK", 1: "GSA_ERR_NULL_ARG", 2: "GSA_ERR_BAD_SHAPE", 3: "GSA_ERR_BAD_DTYPE",
           4: "GSA_ERR_BAD_FLAGS", 5: "GSA_ERR_WORKSPACE", 6: "GSA_ERR_DEVICE",
@@ -94,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.hgsa_decode.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
                                   ctypes.POINTER(HgsaMeta), P, P, P, P, P, ctypes.c_size_t, P]
         L.hgsa_decode.restype = ctypes.c_int
+        L.gsa_decode_noalloc.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV), P, P,
+                                         P, P, P]
+        L.gsa_decode_noalloc.restype = ctypes.c_int
         L.gsa_workspace_status.argtypes = [P, ctypes.c_size_t, P]
         L.gsa_workspace_status.restype = ctypes.c_int
         L.gsa_workspace_reset.argtypes = [P, ctypes.c_size_t, P]
@@ -311,6 +316,22 @@ def gsa_decode(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
                           _stream_ptr(stream, q.device))
     if st != 0:
         raise GsaError(st, "gsa_decode")
+    return out
+
+
+def gsa_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, num_chunks: int,
+                       chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
+                       flags: int = 0, top_p: float = 0.0, out, sel_idx=None, scores=None,
+                       stream=None):
+    """gsa_decode on the library-owned workspace (see gsa_decode_noalloc in
+    include/gsa.h).  `out` must be given: this path allocates nothing."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    p = make_params(q, k_cache.shape[1], top_k, sm_scale, flags, top_p)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    st = lib().gsa_decode_noalloc(ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(out),
+                                  _ptr(sel_idx), _ptr(scores), _stream_ptr(stream, q.device))
+    if st != 0:
+        raise GsaError(st, "gsa_decode_noalloc")
     return out
 
 

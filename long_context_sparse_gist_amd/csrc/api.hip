@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "gsa.h"
 #include "gsa_internal.h"
@@ -252,10 +253,37 @@ size_t hgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa
 
 namespace {
 
-// Everything gsa_decode does after validating its workspace.
+// Library-owned workspace of gsa_decode_noalloc: one copy per GPU, allocated
+// when the code object is loaded on that GPU and held until the process ends.
+constexpr size_t kScratchBytes = (size_t)GSA_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's copy of `scratch` (the name itself is a host
+// stand-in, not a device address), looked up once per device with that device
+// current.
+void* scratch_ptr(int dev) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDev] = {};
+    if (dev < 0 || dev >= kMaxDev) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+// Everything gsa_decode does after validating its workspace.  clear_ctl:
+// first zero the part of the control block this call uses (error word and
+// the units' records) with a fill kernel on `st`.
 gsa_status_t decode_flat(Plan& pl, const gsa_params_t* p, const gsa_kv_t* kv, const void* q,
                          void* out, int32_t* sel_idx, float* scores, void* workspace,
-                         void* stream) {
+                         void* stream, bool clear_ctl) {
     gsa_status_t s;
     Args& a = pl.a;
     char* ws = (char*)workspace;
@@ -279,6 +307,12 @@ gsa_status_t decode_flat(Plan& pl, const gsa_params_t* p, const gsa_kv_t* kv, co
         pl.sc.err = ctl + GSA_WORKSPACE_ERROR_OFFSET / sizeof(unsigned);
         a.urec = ctl + kHdrWords;
         a.spairs = (uint64_t*)(ws + pl.off_spairs);
+        if (clear_ctl) {
+            const size_t words = kHdrWords + (size_t)pl.sc.units * a.recs_per_unit * gsa::kUnitRec;
+            hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                               dim3(256), 0, st, ctl, words);
+            GSA_LAUNCH(hipGetLastError());
+        }
         GSA_LAUNCH(gsa::launch_fused(a, pl.sc, st));
         return GSA_OK;
     }
@@ -309,7 +343,26 @@ gsa_status_t gsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const void* q
     make_plan(p, kv, nullptr, pl);
     if ((s = check_workspace(pl, workspace, workspace_bytes)) != GSA_OK) return s;
     if ((s = check_device()) != GSA_OK) return s;
-    return decode_flat(pl, p, kv, q, out, sel_idx, scores, workspace, stream);
+    return decode_flat(pl, p, kv, q, out, sel_idx, scores, workspace, stream, false);
+}
+
+gsa_status_t gsa_decode_noalloc(const gsa_params_t* p, const gsa_kv_t* kv, const void* q,
+                                void* out, int32_t* sel_idx, float* scores, void* stream) {
+    gsa_status_t s = check_params(p, kv);
+    if (s != GSA_OK) return s;
+    if (!q || !out || !kv->k_cache || !kv->v_cache || !kv->block_table) return GSA_ERR_NULL_ARG;
+    Plan pl;
+    make_plan(p, kv, nullptr, pl);
+    if (pl.total > kScratchBytes) return GSA_ERR_WORKSPACE;
+    if ((s = check_device()) != GSA_OK) return s;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return GSA_ERR_DEVICE;
+    }
+    void* ws = scratch_ptr(dev);
+    if (!ws) return GSA_ERR_DEVICE;
+    return decode_flat(pl, p, kv, q, out, sel_idx, scores, ws, stream, true);
 }
 
 gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m,

@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gsa_workspace_size", "hgsa_workspace_size", "gsa_decode", "hgsa_decode",
-        "gsa_workspace_status", "gsa_workspace_reset", "gsa_status_string", "gsa_version"])
+        "gsa_decode_noalloc", "gsa_workspace_status", "gsa_workspace_reset",
+        "gsa_status_string", "gsa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -168,6 +169,36 @@ def test_hgsa_validation(lib):
 def test_valid_call_without_device_reports_device_error(lib):
     assert call(lib, params(), kvs()) == 6
     assert call_h(lib, params(), kvs(), meta()) == 6
+
+
+def call_na(lib, p, kv, q=FAKE, out=FAKE):
+    return lib.gsa_decode_noalloc(ctypes.byref(p), ctypes.byref(kv), ctypes.c_void_p(q),
+                                  ctypes.c_void_p(out), None, None, None)
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free entry point validates like gsa_decode and rejects
+    shapes whose workspace exceeds its fixed array."""
+    for kw, code in BAD_PARAMS:
+        assert call_na(lib, params(**kw), kvs()) == code
+    for kw, code in BAD_KV:
+        assert call_na(lib, params(), kvs(**kw)) == code
+    assert call_na(lib, params(), kvs(), q=0) == 1
+    assert call_na(lib, params(), kvs(), out=0) == 1
+    # 16 x 16 units of 65536 chunks: keys alone take 64 MiB
+    big_p, big_kv = params(batch=16, num_kv_heads=16, num_q_heads=16), kvs(num_chunks=65536,
+                                                                            max_pages=4097)
+    assert lib.gsa_workspace_size(ctypes.byref(big_p), ctypes.byref(big_kv)) > \
+        gsa.NOALLOC_WORKSPACE_BYTES
+    assert call_na(lib, big_p, big_kv) == 5
+    m = re.search(r"#define GSA_NOALLOC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m is not None and int(m[1]) << int(m[2]) == gsa.NOALLOC_WORKSPACE_BYTES
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible")
+def test_noalloc_without_device_reports_device_error(lib):
+    assert call_na(lib, params(), kvs()) == 6
 
 
 def test_workspace_status_and_reset_validation(lib):
