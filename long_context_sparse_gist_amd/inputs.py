@@ -244,3 +244,45 @@ def share_pages(inp: GsaInputs, src_b: int, dst_b: int) -> GsaInputs:
     bt = inp.block_table.clone()
     bt[dst_b] = bt[src_b]
     return dataclasses.replace(inp, block_table=bt)
+
+
+def level_sizes(num_chunks: int, fanouts) -> list:
+    """Entries of each meta-gist level above `num_chunks` gists (complete
+    groups only): level l has floor(entries of level l-1 / fanouts[l-1])."""
+    out, n = [], num_chunks
+    for R in fanouts:
+        n //= R
+        out.append(n)
+    return out
+
+
+def make_levels(inp: GsaInputs, fanouts, seed: int, plant: bool = True) -> list:
+    """Meta-gist levels for a hierarchy above the gists of `inp`: a list of
+    (k, v) pairs, level 1 first, each [B][Hkv][entries][d] in the inputs'
+    dtype, N(0, 1) drawn on the inputs' device with generator seed `seed`
+    (per level: K, then its planting noise, then V).  With `plant`, the
+    ancestors of every planted chunk at every level get keys aligned with the
+    group's summed query, as the planted gists have (2*sqrt(d)*q_dir + N(0, 0.1))."""
+    wl = inp.wl
+    dev = inp.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    B, Hkv, d = wl.batch, wl.num_kv_heads, wl.head_dim
+    tdt = _TORCH_DTYPE[wl.dtype]
+    qdir = group_direction(inp.q.float(), Hkv)
+    chunks = inp.planted if (plant and wl.plant in ("align", "align_meta")) else None
+    levels, span = [], 1
+    for R, n in zip(fanouts, level_sizes(wl.num_chunks, fanouts)):
+        span *= R
+        x = torch.randn(B, Hkv, max(n, 1), d, generator=g, device=dev, dtype=torch.float32)
+        if chunks is not None and chunks.numel() and n > 0:
+            anc = torch.div(chunks, span, rounding_mode="floor")          # [B][Hkv][P]
+            noise = 0.1 * torch.randn(*anc.shape, d, generator=g, device=dev)
+            val = 2.0 * math.sqrt(d) * qdir.unsqueeze(2) + noise
+            ok = anc < n
+            bi = torch.arange(B, device=dev).view(B, 1, 1).expand_as(anc)[ok]
+            hi = torch.arange(Hkv, device=dev).view(1, Hkv, 1).expand_as(anc)[ok]
+            x[bi, hi, anc[ok]] = val[ok]
+        v = torch.randn(B, Hkv, max(n, 1), d, generator=g, device=dev, dtype=torch.float32)
+        levels.append((x.to(tdt), v.to(tdt)))
+    return levels

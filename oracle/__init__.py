@@ -50,6 +50,11 @@ def load(path: str) -> ctypes.CDLL:
     lib.gsa_oracle_decode.restype = ctypes.c_int
     lib.hgsa_oracle_decode.argtypes = [ctypes.POINTER(OracleCfg)] + [P] * 14 + [ctypes.c_int]
     lib.hgsa_oracle_decode.restype = ctypes.c_int
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.mgsa_oracle_decode.argtypes = ([ctypes.POINTER(OracleCfg)] + [P] * 5 + [ctypes.c_int] +
+                                       [PP, PP, IP, IP, IP, P, PP, PP, PP, ctypes.c_int])
+    lib.mgsa_oracle_decode.restype = ctypes.c_int
     lib.gsa_oracle_threads.restype = ctypes.c_int
     return lib
 
@@ -143,3 +148,47 @@ def hgsa_decode(cfg: dict, q, k_cache, v_cache, block_table, seq_lens, k_meta, v
     if rc:
         raise ValueError(f"oracle rejected the configuration (code {rc})")
     return out, s1, s2, ms, gs
+
+
+def _ptr_array(arrs):
+    """ctypes array of data pointers (None -> NULL)."""
+    return (ctypes.c_void_p * max(1, len(arrs)))(*[None if a is None else a.ctypes.data
+                                                    for a in arrs])
+
+
+def mgsa_decode(cfg: dict, q, k_cache, v_cache, block_table, seq_lens, levels,
+                ext=None, nthreads: int = 0, lib=None):
+    """Hierarchy of len(levels) meta-gist levels above the gists.  levels[l-1]
+    = (k [B][Hkv][max][d], v, fanout, top_k) for level l = 1..L; cfg's top_k
+    is the gist level's k.  ext: None or L + 1 arrays/None (level 0 first).
+    Returns (out float64 [B][Hq][d], sels, keys): sels[l] int32
+    [B][Hkv][k_l] ascending -1 padded, keys[l] float32 [B][Hkv][max_l] of
+    every entry (level 0: [B][Hkv][num_chunks])."""
+    lib = lib or _load()
+    c = _cfg(cfg)
+    B, Hq, Hkv, d = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+    L = len(levels)
+    q, k_cache, v_cache = (_data(x, c.dtype) for x in (q, k_cache, v_cache))
+    ks = [_data(lv[0], c.dtype) for lv in levels]
+    vs = [_data(lv[1], c.dtype) for lv in levels]
+    maxs = (ctypes.c_int * max(1, L))(*[k.shape[2] for k in ks])
+    fans = (ctypes.c_int * max(1, L))(*[int(lv[2]) for lv in levels])
+    tops = (ctypes.c_int * max(1, L))(*[int(lv[3]) for lv in levels])
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.zeros((B, Hq, d), np.float64)
+    kk = [max(c.top_k, 0)] + [max(int(lv[3]), 0) for lv in levels]
+    caps = [c.num_chunks] + [k.shape[2] for k in ks]
+    sels = [np.zeros((B, Hkv, kk[l]), np.int32) for l in range(L + 1)]
+    keys = [np.zeros((B, Hkv, caps[l]), np.float32) for l in range(L + 1)]
+    exts = None
+    if ext is not None:
+        exts = [None if e is None else _c(e, np.int32) for e in ext]
+        assert len(exts) == L + 1
+    rc = lib.mgsa_oracle_decode(ctypes.byref(c), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                _ptr(sl), L, _ptr_array(ks), _ptr_array(vs), maxs, fans, tops,
+                                _ptr(out), _ptr_array(sels), _ptr_array(keys),
+                                None if exts is None else _ptr_array(exts), nthreads)
+    if rc:
+        raise ValueError(f"oracle rejected the configuration (code {rc})")
+    return out, sels, keys

@@ -35,6 +35,18 @@
  *              Uitbreiding"): score meta-gists, keep top-k1, score the gists of
  *              the kept groups, keep top-k2, unfold their raw tokens; attend to
  *              all meta-gists, the kept gists and their raw tokens.
+ *   O7 levels  the recursive hierarchy (ja page 2.2: meta-gists built again
+ *              over meta-gists into a multi-level structure, coarse-to-fine
+ *              selection, O(log n) decoding; nl page "Hierarchische
+ *              Uitbreiding"): L levels of meta-gists above the gists, level l
+ *              entry r summarising entries [r*R_l, (r+1)*R_l) of level l-1.
+ *              Every entry of the top level is scored and attended; going
+ *              down, the candidates of a level are the children of the entries
+ *              kept one level up plus the entries past that level's last
+ *              complete group; the top-k of the candidates are kept.  Set:
+ *              every top-level entry, the kept entries and the past-the-last-
+ *              group entries of each level below it, the kept chunks' raw
+ *              tokens, the raw tail.  L = 1 is O5, L = 0 is O1-O4.
  *   O6         O3-O5 with the selection supplied by the caller: its ids that
  *              lie in the sequence (chunk ids in [0, n), meta-group ids in
  *              [0, n/R)) in place of the top-k at that level, in any order;
@@ -488,6 +500,164 @@ int hgsa_oracle_decode(const oracle_cfg *c, const void *q, const void *k_cache,
                   gist_scores ? gist_scores + (size_t)u * c->num_chunks : NULL,
                   ext_sel_meta ? ext_sel_meta + (size_t)u * c->top_k_meta : NULL,
                   ext_sel ? ext_sel + (size_t)u * c->top_k : NULL);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* ---- O7: hierarchy of L levels ----------------------------------------- */
+
+/* one level of meta-gists (level l >= 1; level 0 is the gists themselves) */
+typedef struct {
+    const void *k, *v;   /* [B][Hkv][max_entries][d] */
+    int max_entries;     /* >= entries of the level below / fanout */
+    int fanout;          /* R_l >= 1 */
+    int top_k;           /* k_l >= 0 entries kept */
+} oracle_level;
+
+/* Keep the ids of an external selection that lie in [0, count), ascending. */
+static int ext_filter(const int32_t *ext, int k, int count, int *sel) {
+    int ns = 0;
+    for (int i = 0; i < k; i++) if (ext[i] >= 0 && ext[i] < count) sel[ns++] = ext[i];
+    qsort(sel, (size_t)ns, sizeof(int), cmp_int);
+    return ns;
+}
+
+static void mgsa_unit(const oracle_cfg *c, const void *q, const void *kc, const void *vc,
+                      const int32_t *bt, const oracle_level *lv, int L, int b, int g,
+                      int n, int tail, double *out, int32_t *const *sel_out, float *const *key_out,
+                      const int32_t *const *ext, size_t u) {
+    int C = c->chunk_size, d = c->head_dim;
+    seqview sv = {c, kc, vc, bt, b, g};
+    int cnt[33];                 /* entries per level */
+    cnt[0] = n;
+    for (int l = 1; l <= L; l++) cnt[l] = cnt[l - 1] / lv[l - 1].fanout;
+    /* flat index of entry r of level l (level 0: the gist row in the cache) */
+#define ROW_OF(l, r) ((l) == 0 ? slot_base(&sv, (long)(r) * (C + 1) + C) \
+                     : ((size_t)b * c->num_kv_heads + g) * (size_t)lv[(l) - 1].max_entries * d + (size_t)(r) * d)
+#define ARR_K(l) ((l) == 0 ? kc : lv[(l) - 1].k)
+#define ARR_V(l) ((l) == 0 ? vc : lv[(l) - 1].v)
+    /* keys of every entry of every level (tests), plain logit sums */
+    for (int l = 0; l <= L; l++) {
+        if (!key_out || !key_out[l]) continue;
+        int nl = cnt[l], cap = l == 0 ? c->num_chunks : lv[l - 1].max_entries;
+        size_t *rows = (size_t *)malloc(sizeof(size_t) * (size_t)(nl > 0 ? nl : 1));
+        float *S = (float *)malloc(sizeof(float) * (size_t)(nl > 0 ? nl : 1));
+        for (int r = 0; r < nl; r++) rows[r] = ROW_OF(l, r);
+        routing_keys(c, q, b, g, ARR_K(l), rows, nl, S);
+        for (int r = 0; r < cap; r++) key_out[l][u * cap + r] = r < nl ? S[r] : -INFINITY;
+        free(rows); free(S);
+    }
+    /* coarse to fine: candidates of the top level are all its entries */
+    int *sel[33];
+    int nsel[33];
+    int *cand = (int *)malloc(sizeof(int) * (size_t)(cnt[L] > 0 ? cnt[L] : 1));
+    int nc = cnt[L];
+    for (int r = 0; r < nc; r++) cand[r] = r;
+    for (int l = L; l >= 0; l--) {
+        int k = l == 0 ? c->top_k : lv[l - 1].top_k;
+        size_t *rows = (size_t *)malloc(sizeof(size_t) * (size_t)(nc > 0 ? nc : 1));
+        float *S = (float *)malloc(sizeof(float) * (size_t)(nc > 0 ? nc : 1));
+        for (int i = 0; i < nc; i++) rows[i] = ROW_OF(l, cand[i]);
+        routing_keys(c, q, b, g, ARR_K(l), rows, nc, S);
+        sel[l] = (int *)malloc(sizeof(int) * (size_t)(k > 0 ? k : 1));
+        if (ext && ext[l]) nsel[l] = ext_filter(ext[l] + u * k, k, cnt[l], sel[l]);
+        else nsel[l] = topk(S, cand, nc, k, sel[l]);
+        if (sel_out && sel_out[l])
+            for (int i = 0; i < k; i++) sel_out[l][u * k + i] = i < nsel[l] ? sel[l][i] : -1;
+        free(rows); free(S);
+        if (l > 0) {  /* children of the kept entries, then the entries past the last group */
+            int R = lv[l - 1].fanout;
+            int nn = nsel[l] * R + (cnt[l - 1] - cnt[l] * R);
+            free(cand);
+            cand = (int *)malloc(sizeof(int) * (size_t)(nn > 0 ? nn : 1));
+            nc = 0;
+            for (int i = 0; i < nsel[l]; i++)
+                for (int j = 0; j < R; j++) cand[nc++] = sel[l][i] * R + j;
+            for (int r = cnt[l] * R; r < cnt[l - 1]; r++) cand[nc++] = r;
+        }
+    }
+    free(cand);
+    /* the set */
+    long cap = (long)n * (C + 1) + tail;
+    for (int l = 1; l <= L; l++) cap += cnt[l];
+    tokref *T = (tokref *)malloc(sizeof(tokref) * (size_t)(cap > 0 ? cap : 1));
+    long nT = 0;
+    for (int l = L; l >= 1; l--) {
+        /* top level: every entry; below: kept or past the last complete group */
+        char *in = (char *)calloc((size_t)(cnt[l] > 0 ? cnt[l] : 1), 1);
+        for (int i = 0; i < nsel[l]; i++) in[sel[l][i]] = 1;
+        int past = l == L ? 0 : cnt[l + 1] * lv[l].fanout;
+        for (int r = 0; r < cnt[l]; r++)
+            if (l == L || in[r] || r >= past) {
+                T[nT].arr_k = ARR_K(l); T[nT].arr_v = ARR_V(l); T[nT].row = ROW_OF(l, r); nT++;
+            }
+        free(in);
+    }
+    char *is_sel = (char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    for (int i = 0; i < nsel[0]; i++) is_sel[sel[0][i]] = 1;
+    int past0 = L == 0 ? 0 : cnt[1] * lv[0].fanout;
+    for (int m = 0; m < n; m++) {
+        long s0 = (long)m * (C + 1);
+        if (is_sel[m])
+            for (int r = 0; r < C; r++) { T[nT].arr_k = kc; T[nT].arr_v = vc; T[nT].row = slot_base(&sv, s0 + r); nT++; }
+        if (L == 0 || is_sel[m] || m >= past0) { T[nT].arr_k = kc; T[nT].arr_v = vc; T[nT].row = slot_base(&sv, s0 + C); nT++; }
+    }
+    for (int r = 0; r < tail; r++) { T[nT].arr_k = kc; T[nT].arr_v = vc; T[nT].row = slot_base(&sv, (long)n * (C + 1) + r); nT++; }
+    attend(c, q, b, g, T, nT, out);
+    free(T); free(is_sel);
+    for (int l = 0; l <= L; l++) free(sel[l]);
+#undef ROW_OF
+#undef ARR_K
+#undef ARR_V
+}
+
+/* L (0..32) levels of meta-gists above the gists.  Level arrays are indexed
+ * by level l = 1..L at [l - 1]: k_levels / v_levels [B][Hkv][max_entries][d],
+ * fanout R_l, top_k_levels k_l.  sel / keys / ext: NULL, or L + 1 pointers
+ * (each NULL or an array), level 0 (the gists) first: sel[0] [B][Hkv][top_k],
+ * sel[l] [B][Hkv][k_l]; keys[0] [B][Hkv][num_chunks], keys[l]
+ * [B][Hkv][max_entries_l] (plain logit-sum keys of every entry, -inf past
+ * the sequence's entries); ext[l]: caller selections, as sel.
+ * Returns 0, or 1 null pointer, 2 bad shape, 3 bad dtype, 4 bad flags. */
+int mgsa_oracle_decode(const oracle_cfg *c, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_table, const int32_t *seq_lens,
+                       int num_levels, const void *const *k_levels, const void *const *v_levels,
+                       const int *max_entries, const int *fanout, const int *top_k_levels,
+                       double *out, int32_t *const *sel, float *const *keys,
+                       const int32_t *const *ext, int nthreads) {
+    if (!c || !q || !k_cache || !v_cache || !block_table || !out) return 1;
+    if (num_levels < 0 || num_levels > 32) return 2;
+    int e = check_cfg(c, 0);
+    if (e) return e;
+    if (num_levels > 0 && (c->flags & (ORACLE_SET_SELECTED_GISTS | ORACLE_SCORE_SUM_PROBS |
+                                       ORACLE_SELECT_TOP_P))) return 4;
+    oracle_level lv[32];
+    long below = c->num_chunks;
+    for (int l = 0; l < num_levels; l++) {
+        if (!k_levels || !v_levels || !max_entries || !fanout || !top_k_levels) return 1;
+        if (!k_levels[l] || !v_levels[l]) return 1;
+        lv[l].k = k_levels[l]; lv[l].v = v_levels[l];
+        lv[l].max_entries = max_entries[l]; lv[l].fanout = fanout[l]; lv[l].top_k = top_k_levels[l];
+        if (lv[l].fanout < 1 || lv[l].top_k < 0) return 2;
+        below /= lv[l].fanout;
+        if (lv[l].max_entries < below) return 2;
+    }
+    for (int b = 0; b < c->batch; b++) {
+        int n, t;
+        if ((e = seq_shape(c, seq_lens, b, &n, &t))) return e;
+    }
+    int units = c->batch * c->num_kv_heads;
+    int G = c->num_q_heads / c->num_kv_heads, d = c->head_dim;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int u = 0; u < units; u++) {
+        int b = u / c->num_kv_heads, g = u % c->num_kv_heads, n, tail;
+        seq_shape(c, seq_lens, b, &n, &tail);
+        mgsa_unit(c, q, k_cache, v_cache, block_table, lv, num_levels, b, g, n, tail,
+                  out + ((size_t)b * c->num_q_heads + (size_t)g * G) * d, sel, keys, ext, (size_t)u);
     }
     (void)nthreads;
     return 0;

@@ -11,6 +11,7 @@ import pytest
 import oracle
 from tests import _util as U
 from tests import test_oracle_pins as P
+from tests import test_oracle_levels as PL
 from long_context_sparse_gist_amd import inputs as gi
 
 MUTANTS = {
@@ -51,6 +52,16 @@ MUTANTS = {
                                 "if (ext_sel[i] >= 0 && ext_sel[i] < c->num_chunks) sel[ns++]"),
     "ext1_ignored": ("    if (ext1) {", "    if (0) {"),
     "ext2_ignored": ("    if (ext2) {", "    if (0) {"),
+    "level_children_wrong": ("cand[nc++] = sel[l][i] * R + j;", "cand[nc++] = sel[l][i] + j * cnt[l];"),
+    "level_tail_not_candidates": ("for (int r = cnt[l] * R; r < cnt[l - 1]; r++) cand[nc++] = r;",
+                                  "for (int r = cnt[l] * R; r < cnt[l] * R; r++) cand[nc++] = r;"),
+    "level_keys_from_v": ("routing_keys(c, q, b, g, ARR_K(l), rows, nc, S);",
+                          "routing_keys(c, q, b, g, ARR_V(l), rows, nc, S);"),
+    "level_kept_not_attended": ("if (l == L || in[r] || r >= past)", "if (l == L || r >= past)"),
+    "level_tail_not_attended": ("if (l == L || in[r] || r >= past)", "if (l == L || in[r])"),
+    "top_level_only_kept_attended": ("if (l == L || in[r] || r >= past)",
+                                     "if (in[r] || (l < L && r >= past))"),
+    "level_gist_tail_dropped": ("if (L == 0 || is_sel[m] || m >= past0)", "if (L == 0 || is_sel[m])"),
     "meta_gists_not_attended": ("for (int r = 0; r < nm; r++) { T[nT].arr_k = km;",
                                 "for (int r = 0; r < 0; r++) { T[nT].arr_k = km;"),
 }
@@ -80,6 +91,18 @@ def pin_battery():
         out.append((f"o6_h/{which}", lambda which=which: P.test_o6_external_selection_hgsa(which)))
     for wl in (P.SMALL_BF16, P.SMALL_F32):
         out.append((f"pi/{wl.name}", lambda wl=wl: P.test_pi_convex_hull(wl)))
+    out += [("lv_flat", PL.test_no_meta_level_is_flat_gsa),
+            ("lv_hgsa", PL.test_one_meta_level_is_two_level_hgsa),
+            ("lv_f32", PL.test_levels_f32_and_planted_ancestors),
+            ("lv_dense", PL.test_everything_kept_is_dense_over_all_levels)]
+    for fo, tp in [((4, 3), (5, 2)), ((3, 2, 2), (4, 3, 2)), ((2, 2, 2), (3, 2, 1))]:
+        for lens in ("full", "ragged"):
+            out.append((f"lv_bf/{fo}/{lens}",
+                        lambda fo=fo, tp=tp, lens=lens: PL.test_levels_match_brute_force(fo, tp, lens)))
+    for which in (0, 1, 2):
+        out.append((f"lv_ext/{which}", lambda which=which: PL.test_caller_selection_at_a_level(which)))
+    for name in sorted(PL.CASES):
+        out.append((f"lv_golden/{name}", lambda name=name: PL.test_levels_hand_worked(name)))
     return out
 
 
