@@ -223,6 +223,46 @@ gsa_status_t gsa_workspace_status(const void* workspace, size_t workspace_bytes,
  * Must not overlap a decode call that uses the same workspace. */
 gsa_status_t gsa_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
+/* Hierarchy of any depth.  One level of meta-gists: level 1 lies over the
+ * gists, level l over level l-1; entry r of level l summarises entries
+ * [r*fanout, (r+1)*fanout) of the level below and exists once all of them do
+ * (the gist-of-gist structure built recursively, ja page 2.2; nl page,
+ * "Hierarchische Uitbreiding").
+ *   k_meta, v_meta : [batch][num_kv_heads][max_meta][head_dim], dtype */
+typedef struct {
+    const void* k_meta;
+    const void* v_meta;
+    int32_t max_meta;   /* >= the level's entries at full capacity: num_chunks
+                           divided (rounding down) by the fanouts up to this level */
+    int32_t fanout;     /* R_l >= 1 */
+    int32_t top_k;      /* k_l >= 0 entries kept at this level */
+} gsa_level_t;
+
+#define GSA_MAX_LEVELS 8
+
+/* Bytes of workspace mgsa_decode needs (0 if the shapes are invalid); the
+ * same layout rules as gsa_workspace_size (control block first). */
+size_t mgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* levels,
+                           int32_t num_levels);
+
+/* One decode step over num_levels (0 .. GSA_MAX_LEVELS) levels of meta-gists
+ * above the gists, coarse to fine: every entry of the top level is scored and
+ * attended and its top-k kept; at each level below, the candidates are the
+ * children of the entries kept one level up plus the entries past the level's
+ * last complete group, and their top-k is kept (the gist level's k is
+ * p->top_k); the kept chunks' raw tokens are unfolded.  Attention set: every
+ * top-level entry, the kept entries and the past-the-last-group entries of
+ * each level below the top (gists included), the kept chunks' raw tokens and
+ * the raw tail.  num_levels = 0 is flat GSA, 1 the two-level H-GSA of
+ * hgsa_decode.  bf16 only, default key and set (flags 0).
+ *   levels : [num_levels], level 1 first (NULL if num_levels = 0)
+ *   sel    : NULL, or num_levels + 1 pointers (each NULL or int32
+ *            [batch][num_kv_heads][k]), the gist level first (k = p->top_k),
+ *            then level l (k = levels[l-1].top_k): kept ids ascending, -1 padded */
+gsa_status_t mgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* levels,
+                         int32_t num_levels, const void* q, void* out, int32_t* const* sel,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status_t s);
 

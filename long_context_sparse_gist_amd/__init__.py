@@ -6,8 +6,8 @@ is loaded on first use and a missing or unloadable library raises; there is no
 fallback path.
 
 Names mirror the C ABI in include/gsa.h: gsa_decode, hgsa_decode,
-gsa_decode_noalloc, gsa_workspace_size, hgsa_workspace_size,
-gsa_workspace_status, gsa_workspace_reset, gsa_status_string, gsa_version.
+gsa_decode_noalloc, mgsa_decode, gsa_workspace_size, hgsa_workspace_size,
+mgsa_workspace_size, gsa_workspace_status, gsa_workspace_reset, gsa_status_string, gsa_version.
 
 Streams: a call runs on `stream` (default: the current stream of q's
 device).  The output and the cached workspace are allocated, and the
@@ -67,6 +67,14 @@ class HgsaMeta(ctypes.Structure):
                 ("top_k_meta", ctypes.c_int32)]
 
 
+class GsaLevel(ctypes.Structure):
+    _fields_ = [("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
+                ("max_meta", ctypes.c_int32), ("fanout", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+MAX_LEVELS = 8
+
+
 class GsaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -99,6 +107,13 @@ def lib() -> ctypes.CDLL:
         L.gsa_decode_noalloc.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV), P, P,
                                          P, P, P]
         L.gsa_decode_noalloc.restype = ctypes.c_int
+        L.mgsa_workspace_size.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
+                                          ctypes.POINTER(GsaLevel), ctypes.c_int32]
+        L.mgsa_workspace_size.restype = ctypes.c_size_t
+        L.mgsa_decode.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV),
+                                  ctypes.POINTER(GsaLevel), ctypes.c_int32, P, P,
+                                  ctypes.POINTER(ctypes.c_void_p), P, ctypes.c_size_t, P]
+        L.mgsa_decode.restype = ctypes.c_int
         L.gsa_workspace_status.argtypes = [P, ctypes.c_size_t, P]
         L.gsa_workspace_status.restype = ctypes.c_int
         L.gsa_workspace_reset.argtypes = [P, ctypes.c_size_t, P]
@@ -362,3 +377,65 @@ def hgsa_decode(q, k_cache, v_cache, block_table, seq_lens, k_meta, v_meta, *, n
     if st != 0:
         raise GsaError(st, "hgsa_decode")
     return out
+
+
+def make_levels(levels) -> "ctypes.Array":
+    """levels: [(k_meta, v_meta, fanout, top_k)], level 1 first, each meta
+    array [B][Hkv][max_meta][d] -> a gsa_level_t array."""
+    arr = (GsaLevel * max(1, len(levels)))()
+    for i, (k, v, R, kk) in enumerate(levels):
+        arr[i] = GsaLevel(_ptr(k), _ptr(v), k.shape[2], R, kk)
+    return arr
+
+
+def mgsa_workspace_size(params: GsaParams, kv: GsaKV, levels_arr, num_levels: int) -> int:
+    return lib().mgsa_workspace_size(ctypes.byref(params), ctypes.byref(kv), levels_arr,
+                                     num_levels)
+
+
+def prepare_mgsa_decode(q, k_cache, v_cache, block_table, seq_lens, levels, *, num_chunks: int,
+                        chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0,
+                        out=None, sel=None, ws=None, stream=None) -> PreparedCall:
+    """mgsa_decode's arguments marshalled into a PreparedCall.  levels:
+    [(k_meta, v_meta, fanout, top_k)], level 1 first; sel: None or
+    len(levels) + 1 int32 tensors / None (the gist level first)."""
+    _check(q, k_cache, v_cache, block_table, seq_lens)
+    for k, v, _, _ in levels:
+        if not k.is_cuda or not k.is_contiguous() or not v.is_contiguous() or k.dtype != q.dtype:
+            raise ValueError("level arrays must be contiguous device tensors of q's dtype")
+    p = make_params(q, k_cache.shape[1], top_k, sm_scale)
+    kv = make_kv(k_cache, v_cache, block_table, seq_lens, num_chunks, chunk_size, page_chunks)
+    lv = make_levels(levels)
+    L = len(levels)
+    if out is None:
+        out = _alloc_out(q, stream)
+    nbytes = mgsa_workspace_size(p, kv, lv, L)
+    if nbytes == 0:
+        raise GsaError(2, "mgsa_workspace_size")
+    if ws is None:
+        ws = workspace(nbytes, q.device, stream)
+    sel_arr = None
+    if sel is not None:
+        if len(sel) != L + 1:
+            raise ValueError("sel needs one entry per level plus the gist level")
+        sel_arr = (ctypes.c_void_p * (L + 1))(*[None if t is None else t.data_ptr() for t in sel])
+    args = (ctypes.byref(p), ctypes.byref(kv), lv, L, _ptr(q), _ptr(out), sel_arr, _ptr(ws),
+            ws.numel() * ws.element_size(), _stream_ptr(stream, q.device))
+    call = PreparedCall(lib().mgsa_decode, args,
+                        (p, kv, lv, q, k_cache, v_cache, block_table, seq_lens, levels, out, sel,
+                         sel_arr, ws), "mgsa_decode")
+    call.out = out
+    return call
+
+
+def mgsa_decode(q, k_cache, v_cache, block_table, seq_lens, levels, *, num_chunks: int,
+                chunk_size: int, page_chunks: int, top_k: int, sm_scale: float = 0.0, out=None,
+                sel=None, ws=None, stream=None):
+    """One decode step over a hierarchy of len(levels) meta-gist levels (see
+    mgsa_decode in include/gsa.h).  Returns out [B][Hq][d]."""
+    call = prepare_mgsa_decode(q, k_cache, v_cache, block_table, seq_lens, levels,
+                               num_chunks=num_chunks, chunk_size=chunk_size,
+                               page_chunks=page_chunks, top_k=top_k, sm_scale=sm_scale, out=out,
+                               sel=sel, ws=ws, stream=stream)
+    call()
+    return call.out

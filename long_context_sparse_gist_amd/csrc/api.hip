@@ -8,6 +8,7 @@
 
 #include "gsa.h"
 #include "gsa_internal.h"
+#include "gsa_levels.h"
 
 namespace {
 
@@ -231,9 +232,138 @@ gsa_status_t run_attn(const Plan& pl, int kind, int splits, hipStream_t st) {
     return GSA_OK;
 }
 
+// ---- hierarchy of any depth ----
+
+struct LvPlan {
+    gsa::LvArgs A;
+    size_t off_keys, off_cid[2], off_desc[2], off_ncand[2], off_fdesc, off_nfin,
+        off_sel[gsa::kMaxLevels + 1], off_ml, off_acc, total;
+};
+
+gsa_status_t check_levels(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* lv, int L) {
+    if (L < 0 || L > gsa::kMaxLevels) return GSA_ERR_BAD_SHAPE;
+    if (L > 0 && !lv) return GSA_ERR_NULL_ARG;
+    if (p->dtype != GSA_BF16) return GSA_ERR_BAD_DTYPE;
+    if (p->flags) return GSA_ERR_BAD_FLAGS;
+    long c = kv->num_chunks;
+    for (int l = 0; l < L; ++l) {
+        if (lv[l].fanout < 1 || lv[l].top_k < 0 || lv[l].top_k > kMaxTopK) return GSA_ERR_BAD_SHAPE;
+        c /= lv[l].fanout;
+        if (lv[l].max_meta < c || lv[l].max_meta < 1) return GSA_ERR_BAD_SHAPE;
+        if ((long)p->batch * p->num_kv_heads * (long)lv[l].max_meta * p->head_dim > (1L << 50))
+            return GSA_ERR_BAD_SHAPE;
+    }
+    return GSA_OK;
+}
+
+void make_lv_plan(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* lv, int L, LvPlan& pl) {
+    memset(&pl, 0, sizeof(pl));
+    Plan base;
+    make_plan(p, kv, nullptr, base);  // shapes and scalars of the flat call
+    gsa::LvArgs& A = pl.A;
+    A.a = base.a;
+    A.L = L;
+    const long units = (long)A.a.B * A.a.Hkv, C = kv->chunk_size;
+    long cnt[gsa::kMaxLevels + 1];
+    cnt[0] = kv->num_chunks;
+    A.topk[0] = p->top_k;
+    for (int l = 1; l <= L; ++l) {
+        cnt[l] = cnt[l - 1] / lv[l - 1].fanout;
+        A.lk[l] = lv[l - 1].k_meta;
+        A.lv[l] = lv[l - 1].v_meta;
+        A.maxe[l] = lv[l - 1].max_meta;
+        A.fan[l] = lv[l - 1].fanout;
+        A.topk[l] = lv[l - 1].top_k;
+    }
+    // candidates of level l-1: the kept entries' children plus fewer than R_l past the last group
+    long cand_max = 0, cand[gsa::kMaxLevels + 1];
+    for (int l = 1; l <= L; ++l) {
+        const long kept = A.topk[l] < cnt[l] ? A.topk[l] : cnt[l];
+        cand[l - 1] = kept * A.fan[l] + A.fan[l] - 1;
+        if (cand[l - 1] > cand_max) cand_max = cand[l - 1];
+    }
+    const long top = cnt[L];
+    A.cap = (int)(top > cand_max ? top : cand_max);
+    if (A.cap < 1) A.cap = 1;
+    const long c0 = L == 0 ? cnt[0] : cand[0];
+    long f = (A.topk[0] < c0 ? A.topk[0] : c0) * (C + 1) + (C - 1);
+    if (L >= 1) f += A.fan[1] - 1;
+    for (int l = 1; l < L; ++l) f += (A.topk[l] < cnt[l] ? A.topk[l] : cnt[l]) + A.fan[l + 1] - 1;
+    A.fcap = (int)(f > 1 ? f : 1);
+    auto splits = [](long rows) { return (int)(rows > 0 ? (rows + 127) / 128 : 1); };
+    A.S_top = splits(top);
+    A.S_cand = splits(cand_max);
+    A.S_fin = splits(A.fcap);
+    A.NS = A.S_top + A.S_fin;
+    size_t off = sizeof(unsigned) * kCtlWords;  // the control block (unused here)
+    pl.off_keys = off;  off += align_up(sizeof(float) * units * A.cap);
+    for (int i = 0; i < 2; ++i) {
+        pl.off_cid[i] = off;   off += align_up(sizeof(int32_t) * units * A.cap);
+        pl.off_desc[i] = off;  off += align_up(sizeof(int64_t) * units * A.cap);
+        pl.off_ncand[i] = off; off += align_up(sizeof(int32_t) * units);
+    }
+    pl.off_fdesc = off; off += align_up(sizeof(int64_t) * units * A.fcap);
+    pl.off_nfin = off;  off += align_up(sizeof(int32_t) * units);
+    for (int l = 0; l <= L; ++l) {
+        pl.off_sel[l] = off;
+        off += align_up(sizeof(int32_t) * units * (A.topk[l] > 0 ? A.topk[l] : 1));
+    }
+    pl.off_ml = off;  off += align_up(sizeof(float) * 2 * units * A.NS * A.a.G);
+    pl.off_acc = off; off += align_up(sizeof(float) * units * A.NS * A.a.G * A.a.D);
+    pl.total = off;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* levels,
+                           int32_t num_levels) {
+    if (check_params(p, kv) != GSA_OK || check_levels(p, kv, levels, num_levels) != GSA_OK) return 0;
+    LvPlan pl;
+    make_lv_plan(p, kv, levels, num_levels, pl);
+    return pl.total;
+}
+
+gsa_status_t mgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* levels,
+                         int32_t num_levels, const void* q, void* out, int32_t* const* sel,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    gsa_status_t s = check_params(p, kv);
+    if (s != GSA_OK) return s;
+    if ((s = check_levels(p, kv, levels, num_levels)) != GSA_OK) return s;
+    if (!q || !out || !kv->k_cache || !kv->v_cache || !kv->block_table) return GSA_ERR_NULL_ARG;
+    for (int l = 0; l < num_levels; ++l)
+        if (!levels[l].k_meta || !levels[l].v_meta) return GSA_ERR_NULL_ARG;
+    LvPlan pl;
+    make_lv_plan(p, kv, levels, num_levels, pl);
+    if (!workspace) return GSA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace) % kAlign || workspace_bytes < pl.total) return GSA_ERR_WORKSPACE;
+    if ((s = check_device()) != GSA_OK) return s;
+    gsa::LvArgs& A = pl.A;
+    char* ws = (char*)workspace;
+    A.a.q = q;
+    A.a.kc = kv->k_cache;
+    A.a.vc = kv->v_cache;
+    A.a.bt = kv->block_table;
+    A.a.seq_lens = kv->seq_lens;
+    A.a.out = out;
+    A.a.part_ml = (float2*)(ws + pl.off_ml);
+    A.a.part_acc = (float*)(ws + pl.off_acc);
+    A.keys = (float*)(ws + pl.off_keys);
+    for (int i = 0; i < 2; ++i) {
+        A.cid[i] = (int32_t*)(ws + pl.off_cid[i]);
+        A.desc[i] = (int64_t*)(ws + pl.off_desc[i]);
+        A.ncand[i] = (int32_t*)(ws + pl.off_ncand[i]);
+    }
+    A.fdesc = (int64_t*)(ws + pl.off_fdesc);
+    A.nfin = (int32_t*)(ws + pl.off_nfin);
+    for (int l = 0; l <= num_levels; ++l) {
+        A.sel[l] = (int32_t*)(ws + pl.off_sel[l]);
+        A.usel[l] = sel ? sel[l] : nullptr;
+    }
+    GSA_LAUNCH(gsa::launch_levels(A, (hipStream_t)stream));
+    return GSA_OK;
+}
 
 size_t gsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv) {
     if (check_params(p, kv) != GSA_OK) return 0;

@@ -284,3 +284,69 @@ def check_hgsa(inp, gpu_res, units=None, top_k=None, top_k_meta=None):
         assert_close(out[b, g * G:(g + 1) * G], e_out[b, g * G:(g + 1) * G], wl.dtype,
                      f"unit {(b, g)}")
     return differ
+
+
+def run_gpu_m(inp, levels, top_k=None):
+    """mgsa_decode through the C ABI with the checked workspace.  levels:
+    [(k, v, fanout, top_k)] on the device.  Returns (out, sels[l] numpy)."""
+    wl = inp.wl
+    k0 = wl.top_k if top_k is None else top_k
+    B, Hkv = wl.batch, wl.num_kv_heads
+    dev = inp.q.device
+    sels = [torch.full((B, Hkv, max(k, 0)), -7, dtype=torch.int32, device=dev)
+            for k in [k0] + [t for _, _, _, t in levels]]
+    p = gsa.make_params(inp.q, Hkv, k0)
+    kv = gsa.make_kv(inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens, wl.num_chunks,
+                     wl.chunk_size, wl.page_chunks)
+    ws = checked_workspace(gsa.mgsa_workspace_size(p, kv, gsa.make_levels(levels), len(levels)), dev)
+    out = gsa.mgsa_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.seq_lens, levels,
+                          num_chunks=wl.num_chunks, chunk_size=wl.chunk_size,
+                          page_chunks=wl.page_chunks, top_k=k0, sel=sels, ws=ws)
+    torch.cuda.synchronize()
+    check_control(ws, f"mgsa_decode {wl.name}")
+    return out.float().cpu().numpy(), [s.cpu().numpy() for s in sels]
+
+
+def check_mgsa(inp, levels, gpu_res, top_k=None, units=None):
+    """The hierarchy of any depth: the gap rule at every level (candidates: all
+    top-level entries, below them the children of the GPU's kept entries one
+    level up plus the entries past the level's last complete group), outputs
+    against the oracle run with the GPU's selections at every level.
+    Returns the number of units with a differing set at some level."""
+    wl = inp.wl
+    out, sels = gpu_res
+    k0 = wl.top_k if top_k is None else top_k
+    G, C = wl.group, wl.chunk_size
+    L = len(levels)
+    cpu = _cpu(inp)
+    lv = [(U.np_raw(k), U.np_raw(v), R, t) for k, v, R, t in levels]
+    cfg = U.cfg_of(cpu, top_k=k0)
+    args = (U.np_raw(cpu.q), U.np_raw(cpu.k_cache), U.np_raw(cpu.v_cache),
+            U.np_raw(cpu.block_table), U.np_raw(cpu.seq_lens))
+    import oracle
+    _, _, okeys = oracle.mgsa_decode(cfg, *args, lv)
+    n_all, _ = U.shapes(cpu)
+    tops = [k0] + [t for _, _, _, t in levels]
+    Rs = [None] + [R for _, _, R, _ in levels]
+    units = _all_units(wl, units)
+    differ = 0
+    for b, g in units:
+        cnt = [int(n_all[b])]
+        for R in Rs[1:]:
+            cnt.append(cnt[-1] // R)
+        cand = np.arange(cnt[L])
+        same = True
+        for l in range(L, -1, -1):
+            same &= check_set(sels[l][b, g], okeys[l][b, g, cand], tops[l], ids=cand)
+            if l > 0:
+                kept = [int(r) for r in sels[l][b, g] if r >= 0]
+                R = Rs[l]
+                cand = np.array([r * R + j for r in kept for j in range(R)] +
+                                list(range(cnt[l] * R, cnt[l - 1])), np.int64)
+        differ += not same
+    e_out, _, _ = oracle.mgsa_decode(cfg, *args, lv,
+                                     ext=[np.ascontiguousarray(s, np.int32) for s in sels])
+    for b, g in units:
+        assert_close(out[b, g * G:(g + 1) * G], e_out[b, g * G:(g + 1) * G], wl.dtype,
+                     f"unit {(b, g)}")
+    return differ

@@ -39,8 +39,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gsa_workspace_size", "hgsa_workspace_size", "gsa_decode", "hgsa_decode",
-        "gsa_decode_noalloc", "gsa_workspace_status", "gsa_workspace_reset",
-        "gsa_status_string", "gsa_version"])
+        "gsa_decode_noalloc", "mgsa_workspace_size", "mgsa_decode", "gsa_workspace_status",
+        "gsa_workspace_reset", "gsa_status_string", "gsa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -199,6 +199,43 @@ def test_noalloc_validation(lib):
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible")
 def test_noalloc_without_device_reports_device_error(lib):
     assert call_na(lib, params(), kvs()) == 6
+
+
+def lvl(**kw):
+    d = dict(k_meta=FAKE, v_meta=FAKE, max_meta=16, fanout=4, top_k=2)
+    d.update(kw)
+    return gsa.GsaLevel(**d)
+
+
+def call_m(lib, p, kv, levels, n=None, ws_bytes=1 << 30):
+    arr = (gsa.GsaLevel * max(1, len(levels)))(*levels)
+    return lib.mgsa_decode(ctypes.byref(p), ctypes.byref(kv), arr, len(levels) if n is None else n,
+                           ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None,
+                           ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def test_mgsa_validation(lib):
+    """The hierarchy of any depth: level count, fanouts, capacities, dtype and
+    flags are checked before anything is enqueued."""
+    p, kv = params(), kvs()   # 64 chunks: 16 entries at fanout 4, 4 at 4 x 4
+    two = [lvl(), lvl(max_meta=4)]
+    arr = (gsa.GsaLevel * 2)(*two)
+    need = lib.mgsa_workspace_size(ctypes.byref(p), ctypes.byref(kv), arr, 2)
+    assert need > gsa.WORKSPACE_CONTROL_BYTES and need % 256 == 0
+    assert lib.mgsa_workspace_size(ctypes.byref(p), ctypes.byref(kv), None, 0) > 0
+    assert call_m(lib, p, kv, two, n=9) == 2                           # > GSA_MAX_LEVELS
+    assert call_m(lib, p, kv, two, n=-1) == 2
+    assert call_m(lib, p, kv, [lvl(fanout=0)]) == 2
+    assert call_m(lib, p, kv, [lvl(top_k=-1)]) == 2
+    assert call_m(lib, p, kv, [lvl(), lvl(max_meta=3)]) == 2           # level 2 holds 4
+    assert call_m(lib, p, kv, [lvl(max_meta=15)]) == 2
+    assert call_m(lib, params(dtype=gsa.GSA_F32), kv, two) == 3
+    assert call_m(lib, params(flags=gsa.GSA_SET_SELECTED_GISTS), kv, two) == 4
+    assert call_m(lib, p, kv, [lvl(k_meta=0)]) == 1
+    assert lib.mgsa_decode(ctypes.byref(p), ctypes.byref(kv), None, 1, ctypes.c_void_p(FAKE),
+                           ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), 1 << 30, None) == 1
+    assert call_m(lib, p, kv, two, ws_bytes=need - 1) == 5
+    assert call_m(lib, params(batch=0), kv, two) == 2
 
 
 def test_workspace_status_and_reset_validation(lib):
