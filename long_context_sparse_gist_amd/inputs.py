@@ -109,6 +109,28 @@ WORKLOADS = [TINY_F32, LLAMA1B_32K, QWEN7B_128K, MULTIDOC_120K, HGSA_1M]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
+@dataclasses.dataclass(frozen=True)
+class Hierarchy:
+    """A decode shape with meta-gist levels above the gists: fanouts and kept
+    entries per level, level 1 first (the gist level keeps wl.top_k)."""
+
+    wl: Workload
+    fanouts: tuple
+    tops: tuple
+
+    @property
+    def name(self) -> str:
+        return self.wl.name
+
+
+# The 1M-token H-GSA shape with a third level: 4096 level-1 entries under 256
+# level-2 entries; 16 kept at the top, 32 below, 64 chunks unfolded.
+MGSA_1M = Hierarchy(Workload("mgsa-1m-c16-r16x16", BF16, 4, 32, 8, 128, 16, 65536, 64, 16,
+                             plant="align", plant_count=16), (16, 16), (32, 16))
+HIERARCHIES = [MGSA_1M]
+HIER_BY_NAME = {h.name: h for h in HIERARCHIES}
+
+
 def seed_of(index: int) -> int:
     """Seed of workload `index` in WORKLOADS."""
     return 1000 + index
@@ -286,3 +308,39 @@ def make_levels(inp: GsaInputs, fanouts, seed: int, plant: bool = True) -> list:
         v = torch.randn(B, Hkv, max(n, 1), d, generator=g, device=dev, dtype=torch.float32)
         levels.append((x.to(tdt), v.to(tdt)))
     return levels
+
+
+def make_inputs_large(wl: Workload, seed: int, device) -> GsaInputs:
+    """Inputs for long full-length contexts: the layout of make_inputs, with the
+    bf16 caches drawn N(0, 1) in place (no fp32 copy of a whole sequence) from
+    a generator seeded with `seed` (caches, then q, then planted positions and
+    their noise), pages shuffled, and the planted chunks' gist keys aligned
+    with the group's summed query as in make_inputs."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    B, Hq, Hkv, d, C = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.chunk_size
+    tdt = _TORCH_DTYPE[wl.dtype]
+    spp, max_pages = wl.slots_per_page, wl.max_pages
+    num_pages = B * max_pages
+    k_cache = torch.empty(num_pages, Hkv, spp, d, dtype=tdt, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    for cache in (k_cache, v_cache):
+        for p0 in range(0, num_pages, 4096):
+            cache[p0:p0 + 4096].normal_(generator=g)
+    q = torch.randn(B, Hq, d, generator=g, device=dev, dtype=torch.float32).to(tdt)
+    qdir = group_direction(q.float(), Hkv)
+    block_table = torch.randperm(num_pages, generator=g, device=dev).view(B, max_pages).to(torch.int32)
+    M = wl.num_chunks
+    P = wl.plant_count if wl.plant == "align" else 0
+    planted = torch.stack([torch.randperm(M, generator=g, device=dev)[:P]
+                           for _ in range(B * Hkv)]).view(B, Hkv, -1)
+    if P:
+        slots = planted * (C + 1) + C                                     # [B][Hkv][P]
+        bi = torch.arange(B, device=dev).view(B, 1, 1).expand_as(slots)
+        hi = torch.arange(Hkv, device=dev).view(1, Hkv, 1).expand_as(slots)
+        page = block_table.long()[bi, slots // spp]
+        noise = 0.1 * torch.randn(B, Hkv, P, d, generator=g, device=dev)
+        k_cache[page, hi, slots % spp] = (2.0 * math.sqrt(d) * qdir.unsqueeze(2) + noise).to(tdt)
+    sl = torch.full((B,), M * C, dtype=torch.int32, device=dev)
+    return GsaInputs(wl, q, k_cache, v_cache, block_table, sl, planted)
