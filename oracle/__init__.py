@@ -55,6 +55,9 @@ def load(path: str) -> ctypes.CDLL:
     lib.mgsa_oracle_decode.argtypes = ([ctypes.POINTER(OracleCfg)] + [P] * 5 + [ctypes.c_int] +
                                        [PP, PP, IP, IP, IP, P, PP, PP, PP, ctypes.c_int])
     lib.mgsa_oracle_decode.restype = ctypes.c_int
+    lib.gsa_prefill_oracle.argtypes = [ctypes.POINTER(OracleCfg)] + [P] * 5 + [ctypes.c_int, P,
+                                                                            ctypes.c_int]
+    lib.gsa_prefill_oracle.restype = ctypes.c_int
     lib.gsa_oracle_threads.restype = ctypes.c_int
     return lib
 
@@ -192,3 +195,20 @@ def mgsa_decode(cfg: dict, q, k_cache, v_cache, block_table, seq_lens, levels,
     if rc:
         raise ValueError(f"oracle rejected the configuration (code {rc})")
     return out, sels, keys
+
+
+def prefill(cfg: dict, q, k_cache, v_cache, block_table, q_start, nthreads: int = 0, lib=None):
+    """Multi-query attention under the gist causal mask: q [B][T][Hq][d] are
+    the queries of logical slots q_start[b] .. q_start[b] + T - 1.  Returns
+    out float64 [B][T][Hq][d]."""
+    lib = lib or _load()
+    c = _cfg(cfg)
+    q, k_cache, v_cache = (_data(x, c.dtype) for x in (q, k_cache, v_cache))
+    B, T, Hq, d = q.shape
+    out = np.zeros((B, T, Hq, d), np.float64)
+    rc = lib.gsa_prefill_oracle(ctypes.byref(c), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(_c(block_table, np.int32)), _ptr(_c(q_start, np.int32)), T,
+                                _ptr(out), nthreads)
+    if rc:
+        raise ValueError(f"oracle rejected the configuration (code {rc})")
+    return out

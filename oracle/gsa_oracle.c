@@ -47,6 +47,16 @@
  *              every top-level entry, the kept entries and the past-the-last-
  *              group entries of each level below it, the kept chunks' raw
  *              tokens, the raw tail.  L = 1 is O5, L = 0 is O1-O4.
+ *   O8 prefill the multi-query side: T consecutive slots of the interleaved
+ *              sequence (chunked prefill, or several draft tokens checked at
+ *              once) attend under the gist causal mask (ja page 2.1 item 1; nl
+ *              page "Het Proces", Compressie: a gist sees only its own chunk
+ *              and the gists before it).  Reading for raw tokens, which the
+ *              pages leave open: they see the gists of earlier chunks and the
+ *              slots of their own chunk up to themselves (earlier chunks are
+ *              present only through their gists, which stand in for their raw
+ *              tokens' cache).  Query at slot s in chunk m = s / (C+1): keys =
+ *              gists of chunks m' < m plus slots m*(C+1) .. s.
  *   O6         O3-O5 with the selection supplied by the caller: its ids that
  *              lie in the sequence (chunk ids in [0, n), meta-group ids in
  *              [0, n/R)) in place of the top-k at that level, in any order;
@@ -658,6 +668,63 @@ int mgsa_oracle_decode(const oracle_cfg *c, const void *q, const void *k_cache,
         seq_shape(c, seq_lens, b, &n, &tail);
         mgsa_unit(c, q, k_cache, v_cache, block_table, lv, num_levels, b, g, n, tail,
                   out + ((size_t)b * c->num_q_heads + (size_t)g * G) * d, sel, keys, ext, (size_t)u);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* ---- O8: prefill under the gist causal mask ---------------------------- */
+
+/* q, out: [B][T][Hq][d] (out double).  q_start: [B] logical slot of each
+ * sequence's first query; every query slot q_start[b] + t must lie within the
+ * block-table row.  Returns 0, or 1 null pointer, 2 bad shape, 3 bad dtype. */
+int gsa_prefill_oracle(const oracle_cfg *c, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_table, const int32_t *q_start,
+                       int T, double *out, int nthreads) {
+    if (!c || !q || !k_cache || !v_cache || !block_table || !q_start || !out) return 1;
+    if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 || c->head_dim < 1) return 2;
+    if (c->num_q_heads % c->num_kv_heads || c->chunk_size < 1 || c->page_chunks < 1) return 2;
+    if (c->max_pages < 1 || T < 0) return 2;
+    if (c->dtype != 0 && c->dtype != 1) return 3;
+    long spp = (long)c->page_chunks * (c->chunk_size + 1);
+    for (int b = 0; b < c->batch; b++)
+        if (q_start[b] < 0 || (long)q_start[b] + T > (long)c->max_pages * spp) return 2;
+    int C = c->chunk_size, d = c->head_dim, Hq = c->num_q_heads;
+    int G = Hq / c->num_kv_heads;
+    double tau = tau_of(c);
+    long rows = (long)c->batch * T * Hq;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+#endif
+    for (long i = 0; i < rows; i++) {
+        int h = (int)(i % Hq), t = (int)((i / Hq) % T), b = (int)(i / ((long)Hq * T));
+        seqview sv = {c, k_cache, v_cache, block_table, b, h / G};
+        long s = (long)q_start[b] + t;
+        long m = s / (C + 1);
+        long nk = m + (s - m * (C + 1)) + 1;
+        size_t *krow = (size_t *)malloc(sizeof(size_t) * (size_t)nk);
+        double *z = (double *)malloc(sizeof(double) * (size_t)nk);
+        long j = 0;
+        for (long mp = 0; mp < m; mp++) krow[j++] = slot_base(&sv, mp * (C + 1) + C);
+        for (long sp = m * (C + 1); sp <= s; sp++) krow[j++] = slot_base(&sv, sp);
+        size_t qb = (((size_t)b * T + t) * Hq + h) * d;
+        double mu = -INFINITY;
+        for (j = 0; j < nk; j++) {                     /* pass 1: logits, max */
+            double acc = 0.0;
+            for (int e = 0; e < d; e++) acc += ld(q, qb + e, c->dtype) * ld(k_cache, krow[j] + e, c->dtype);
+            z[j] = tau * acc;
+            if (z[j] > mu) mu = z[j];
+        }
+        double lam = 0.0, *o = out + qb;
+        for (int e = 0; e < d; e++) o[e] = 0.0;
+        for (j = 0; j < nk; j++) {                     /* pass 2: sums */
+            double p = exp(z[j] - mu);
+            lam += p;
+            for (int e = 0; e < d; e++) o[e] += p * ld(v_cache, krow[j] + e, c->dtype);
+        }
+        for (int e = 0; e < d; e++) o[e] /= lam;
+        free(krow); free(z);
     }
     (void)nthreads;
     return 0;

@@ -12,6 +12,7 @@ import oracle
 from tests import _util as U
 from tests import test_oracle_pins as P
 from tests import test_oracle_levels as PL
+from tests import test_oracle_prefill as PP
 from long_context_sparse_gist_amd import inputs as gi
 
 MUTANTS = {
@@ -62,6 +63,15 @@ MUTANTS = {
     "top_level_only_kept_attended": ("if (l == L || in[r] || r >= past)",
                                      "if (in[r] || (l < L && r >= past))"),
     "level_gist_tail_dropped": ("if (L == 0 || is_sel[m] || m >= past0)", "if (L == 0 || is_sel[m])"),
+    "prefill_gist_slot_off_by_one": ("for (long mp = 0; mp < m; mp++) krow[j++] = slot_base(&sv, mp * (C + 1) + C);",
+                                     "for (long mp = 0; mp < m; mp++) krow[j++] = slot_base(&sv, mp * (C + 1) + C - 1);"),
+    "prefill_scale_dropped": ("z[j] = tau * acc;", "z[j] = acc;"),
+    "prefill_wrong_kv_head": ("seqview sv = {c, k_cache, v_cache, block_table, b, h / G};",
+                              "seqview sv = {c, k_cache, v_cache, block_table, b, h % c->num_kv_heads};"),
+    "prefill_v_from_k": ("o[e] += p * ld(v_cache, krow[j] + e, c->dtype);",
+                         "o[e] += p * ld(k_cache, krow[j] + e, c->dtype);"),
+    "prefill_query_slot_shifted": ("long s = (long)q_start[b] + t;",
+                                   "long s = (long)q_start[b] + t - (t > 0);"),
     "meta_gists_not_attended": ("for (int r = 0; r < nm; r++) { T[nT].arr_k = km;",
                                 "for (int r = 0; r < 0; r++) { T[nT].arr_k = km;"),
 }
@@ -103,6 +113,15 @@ def pin_battery():
         out.append((f"lv_ext/{which}", lambda which=which: PL.test_caller_selection_at_a_level(which)))
     for name in sorted(PL.CASES):
         out.append((f"lv_golden/{name}", lambda name=name: PL.test_levels_hand_worked(name)))
+    for wl in (PP.SMALL, PP.SMALL_F32):
+        for start in ("chunk", "mid", "tail"):
+            out.append((f"pf_dense/{wl.name}/{start}",
+                        lambda wl=wl, start=start: PP.test_prefill_matches_masked_dense(wl, start)))
+    out += [("pf_decode", PP.test_prefill_tail_query_is_decode_with_no_chunk_unfolded),
+            ("pf_first", PP.test_prefill_first_slot_and_first_gist),
+            ("pf_pages", PP.test_prefill_page_order_invariant)]
+    for name in sorted(PP.CASES):
+        out.append((f"pf_golden/{name}", lambda name=name: PP.test_prefill_hand_worked(name)))
     return out
 
 
