@@ -263,6 +263,26 @@ gsa_status_t mgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_le
                          int32_t num_levels, const void* q, void* out, int32_t* const* sel,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* The multi-query side: num_queries consecutive slots of each sequence's
+ * interleaved layout attend under the gist causal mask (ja page 2.1 item 1:
+ * gists trained under a causal mask to summarise their chunk; nl page, "Het
+ * Proces", Compressie: a gist sees only its own chunk and the gists before
+ * it).  The query at slot s of chunk m = s / (C+1) attends to the gists of
+ * chunks before m and to the slots of chunk m up to and including s (raw
+ * tokens of earlier chunks are present only through their gists).  This is
+ * the step that builds the interleaved cache (chunked prefill, one chunk of
+ * slots at a time) and the one that checks several draft tokens at once; the
+ * caller writes the queries' own K/V rows into the cache first.
+ *   q_start : int32 device [batch], first query slot of each sequence, with
+ *             q_start[b] + num_queries <= max_pages * page_chunks * (C+1)
+ *             (clamped into that range)
+ *   q, out  : [batch][num_queries][num_q_heads][head_dim], bf16
+ * Uses kv's caches, block table, chunk size and page geometry; seq_lens,
+ * top_k and num_chunks (beyond validation) are not used.  bf16 only, flags 0.
+ * No workspace: the kernel keeps every query's state on chip. */
+gsa_status_t gsa_prefill(const gsa_params_t* p, const gsa_kv_t* kv, const int32_t* q_start,
+                         int32_t num_queries, const void* q, void* out, void* stream);
+
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status_t s);
 

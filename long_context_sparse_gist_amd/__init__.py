@@ -6,7 +6,7 @@ is loaded on first use and a missing or unloadable library raises; there is no
 fallback path.
 
 Names mirror the C ABI in include/gsa.h: gsa_decode, hgsa_decode,
-gsa_decode_noalloc, mgsa_decode, gsa_workspace_size, hgsa_workspace_size,
+gsa_decode_noalloc, mgsa_decode, gsa_prefill, gsa_workspace_size, hgsa_workspace_size,
 mgsa_workspace_size, gsa_workspace_status, gsa_workspace_reset, gsa_status_string, gsa_version.
 
 Streams: a call runs on `stream` (default: the current stream of q's
@@ -114,6 +114,9 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(GsaLevel), ctypes.c_int32, P, P,
                                   ctypes.POINTER(ctypes.c_void_p), P, ctypes.c_size_t, P]
         L.mgsa_decode.restype = ctypes.c_int
+        L.gsa_prefill.argtypes = [ctypes.POINTER(GsaParams), ctypes.POINTER(GsaKV), P,
+                                  ctypes.c_int32, P, P, P]
+        L.gsa_prefill.restype = ctypes.c_int
         L.gsa_workspace_status.argtypes = [P, ctypes.c_size_t, P]
         L.gsa_workspace_status.restype = ctypes.c_int
         L.gsa_workspace_reset.argtypes = [P, ctypes.c_size_t, P]
@@ -437,5 +440,42 @@ def mgsa_decode(q, k_cache, v_cache, block_table, seq_lens, levels, *, num_chunk
                                num_chunks=num_chunks, chunk_size=chunk_size,
                                page_chunks=page_chunks, top_k=top_k, sm_scale=sm_scale, out=out,
                                sel=sel, ws=ws, stream=stream)
+    call()
+    return call.out
+
+
+def prepare_gsa_prefill(q, k_cache, v_cache, block_table, q_start, *, chunk_size: int,
+                        page_chunks: int, sm_scale: float = 0.0, out=None,
+                        stream=None) -> PreparedCall:
+    """gsa_prefill's arguments marshalled into a PreparedCall.  q [B][T][Hq][d]
+    are the queries of slots q_start[b] .. q_start[b] + T - 1 (q_start: int32
+    device [B])."""
+    for t in (q, k_cache, v_cache, block_table, q_start):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, caches, block_table and q_start must be contiguous device tensors")
+    if block_table.dtype != torch.int32 or q_start.dtype != torch.int32:
+        raise TypeError("block_table and q_start must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    B, T, Hq, d = q.shape
+    p = GsaParams(B, Hq, k_cache.shape[1], d, 0, sm_scale, _dtype_code(q), 0, 0.0)
+    cap_chunks = block_table.shape[1] * page_chunks
+    kv = make_kv(k_cache, v_cache, block_table, None, cap_chunks, chunk_size, page_chunks)
+    if out is None:
+        out = _alloc_out(q, stream)
+    args = (ctypes.byref(p), ctypes.byref(kv), _ptr(q_start), T, _ptr(q), _ptr(out),
+            _stream_ptr(stream, q.device))
+    call = PreparedCall(lib().gsa_prefill, args,
+                        (p, kv, q, k_cache, v_cache, block_table, q_start, out), "gsa_prefill")
+    call.out = out
+    return call
+
+
+def gsa_prefill(q, k_cache, v_cache, block_table, q_start, *, chunk_size: int, page_chunks: int,
+                sm_scale: float = 0.0, out=None, stream=None):
+    """Attention of T consecutive slots per sequence under the gist causal mask
+    (see gsa_prefill in include/gsa.h).  Returns out [B][T][Hq][d]."""
+    call = prepare_gsa_prefill(q, k_cache, v_cache, block_table, q_start, chunk_size=chunk_size,
+                               page_chunks=page_chunks, sm_scale=sm_scale, out=out, stream=stream)
     call()
     return call.out

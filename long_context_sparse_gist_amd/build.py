@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgsa.so")
 SOURCES = ["api.hip", "fused.hip", "attn_mfma.hip", "attn_portable.hip", "select.hip",
-           "merge.hip", "levels.hip"]
+           "merge.hip", "levels.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -545,6 +545,26 @@ gsa_status_t hgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_m
     return GSA_OK;
 }
 
+gsa_status_t gsa_prefill(const gsa_params_t* p, const gsa_kv_t* kv, const int32_t* q_start,
+                         int32_t num_queries, const void* q, void* out, void* stream) {
+    gsa_status_t s = check_params(p, kv);
+    if (s != GSA_OK) return s;
+    if (!q || !out || !q_start || !kv->k_cache || !kv->v_cache || !kv->block_table)
+        return GSA_ERR_NULL_ARG;
+    if (p->dtype != GSA_BF16) return GSA_ERR_BAD_DTYPE;
+    if (p->flags) return GSA_ERR_BAD_FLAGS;
+    const long spp = (long)kv->page_chunks * (kv->chunk_size + 1);
+    if (num_queries < 0 || (long)num_queries > (long)kv->max_pages * spp) return GSA_ERR_BAD_SHAPE;
+    if ((long)num_queries * p->num_q_heads > (1L << 30)) return GSA_ERR_BAD_SHAPE;
+    if ((s = check_device()) != GSA_OK) return s;
+    const float tau = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / sqrt((double)p->head_dim));
+    GSA_LAUNCH(gsa::launch_prefill(q, out, kv->k_cache, kv->v_cache, kv->block_table, q_start,
+                                   p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim,
+                                   kv->chunk_size, num_queries, (int)spp, kv->max_pages, tau,
+                                   (hipStream_t)stream));
+    return GSA_OK;
+}
+
 gsa_status_t gsa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
     if (!workspace) return GSA_ERR_NULL_ARG;
     if (((uintptr_t)workspace) % kAlign || workspace_bytes < GSA_WORKSPACE_CONTROL_BYTES)

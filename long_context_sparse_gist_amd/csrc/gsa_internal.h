@@ -193,5 +193,8 @@ hipError_t launch_probs_keys(const Args& a, hipStream_t st);
 constexpr int kTopPMaxK = 2048;  // largest top_k (the cap) with top-p selection
 hipError_t launch_merge(const Args& a, int hier, hipStream_t st);
 hipError_t launch_cand_keys(const Args& a, hipStream_t st);
+hipError_t launch_prefill(const void* q, void* out, const void* kc, const void* vc, const int32_t* bt,
+                          const int32_t* q_start, int B, int Hq, int Hkv, int D, int C, int T, int spp,
+                          int max_pages, float tau, hipStream_t st);
 
 }  // namespace gsa

@@ -1,0 +1,267 @@
+// The multi-query side of gist sparse attention: T consecutive slots of the
+// interleaved sequence (a chunked-prefill step, or several draft tokens
+// checked at once) attend under the gist causal mask ("Forget, Then Recall",
+// ja page section 2.1 item 1; nl page "Het Proces", Compressie): the query at
+// slot s of chunk m = s / (C+1) sees the gists of chunks m' < m and the slots
+// of its own chunk up to s.  The caller has written the queries' own K/V rows
+// into the paged cache.
+//
+// Many queries share the same gist rows, so this is a dense contraction and
+// runs on MFMA.  A workgroup owns 128 columns of one (batch, kv-head) unit --
+// column j is query t = j / G, head j % G of the GQA group -- as 8 blocks of 16
+// (two per wavefront).  It streams key blocks of 32 rows: first the gists of
+// every chunk up to the last query's, then the slots of the chunks its
+// queries lie in.  Each block's K and V rows go from global memory straight
+// into LDS (global_load_lds, the four wavefronts sharing the loads and the
+// tiles; double-buffered, so block i+1 loads while block i is used); every
+// wavefront reads its K operand from the K tile (rows 16-byte-swizzled so the
+// 16 rows one instruction reads hit different banks) and its V operand
+// transposed from the V tile.  Scores S^T[key][column] = K.Q^T, the mask per
+// (key, column), online softmax per column in the exp2 domain, P (bf16) . V
+// accumulated in fp32, and the output written once at the end: no partials,
+// no workspace.
+#include "gsa_mfma_core.h"
+
+namespace gsa {
+
+// Kernel arguments of one prefill launch.
+struct PrefillArgs {
+    const void* q;        // [B][T][Hq][D]
+    void* out;            // [B][T][Hq][D]
+    const void* kc;
+    const void* vc;
+    const int32_t* bt;    // [B][max_pages]
+    const int32_t* q_start;  // [B] first query slot
+    int B, Hq, Hkv, G, C, T, spp, max_pages, ncols;  // ncols = T * G
+    float tau_log2e;
+};
+
+namespace {
+
+constexpr int kPThreads = 256;
+constexpr int kNCB = 2;                   // 16-column blocks per wavefront
+constexpr int kPCols = 4 * kNCB * 16;     // columns per workgroup
+constexpr int kPBtLds = 7936;             // block-table entries kept in LDS (64 KB in all at d = 128)
+
+// Wait for this wavefront's outstanding memory operations (global loads into
+// LDS and LDS reads).
+__device__ inline void wait_mem() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+
+template <int D>
+struct PTiles {
+    static constexpr int TILE = 32 * D * 2;
+    static constexpr int bytes(int max_pages) {
+        return 4 * TILE + 4 * (max_pages <= kPBtLds ? max_pages : 0);
+    }
+};
+
+// Issue this wavefront's share of one key block's tile loads (1 KB per
+// instruction: 64 lanes x 16 bytes into consecutive LDS).  o0 / o1: element
+// offsets of the block's rows lane % 16 and 16 + lane % 16.  K: position p of
+// row r holds the row's 16-byte chunk p ^ (r mod CPR); V: the layout
+// WaveAttnL::pv reads.
+template <int D>
+__device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, size_t o1, unsigned char* kt,
+                                            unsigned char* vt, int w, int lane) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int qq = 0; qq < CPR / 2; ++qq) {
+        if ((qq & 3) != w) continue;
+        const int f = 64 * qq + lane, r = f / CPR, p = f % CPR;
+        const size_t src = (64 * qq) / CPR < 16 ? o0 : o1;  // uniform per qq
+        const unsigned lo = __shfl((unsigned)src, r % 16), hi = __shfl((unsigned)(src >> 32), r % 16);
+        const size_t ro = ((size_t)hi << 32) | lo;
+        __builtin_amdgcn_global_load_lds((const __bf16*)a.kc + ro + 8 * (p ^ (r % CPR)),
+                                         (lds_void_t*)(kt + 1024 * qq), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __bf16*)a.vc + ro + 8 * (p ^ WaveAttnL<D>::swz(r)),
+                                         (lds_void_t*)(vt + 1024 * qq), 16, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int KK = D / 32, DB = D / 16, CPR = D / 8, TILE = PTiles<D>::TILE;
+    unsigned char* ktile = smem;             // 2 buffers
+    unsigned char* vtile = smem + 2 * TILE;  // 2 buffers
+    int* btl = (int*)(smem + 4 * TILE);
+    const int u = blockIdx.y, b = u / a.Hkv, g = u - b * a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int G = a.G, C = a.C, T = a.T;
+    // the queries' slots, clamped into the block-table row
+    const int cap = a.max_pages * a.spp;
+    const int s0 = min(max(a.q_start[b], 0), max(cap - T, 0));
+    const int jw = blockIdx.x * kPCols;
+    const int t_lo = jw / G, t_hi = min(T - 1, (jw + kPCols - 1) / G);
+    const int m_lo = (s0 + t_lo) / (C + 1), m_hi = (s0 + t_hi) / (C + 1);
+    const int s_hi = s0 + t_hi, l0 = m_lo * (C + 1);
+    const bool bt_lds = a.max_pages <= kPBtLds;
+    const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
+    if (bt_lds)
+        for (int i = tid; i < a.max_pages; i += kPThreads) btl[i] = btrow[i];
+    __syncthreads();
+    auto slot_off = [&](int slot) -> size_t {
+        const int p = slot / a.spp;
+        const int phys = bt_lds ? btl[p] : btrow[p];
+        return (((size_t)phys * a.Hkv + g) * a.spp + (slot - p * a.spp)) * (size_t)D;
+    };
+
+    // this lane's column (lr) of each of the wavefront's column blocks
+    WaveAttnL<D> wa[kNCB];
+    int colm[kNCB], cols[kNCB];
+    bool colv[kNCB];
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) {
+        const int j = jw + (w * kNCB + cb) * 16 + lr;
+        colv[cb] = j < a.ncols;
+        const int t = colv[cb] ? j / G : 0, h = j - (j / G) * G;
+        cols[cb] = s0 + t;
+        colm[cb] = cols[cb] / (C + 1);
+        const __bf16* qp = (const __bf16*)a.q + (((size_t)b * T + t) * a.Hq + (size_t)g * G + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (colv[cb]) {
+                wa[cb].qB[kk] = *(const bf16x8_t*)(qp + 32 * kk + 8 * lg);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wa[cb].qB[kk][i] = (__bf16)0.0f;
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) wa[cb].o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        wa[cb].m = -INFINITY;
+        wa[cb].l = 0.f;
+    }
+
+    // key blocks: the gists of chunks [0, m_hi), then the slots [l0, s_hi]
+    const int nA = (m_hi + 31) / 32;
+    const int nblk = nA + (s_hi - l0 + 1 + 31) / 32;
+    // element offsets of block i's rows lr and 16 + lr (a row past the end
+    // repeats the last real one: it is masked)
+    auto rows_of = [&](int i, size_t& o0, size_t& o1) {
+        int s[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int k = 32 * i + 16 * hh + lr;
+            s[hh] = i < nA ? min(k, m_hi - 1) * (C + 1) + C : min(l0 + k - 32 * nA, s_hi);
+        }
+        o0 = slot_off(s[0]);
+        o1 = slot_off(s[1]);
+    };
+    // every wavefront issues its share of block i's tile loads
+    auto issue = [&](int i, int buf) {
+        size_t o0, o1;
+        rows_of(i, o0, o1);
+        issue_tiles<D>(a, o0, o1, ktile + buf * TILE, vtile + buf * TILE, w, lane);
+    };
+    const float tl = a.tau_log2e;
+    if (nblk > 0) issue(0, 0);
+    wait_mem();
+    for (int i = 0; i < nblk; ++i) {
+        __syncthreads();  // block i's tiles are in LDS; buffer (i+1)&1 is free
+        if (i + 1 < nblk) issue(i + 1, (i + 1) & 1);
+        const unsigned char* kt = ktile + (i & 1) * TILE;
+        const unsigned char* vt = vtile + (i & 1) * TILE;
+        bf16x8_t kA[2][KK];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int r = 16 * t + lr;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kA[t][kk] = *(const bf16x8_t*)(kt + r * 2 * D + 16 * ((4 * kk + lg) ^ (r % CPR)));
+        }
+        const bool gist_blk = i < nA;
+        const int kbase = gist_blk ? 32 * i : l0 + 32 * (i - nA);
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb) {
+            f32x4_t sc[2];
+            wa[cb].scores(kA, sc);
+            // key 16t + 4lg + r against column lr
+            bool ok[2][4];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kbase + 16 * t + 4 * lg + r;
+                    ok[t][r] = colv[cb] && (gist_blk ? key < colm[cb]
+                                                     : key <= cols[cb] && key >= colm[cb] * (C + 1));
+                    if (ok[t][r]) bm = fmaxf(bm, sc[t][r]);
+                }
+            bm = rows4_max(bm);
+            const float mold = wa[cb].m, mnew = fmaxf(mold, bm);
+            const float alpha = mnew == -INFINITY ? 1.f : exp2f((mold - mnew) * tl);
+            const float mb = mnew * tl;
+            bf16x8_t P;
+            float ls = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const __bf16 pb = (__bf16)(ok[t][r] ? exp2f(sc[t][r] * tl - mb) : 0.f);
+                    ls += (float)pb;
+                    P[4 * t + r] = pb;
+                }
+            wa[cb].l = wa[cb].l * alpha + ls;
+            wa[cb].m = mnew;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) wa[cb].o[db][r] *= ar;
+            }
+            wa[cb].pv(P, vt);
+        }
+        // this block's LDS reads are done and block i+1's tiles have landed
+        wait_mem();
+    }
+    // out[column 4lg + r][16db + lr] = o[db][r] / l(column 4lg + r)
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) {
+        const float lcol = rows4_sum(wa[cb].l);  // lane lr: column lr's sum
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float L = __shfl(lcol, 4 * lg + r);
+            const int j = jw + (w * kNCB + cb) * 16 + 4 * lg + r;
+            if (j >= a.ncols) continue;
+            const int t = j / G, h = j - t * G;
+            __bf16* op = (__bf16*)a.out + (((size_t)b * T + t) * a.Hq + (size_t)g * G + h) * D;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) op[16 * db + lr] = (__bf16)(wa[cb].o[db][r] * inv);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const void* q, void* out, const void* kc, const void* vc, const int32_t* bt,
+                          const int32_t* q_start, int B, int Hq, int Hkv, int D, int C, int T, int spp,
+                          int max_pages, float tau, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    PrefillArgs a;
+    a.q = q;
+    a.out = out;
+    a.kc = kc;
+    a.vc = vc;
+    a.bt = bt;
+    a.q_start = q_start;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.C = C;
+    a.T = T;
+    a.spp = spp;
+    a.max_pages = max_pages;
+    a.ncols = T * a.G;
+    a.tau_log2e = (float)((double)tau * 1.4426950408889634);
+    dim3 grid((a.ncols + kPCols - 1) / kPCols, B * Hkv);
+    if (D == 64)
+        hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kPThreads), PTiles<64>::bytes(max_pages), st, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(kPThreads), PTiles<128>::bytes(max_pages), st, a);
+    return hipGetLastError();
+}
+
+}  // namespace gsa

@@ -39,7 +39,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "gsa_workspace_size", "hgsa_workspace_size", "gsa_decode", "hgsa_decode",
-        "gsa_decode_noalloc", "mgsa_workspace_size", "mgsa_decode", "gsa_workspace_status",
+        "gsa_decode_noalloc", "mgsa_workspace_size", "mgsa_decode", "gsa_prefill",
+        "gsa_workspace_status",
         "gsa_workspace_reset", "gsa_status_string", "gsa_version"])
 
 
@@ -236,6 +237,34 @@ def test_mgsa_validation(lib):
                            ctypes.c_void_p(FAKE), None, ctypes.c_void_p(FAKE), 1 << 30, None) == 1
     assert call_m(lib, p, kv, two, ws_bytes=need - 1) == 5
     assert call_m(lib, params(batch=0), kv, two) == 2
+
+
+def call_p(lib, p, kv, T=4, q_start=FAKE, q=FAKE, out=FAKE):
+    return lib.gsa_prefill(ctypes.byref(p), ctypes.byref(kv), ctypes.c_void_p(q_start), T,
+                           ctypes.c_void_p(q), ctypes.c_void_p(out), None)
+
+
+def test_prefill_validation(lib):
+    """gsa_prefill checks shapes, dtype, flags and pointers before anything is
+    enqueued."""
+    p, kv = params(), kvs()
+    for kw, code in BAD_PARAMS:
+        if "top_p" in kw:
+            continue
+        assert call_p(lib, params(**kw), kv) == code
+    assert call_p(lib, params(dtype=gsa.GSA_F32), kv) == 3
+    assert call_p(lib, params(flags=gsa.GSA_SET_SELECTED_GISTS), kv) == 4
+    assert call_p(lib, p, kv, T=-1) == 2
+    assert call_p(lib, p, kv, T=5 * 16 * 17 + 1) == 2    # more queries than the row holds
+    assert call_p(lib, p, kv, q_start=0) == 1
+    assert call_p(lib, p, kv, q=0) == 1
+    assert call_p(lib, p, kv, out=0) == 1
+    assert call_p(lib, p, kvs(k_cache=0)) == 1
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible")
+def test_prefill_without_device_reports_device_error(lib):
+    assert call_p(lib, params(), kvs()) == 6
 
 
 def test_workspace_status_and_reset_validation(lib):
