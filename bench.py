@@ -95,13 +95,88 @@ def alg_bytes_levels(wl: gi.Workload, fanouts, tops) -> int:
     return wl.batch * wl.num_kv_heads * (e * d * rows + 2 * G * d * e)
 
 
+def prefill_flops(wl: gi.Workload, T: int, q_start: int) -> int:
+    """Multiply-add flops of one prefill step: per query head 2*d for the score
+    and 2*d for the weighted value of every key its mask admits (the gists of
+    earlier chunks and its own chunk's slots up to itself)."""
+    C = wl.chunk_size
+    s = np.arange(q_start, q_start + T)
+    keys = s // (C + 1) + s % (C + 1) + 1
+    return int(keys.sum()) * 4 * wl.head_dim * wl.num_q_heads * wl.batch
+
+
+def prefill_bench(args, step, dev):
+    """Time gsa_prefill on the last `step.queries` slots of every sequence
+    (bound: bf16 MFMA; 2.5 PFLOP/s dense peak)."""
+    wl, T = step.wl, step.queries
+    cap = wl.num_chunks * (wl.chunk_size + 1)
+    inp = gi.make_inputs_large(wl, 1500, dev)
+    g = torch.Generator(device=dev).manual_seed(9)
+    q = torch.randn(wl.batch, T, wl.num_q_heads, wl.head_dim, generator=g, device=dev).to(torch.bfloat16)
+    qs = torch.full((wl.batch,), cap - T, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty_like(q)
+    caches = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone())
+                                              for _ in range(max(1, args.copies) - 1)]
+    calls = [gsa.prepare_gsa_prefill(q, k, v, inp.block_table, qs, chunk_size=wl.chunk_size,
+                                     page_chunks=wl.page_chunks, out=out, stream=stream)
+             for k, v in caches]
+    for i in range(args.warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    flops = prefill_flops(wl, T, cap - T)
+    achieved = flops / call_s / 1e12
+    res = {"metric": "GSA prefill query-heads/sec under the gist causal mask (multi-query side)",
+           "value": wl.batch * T * wl.num_q_heads * args.steps / wall, "unit": "query-heads/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": step.name, "batch": wl.batch, "q_heads": wl.num_q_heads,
+                      "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                      "context_tokens": wl.raw_tokens, "chunk_size": wl.chunk_size,
+                      "queries": T, "first_query_slot": cap - T, "cache_copies": len(caches)},
+           "launch_us": call_s * 1e6,
+           "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
+                        "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                        "traffic": None, "flops_per_launch": flops}}
+    if args.cpu_baseline:
+        del calls, caches
+        torch.cuda.empty_cache()
+        import oracle
+        from tests import _util as U
+        cpu_q = q[:, :8].cpu()   # a bounded sample: the first 8 queries of every sequence
+        cfg = U.cfg_of(inp, top_k=0)
+        kc, vc, bt = U.np_raw(inp.k_cache), U.np_raw(inp.v_cache), U.np_raw(inp.block_table)
+        st = np.full(wl.batch, cap - T, np.int32)
+        times = []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            oracle.prefill(cfg, U.np_raw(cpu_q), kc, vc, bt, st)
+            times.append(time.perf_counter() - t1)
+        rows = wl.batch * 8 * wl.num_q_heads
+        res["cpu_baseline"] = {"value": rows / statistics.median(times), "unit": "query-heads/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"the first 8 queries of each sequence ({rows} query "
+                                         f"heads), median of 3 runs, fp64, OpenMP over rows"}
+    print(json.dumps(res), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=gi.QWEN7B_128K.name,
-                    choices=sorted(gi.BY_NAME) + sorted(gi.HIER_BY_NAME))
+                    choices=sorted(gi.BY_NAME) + sorted(gi.HIER_BY_NAME) + sorted(gi.PREFILL_BY_NAME))
     ap.add_argument("--score", default="sum_logits", choices=["sum_logits", "sum_probs"],
                     help="group routing key (flat GSA): sum of the heads' logits, or of their "
                          "softmax probabilities over the gists (multi-launch kernels)")
@@ -257,6 +332,9 @@ def main():
     gsa.lib()
     if args.level_sweep:
         level_sweep(dev)
+        return
+    if args.workload in gi.PREFILL_BY_NAME:
+        prefill_bench(args, gi.PREFILL_BY_NAME[args.workload], dev)
         return
     hier = gi.HIER_BY_NAME.get(args.workload)
     wl = hier.wl if hier is not None else gi.BY_NAME[args.workload]

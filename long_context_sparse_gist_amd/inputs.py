@@ -131,6 +131,27 @@ HIERARCHIES = [MGSA_1M]
 HIER_BY_NAME = {h.name: h for h in HIERARCHIES}
 
 
+@dataclasses.dataclass(frozen=True)
+class PrefillStep:
+    """A multi-query step: the last `queries` slots of full-length sequences
+    of `wl` attend under the gist causal mask."""
+
+    wl: Workload
+    queries: int
+
+    @property
+    def name(self) -> str:
+        return f"{self.wl.name}-t{self.queries}"
+
+
+# A chunked-prefill step of 120 chunks (1920 raw tokens and their 120 gists) at
+# the end of a 128K-token context, Qwen2-7B shape.
+PREFILL_128K = PrefillStep(Workload("prefill-qwen2-7b-128k", BF16, 8, 28, 4, 128, 16, 8192, 0, 16,
+                                    plant="align", plant_count=16), 2040)
+PREFILLS = [PREFILL_128K]
+PREFILL_BY_NAME = {p.name: p for p in PREFILLS}
+
+
 def seed_of(index: int) -> int:
     """Seed of workload `index` in WORKLOADS."""
     return 1000 + index
