@@ -153,10 +153,20 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         pl.S2 = pl.S2 > 0 ? pl.S2 : 1;
         if (pl.hier) pl.Sc = pl.Sc > 0 ? pl.Sc : 1;
     }
+    if (pl.fused && !pl.hier) {
+        // flat GSA: S tasks per unit, the gist slices first (the last of them
+        // selects); every other task streams at most one 32-row block of the
+        // unfolded list per wavefront (4 per task) at full length
+        const long ublocks = (cap2 + 31) / 32;
+        const long need = 1 + (ublocks + 3) / 4;  // the selector does no unfolded block
+        if (need > pl.S1) pl.S1 = (int)need;
+        pl.S2 = 0;
+        TB = 32;
+    }
     a.S1 = pl.S1;
     a.SL = TA;
     a.SR = TB;
-    a.NS = pl.S1 + pl.S2;
+    a.NS = pl.S1 + pl.S2;  // partial slots per unit (flat single launch: one per task)
     pl.sc.units = (int)units;
     pl.sc.S1 = pl.S1;
     pl.sc.S3 = pl.fused && pl.hier ? pl.Sc : 0;

@@ -371,7 +371,8 @@ __device__ inline void select_prefetch(const Args& a, const ListCtx& c, int n, i
 // have completed (at most once; maybe not at all).  pre: the block-table row
 // loaded by select_prefetch.  Slice `own` (the calling one) is not bucket
 // sorted: every thread brings its key (ownk: order key | list index << 32,
-// ownv: present), so that slice is complete among the candidates.
+// ownv: present), so that slice is complete among the candidates.  own < 0:
+// the caller owns no slice (every slice published its sorted keys).
 template <int KIND, typename Drained>
 __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int n, int nA,
                                              const float* keys, unsigned char* smem, SelPre& pre, int own,
@@ -410,7 +411,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
         drain();
-        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)(nA - 1), sc.err);
+        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) {
@@ -1307,6 +1308,350 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
     }
 }
 
+// Flat GSA: task idx of unit u, S = s.S1 tasks per unit.  Tasks idx < nA own
+// a slice of 256 gists each; the last of them, nA - 1, is the unit's selector;
+// every other task is an unfolded worker.
+//   slice     K pass over its gists (routing keys; with the all-gists set also
+//             the blocks' softmax probabilities against their maximum), keys
+//             out and -- but for the selector -- bucket-sorted and published,
+//             counted in (cntA); then its V pass.
+//   selector  keeps its slice's keys in registers and runs the top-k select
+//             over the slices' sorted keys as soon as they are published
+//             (select_fused), which writes the selection and each selected
+//             chunk's first-row offset into the unit's record; then its V pass
+//             and partial, and the merge.
+//   workers   after their V pass (if any), 32-row blocks of the unfolded list
+//             (raw tokens of the selected chunks, raw tail, selected gists of
+//             the selected-gists set): block jb goes to worker wave jb mod 4W
+//             (W = S - 1 workers), spread over the tasks first.  A worker polls
+//             its blocks' row offsets (written by the select, in practice
+//             while the V passes stream), attends them into the same
+//             online-softmax state and publishes one partial (slot idx).
+//   merge     every task publishes its partial (slot idx) and counts in
+//             (cntB); the last R to count in (R = min(4, EJ)) each fold one
+//             R-th of the output's elements from all S partials in slot order
+//             (merge_part) once the count is full, and the last of them to
+//             finish (cntP) returns the unit's record to zero.
+// Waits go one way within a unit (the select waits for its slices' keys, the
+// workers for the select, the mergers for the last task to count in), and
+// only within it.  Tasks are numbered unit by
+// unit and each XCD dispatches its workgroups in id order, so on every XCD the
+// smallest unfinished unit's tasks come before any later unit's: slots held by
+// earlier units free up as those finish, all of its tasks become resident
+// together (a unit's tasks are far fewer than an XCD's slots) and it
+// finishes; by induction every unit does.
+
+// Merge the elements j = jr + R k (k < JS) of unit u's G x D output (element
+// threadIdx.x + j * kThreads) from all S partials, in slot order, and write
+// them to out; every partial is in memory.  A wavefront's elements of one j
+// belong to one head (D is a multiple of 64): lane i takes slot i's (max, sum)
+// of that head, wavefront reductions give the common max and the sum, and the
+// slots' factors reach every lane by readlane -- no LDS and no barrier between
+// the (max, sum) loads and the accumulator loads, which go out together.
+// Slots in groups of 64, each rescaled to the running maximum; within a group
+// NB slots' loads are in flight while the NB before are folded.  The order
+// (hence every bit of the output) does not depend on which task merges.
+template <int D, int JS>
+__device__ __forceinline__ void merge_part(const Args& a, int u, int S, int jr, int R, __bf16* out) {
+    static_assert(D % 64 == 0, "one head per wavefront and j");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int G = a.G, GD = G * D;
+    const size_t base = (size_t)u * a.NS;
+    const __amdgpu_buffer_rsrc_t racc = buf_view(a.part_acc + base * GD, 4u * a.NS * GD);
+    const __amdgpu_buffer_rsrc_t rml = buf_view(a.part_ml + base * G, 8u * a.NS * G);
+    unsigned eo[JS];
+    int hh[JS];
+    float acc[JS], M[JS], L[JS];
+#pragma unroll
+    for (int k = 0; k < JS; ++k) {
+        const int e0 = 64 * w + (jr + R * k) * kThreads;  // the wavefront's first element
+        hh[k] = e0 / D;
+        eo[k] = e0 + lane < GD ? 4u * (unsigned)(e0 + lane) : kBufOut;
+        acc[k] = 0.f;
+        M[k] = -INFINITY;
+        L[k] = 0.f;
+    }
+    constexpr int NB = 32 / JS;  // slots per batch (2 NB divides 64)
+    // a slot past the group or an element past G x D reads 0
+    auto issue = [&](float (&v)[JS][NB], int g0, int ng, int s0) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const unsigned os = s0 + i < ng ? 4u * (unsigned)((g0 + s0 + i) * GD) : kBufOut;
+#pragma unroll
+            for (int k = 0; k < JS; ++k) v[k][i] = ld_dev_buf(racc, eo[k] + os);
+        }
+    };
+    for (int g0 = 0; g0 < S; g0 += 64) {
+        const int ng = min(64, S - g0);
+        float x[JS], y[JS];
+#pragma unroll
+        for (int k = 0; k < JS; ++k) {
+            const bool on = lane < ng && hh[k] < G;
+            const unsigned om = on ? 8u * (unsigned)((g0 + lane) * G + hh[k]) : kBufOut;
+            x[k] = ld_dev_buf(rml, om);
+            y[k] = ld_dev_buf(rml, om + 4u);
+            x[k] = on ? x[k] : -INFINITY;
+        }
+        float va[JS][NB], vb[JS][NB];
+        issue(va, g0, ng, 0);
+        float f[JS];  // this lane's slot factor
+#pragma unroll
+        for (int k = 0; k < JS; ++k) {
+            float mx = x[k];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            const float Mn = fmaxf(M[k], mx);
+            f[k] = x[k] == -INFINITY ? 0.f : exp2f(x[k] - Mn);
+            const float r = M[k] == -INFINITY ? 0.f : exp2f(M[k] - Mn);
+            float ls = y[k] * f[k];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+            L[k] = L[k] * r + ls;
+            acc[k] *= r;
+            M[k] = Mn;
+        }
+        auto fold = [&](const float (&v)[JS][NB], int s0) {
+#pragma unroll
+            for (int k = 0; k < JS; ++k) {
+                float t = acc[k];
+#pragma unroll
+                for (int i = 0; i < NB; ++i)
+                    t += v[k][i] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f[k]), s0 + i));
+                acc[k] = t;
+            }
+        };
+        for (int s0 = 0; s0 < ng; s0 += 2 * NB) {
+            if (s0 + NB < ng) issue(vb, g0, ng, s0 + NB);
+            fold(va, s0);
+            if (s0 + 2 * NB < ng) issue(va, g0, ng, s0 + 2 * NB);
+            if (s0 + NB < ng) fold(vb, s0 + NB);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < JS; ++k) {
+        const int e = 64 * w + (jr + R * k) * kThreads + lane;
+        if (e < GD) out[e] = (__bf16)((M[k] == -INFINITY || L[k] == 0.f) ? 0.f : acc[k] / L[k]);
+    }
+}
+
+template <int D, int EJ>
+__device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
+                                          CombineSmem& cs, FoldHdr& fh, int* wsum) {
+    constexpr int NBW = kFusedTA / 128;  // 32-row gist blocks per wavefront
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int G = a.G, C = a.C;
+    const int b = u / a.Hkv, g = u - b * a.Hkv;
+    const int S = s.S1, W = S - 1;
+    const int p0 = idx * kFusedTA;
+    auto row_p = [&](int j, int t) { return p0 + 32 * (w + 4 * j) + 16 * t + lr; };
+    // gist rows: block-table lookups issued with the length load
+    size_t off[NBW][2];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int p = min(row_p(j, t), a.num_chunks - 1);
+            off[j][t] = slot_offset(a, b, g, max(p, 0) * (C + 1) + C);
+        }
+    ListCtx c;
+    make_ctx(a, kListGists, u, false, c);
+    const int n = c.n;
+    const int nA = max(1, (n + kFusedTA - 1) / kFusedTA);  // gist slices (<= S)
+    const int sel = nA - 1;
+    const bool selector = idx == sel;
+    const int cnt = max(0, min(kFusedTA, n - p0));
+    const bool attn = !(a.flags & kFlagSelectedGists);
+    const int ulen = c.ns * C + c.tail + (attn ? 0 : c.ns);  // unfolded list
+    const int nUB = (ulen + 31) / 32;
+    const int widx = idx < sel ? idx : idx - 1;
+    float* keys = a.keys + (size_t)u * a.key_stride;
+
+    WaveAttnL<D> wa;
+    wa.init((const __bf16*)a.q + ((size_t)b * a.Hq + (size_t)g * G) * D, G, lr, lg);
+    unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
+    SelPre pre;
+    uint64_t ownk = 0;  // the selector's key of this thread (its slice is not bucket sorted)
+    bool ownv = false;
+    int nval[NBW], nbw = 0;
+    bf16x8_t P[NBW];
+    if (cnt > 0) {
+        const int nblk = (cnt + 31) / 32;
+        nbw = nblk > w ? (nblk - w + 3) / 4 : 0;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            nval[j] = max(0, min(32, cnt - 32 * (w + 4 * j)));
+            // a token past the end reads the block's first row (in range)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (16 * t + lr >= nval[j]) off[j][t] = __shfl(off[j][0], lane & 48);
+        }
+        float* stash = (float*)(smem + Lds::stash(D)) + 64 * w;
+        const float tau = a.tau;
+        auto on_scores = [&](int j, const f32x4_t sc[2]) {
+            // routing keys: tau * sum over the group's heads (padding heads are 0)
+            float kv = 0.f;
+            int kt = -1;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = rowsum16(sc[t][r]);
+                    if (4 * t + r == lr) {
+                        kv = x * tau;
+                        kt = 16 * t + 4 * lg + r;
+                    }
+                }
+            if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kv;
+        };
+        if (attn)
+            wa.template kpass<NBW>((const __bf16*)a.kc, off, nval, nbw, a.tau_log2e, lg, P, on_scores);
+        else
+            wa.template stream<NBW>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, false,
+                                    a.tau_log2e, lr, lg, tile, on_scores);
+        if (selector) select_prefetch<kListGists>(a, c, n, nA, pre);
+        // thread t takes key slot t % 64 of wavefront t / 64
+        static_assert(NBW * 32 * 4 <= kThreads, "one key slot per thread");
+        __syncthreads();
+        const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
+        const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
+        const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
+        if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
+        __syncthreads();  // the stash is read
+        if (!selector) {
+            uint64_t* pairs = a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
+            uint64_t* lead = nA > kRecSlices ? nullptr : unit_lead(a, u) + idx * kFSelL;
+            bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+            drain();
+            __syncthreads();
+            if (threadIdx.x == 0) add_dev(unit_cntA(a, u), 1u);
+            // V pass over this slice's gists
+            if (attn) wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile);
+        } else {
+            ownk = (uint64_t)order_key(kv) | ((uint64_t)(uint32_t)(p0 + kpos) << 32);
+            ownv = kpos < cnt;
+        }
+    } else if (selector) {
+        select_prefetch<kListGists>(a, c, n, nA, pre);
+    }
+    if (selector) {
+        // the select as soon as the slices' keys are in (only the K pass's
+        // probabilities, running max and sum stay live across it: O is still
+        // zero and is re-initialised after)
+        __syncthreads();
+        __builtin_amdgcn_s_setprio(2);  // everything of the unit waits for the select
+        for (int i = n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
+        select_fused<kListGists>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, []() {});
+        if (nA <= kRecSlices) {  // the leading keys back to zero: each has been read
+            uint64_t* lead = unit_lead(a, u);
+            for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
+                const int sl = i / kFSelL;
+                if (i - sl * kFSelL < min(kFusedTA, n - sl * kFusedTA)) st_dev(lead + i, 0ull);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __syncthreads();  // the select's LDS is free for the V tiles
+#pragma unroll
+        for (int db = 0; db < WaveAttnL<D>::DB; ++db) wa.o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if (attn && cnt > 0) wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile);
+    }
+
+    // unfolded blocks of this wavefront (workers)
+    if (!selector && nUB > 0) {
+        __builtin_amdgcn_s_setprio(1);  // the unit's result waits for these rows
+        const int64_t* ro = unit_rowoff(a, u);
+        const int raw = c.ns * C;
+        const int64_t tail_off = c.tail > 0 ? (int64_t)slot_offset(a, b, g, n * (C + 1)) : 0;
+        for (int jb = w * W + widx; jb < nUB; jb += 4 * W) {
+            size_t uoff[1][2];
+            int unval[1];
+            int jr[2];
+            int64_t o[2], add[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int rel = 32 * jb + 16 * t + lr;
+                const int p = rel < ulen ? rel : 32 * jb;  // a row past the end reads the block's first
+                jr[t] = -1;
+                add[t] = 0;
+                o[t] = 1;
+                if (p < raw) {
+                    jr[t] = p / C;
+                    add[t] = (int64_t)(p - jr[t] * C) * D;
+                } else if (p < raw + c.tail) {
+                    o[t] = tail_off + (int64_t)(p - raw) * D + 1;
+                } else {
+                    jr[t] = p - raw - c.tail;
+                    add[t] = (int64_t)C * D;  // the selected chunk's gist
+                }
+                if (jr[t] >= 0) o[t] = ld_dev(ro + jr[t]);
+            }
+            for (unsigned it = 0;; ++it) {
+                if (!__ballot(o[0] == 0 || o[1] == 0)) break;
+                if (it >= kSpinLimit) {  // never expected: report, read a row in range
+                    if (lane == 0) st_dev(s.err, 1u);
+                    o[0] = o[0] == 0 ? 1 : o[0];
+                    o[1] = o[1] == 0 ? 1 : o[1];
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (o[t] == 0) o[t] = ld_dev(ro + jr[t]);
+            }
+            unval[0] = min(32, ulen - 32 * jb);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) uoff[0][t] = (size_t)(o[t] - 1 + add[t]);
+            wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, uoff, unval, 1, true,
+                                  a.tau_log2e, lr, lg, tile, [](int, const f32x4_t*) {});
+        }
+    }
+    // publish this task's partial (slot idx) and count in; the last to count
+    // in merges
+    __syncthreads();
+    {
+        float gacc[EJ];
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) gacc[j] = 0.f;
+        if (threadIdx.x < 16) {
+            fh.m[threadIdx.x] = -INFINITY;
+            fh.l[threadIdx.x] = 0.f;
+        }
+        combine_publish<D, EJ, false>(wa, a, u, idx, gacc, fh, (float*)smem, cs);
+    }
+    drain();
+    __syncthreads();
+    if (threadIdx.x == 0) wsum[0] = (int)add_dev(unit_cntB(a, u), 1u);
+    __syncthreads();
+    // the last R tasks to count in merge, element block j to the one of rank
+    // j mod R; all but the last wait for it (a short wait: they are the last)
+    constexpr int R = EJ < 4 ? EJ : 4;
+    const int rank = wsum[0] - (S - R);
+    const bool few = S < R;  // fewer tasks than mergers: the last merges all
+    if (rank < 0 || (few && rank != R - 1)) return;
+    if (rank != R - 1) {
+        wait_at_least<1>(unit_cntB(a, u), (unsigned)S, s.err);
+        __syncthreads();
+    }
+    __bf16* out = (__bf16*)a.out + ((size_t)b * a.Hq + (size_t)g * G) * D;
+    if (few) {
+        for (int jr = 0; jr < R; ++jr) merge_part<D, EJ / R>(a, u, S, jr, R, out);
+    } else {
+        merge_part<D, EJ / R>(a, u, S, rank, R, out);
+    }
+    // the last merger to finish returns the record to zero (every task has
+    // read the selection before counting in, every merger has seen the count)
+    __syncthreads();
+    if (threadIdx.x == 0) wsum[0] = (int)add_dev(unit_cntP(a, u), 1u);
+    __syncthreads();
+    if (wsum[0] != (few ? 0 : R - 1)) return;
+    for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
+    if (threadIdx.x == 0) {
+        st_dev(unit_cntA(a, u), 0u);
+        st_dev(unit_cntB(a, u), 0u);
+        st_dev(unit_cntP(a, u), 0u);
+    }
+}
+
 template <int D, int EJ, bool HIER, int NBB>
 __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1316,7 +1661,10 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     __shared__ int s_flag;
     const int nA = s.units * s.S1, nC = s.units * s.S3;
     const int t = blockIdx.x;
-    if (t < nA) {
+    if (!HIER) {
+        const int u = t / s.S1;
+        task_flat<D, EJ>(a, s, u, t - u * s.S1, smem, cs, fh, wsum);
+    } else if (t < nA) {
         const int u = t / s.S1;
         task_slices<D, EJ, HIER ? kListMeta : kListGists>(a, s, u, t - u * s.S1, smem, cs, wsum);
     } else if (HIER && t < nA + nC) {
@@ -1335,8 +1683,6 @@ template <int D, int EJ>
 void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
     if (s.hier)
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
-    else if (s.TB == 2 * kFusedTB)
-        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 2>), dim3(s.total), dim3(kThreads), lds, st, a, s);
     else
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
 }

@@ -426,6 +426,82 @@ struct WaveAttnL {
         }
     }
 
+    // K half of a two-pass stream over this wavefront's blocks j < nbw (<=
+    // NBW): every block's K rows are loaded (all in flight together), scored
+    // (on_scores(j, s) sees them) and turned into probabilities against the
+    // running maximum over all of them, P[j] (the PV A operand), with the
+    // running sum l updated and O rescaled.  vpass then multiplies them into O.
+    template <int NBW, typename OnScores>
+    __device__ inline void kpass(const __bf16* kbase, const size_t (&off)[NBW][2], const int (&nval)[NBW],
+                                 int nbw, float tau_log2e, int lg, bf16x8_t (&P)[NBW], OnScores on_scores) {
+        f32x4_t s[NBW][2];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            if (j < nbw) {
+                bf16x8_t kb[2][KK];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        kb[t][kk] = *(const bf16x8_t*)(kbase + off[j][t] + 32 * kk + 8 * lg);
+                scores(kb, s[j]);
+                on_scores(j, s[j]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * t + 4 * lg + r < nval[j]) bm = fmaxf(bm, s[j][t][r]);
+            }
+        }
+        if (nbw <= 0) return;
+        bm = rows4_max(bm);
+        const float mnew = fmaxf(m, bm);  // finite: a block has a real token
+        const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on an empty state
+        const float mb = mnew * tau_log2e;
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pv = (j < nbw && 16 * t + 4 * lg + r < nval[j]) ? exp2f(s[j][t][r] * tau_log2e - mb)
+                                                                                 : 0.f;
+                    const __bf16 pb = (__bf16)pv;
+                    ls += (float)pb;
+                    P[j][4 * t + r] = pb;
+                }
+        }
+        const bool first = m == -INFINITY;
+        l = l * alpha + ls;
+        m = mnew;
+        if (!first) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db][r] *= ar;
+            }
+        }
+    }
+
+    // V half: block j's V rows through the tile, O += P[j] . V.
+    template <int NBW>
+    __device__ inline void vpass(const __bf16* vbase, const size_t (&off)[NBW][2], int nbw,
+                                 const bf16x8_t (&P)[NBW], unsigned char* tile) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            if (j < nbw) {
+                load_v(vbase, off[j][0], off[j][1], tile);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tile is loaded
+                pv(P[j], tile);
+                // the next block's loads overwrite the tile: its reads are done
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        }
+    }
+
     // Stream this wavefront's blocks j < nbw (<= NBW): block j's rows sit at
     // element offsets off[j][t] and its first nval[j] tokens are real.
     // on_scores(j, s) sees every block's scores; attn = false skips V and PV.
