@@ -290,10 +290,10 @@ __device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, in
     uint64_t* pair_st = (uint64_t*)(smem + kBins * 4);  // kFusedTA pairs
     const int tid = threadIdx.x;
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
     const uint32_t ok = order_key(kv);
     if (pos >= 0) atomicAdd(&hist[ok >> 21], 1);
-    __syncthreads();
+    lds_barrier();
     int h[PER];
     int s = 0;
 #pragma unroll
@@ -310,20 +310,20 @@ __device__ __forceinline__ void bucket_slice(uint64_t* pairs, uint64_t* lead, in
         cur[i] = run;  // keys in buckets above bucket PER*tid + i
         run += h[i];
     }
-    __syncthreads();  // histogram reads done
+    lds_barrier();  // histogram reads done
 #pragma unroll
     for (int i = 0; i < PER; ++i) hist[PER * tid + i] = cur[i];
-    __syncthreads();
+    lds_barrier();
     if (pos >= 0) {
         const int at = atomicAdd(&hist[ok >> 21], 1);
         pair_st[at] = (uint64_t)ok | ((uint64_t)(uint32_t)(p0 + pos) << 32);
     }
-    __syncthreads();
+    lds_barrier();
     static_assert(kFusedTA == kThreads, "one pair per thread");
     if (tid < tot) st_dev(pairs + tid, pair_st[tid]);
     // the leading keys again, into the unit's record, index + 1: nonzero once written
     if (lead && tid < min(tot, kFSelL)) st_dev(lead + tid, pair_st[tid] + (1ull << 32));
-    __syncthreads();
+    lds_barrier();  // the staged pairs are read (the stores need not have landed)
 }
 
 // Top-k of unit u (ascending chunk ids, -1 padded) and each selected chunk's
@@ -367,8 +367,15 @@ __device__ inline void select_prefetch(const Args& a, const ListCtx& c, int n, i
     }
 }
 
+// The drained() of a caller with nothing to do once its stores have landed:
+// the bucketed path then skips that wait (the paths that read stored keys
+// wait for them themselves).
+struct NoDrain {
+    __device__ void operator()() const {}
+};
+
 // drained(): called by every thread once every wavefront's earlier stores
-// have completed (at most once; maybe not at all).  pre: the block-table row
+// have completed (at most once; maybe not at all; never with NoDrain).  pre: the block-table row
 // loaded by select_prefetch.  Slice `own` (the calling one) is not bucket
 // sorted: every thread brings its key (ownk: order key | list index << 32,
 // ownv: present), so that slice is complete among the candidates.  own < 0:
@@ -411,7 +418,9 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
         drain();
-        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
+        // (a flat gist slice counts in once per wavefront)
+        const unsigned per = KIND == kListGists ? 4u : 1u;
+        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), per * (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) {
@@ -600,13 +609,18 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     };
     bool general = !fast;
     if (fast) {
-        drain();          // (the polls above have waited for nearly all of it)
-        __syncthreads();  // every thread's part of the LDS state is clear
-        drained();
+        constexpr bool kDrain = !__is_same(Drained, NoDrain);
+        if (kDrain) {
+            drain();  // (the polls above have waited for nearly all of it)
+            __syncthreads();
+        } else {
+            lds_barrier();  // every thread's part of the LDS state is clear
+        }
+        if (kDrain) drained();
 #pragma unroll
         for (int j = 0; j <= KQ; ++j)
             if (up_used(j) && up_valid(j)) atomicAdd(&sh.uh[(uint32_t)up_key(j) >> 21], 1);
-        __syncthreads();
+        lds_barrier();
         find_boundary();  // bT: the bucket of the keff-th largest candidate
         // classify against bT; a slice whose kFSelL-th key is in a bucket >= bT
         // may hold more such keys: then a second round, and classify again
@@ -624,7 +638,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             wneed |= (((bm >> 31) & 1ull) << (8 * j + 2 * w)) | (((bm >> 63) & 1ull) << (8 * j + 2 * w + 1));
         }
         if (lane == 0 && wneed) atomicOr((unsigned long long*)&sh.needmask, wneed);
-        __syncthreads();
+        lds_barrier();
         const uint64_t needmask = sh.needmask;
         if (needmask) {
             // round trip 2: the keys of buckets >= bT past kFSelL of those
@@ -811,7 +825,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             }
         }
     }  // wavefront 0
-    __syncthreads();
+    lds_barrier();
     park_kept();
     for (int i = tid; i < keff; i += kThreads) emit(i, ids[i]);
     return fast;
@@ -1043,7 +1057,9 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
 // (fh.m / fh.l, gacc) and publish the result as partial slot `slot` of unit u,
-// or (LOCAL) leave it in (gacc, fh.m, fh.l) for a fold to continue from.
+// or (LOCAL) leave it in (gacc, fh.m, fh.l) for a fold to continue from.  The
+// partial's stores may still be in flight on return: a caller drains before
+// counting it in.
 template <int D, int EJ, bool LOCAL, typename WA>
 __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, int slot, float (&gacc)[EJ],
                                 FoldHdr& fh, float* red, CombineSmem& cs) {
@@ -1057,7 +1073,7 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
         cs.wm[w][lr] = wa.m;
         cs.wl[w][lr] = l;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * lg + r;
@@ -1093,7 +1109,7 @@ __device__ __forceinline__ void combine_publish(WA& wa, const Args& a, int u, in
             st_dev(p + 1, L);
         }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < EJ; ++j) {
         const int e = threadIdx.x + j * kThreads;
@@ -1313,8 +1329,9 @@ __device__ __forceinline__ void task_unfolded(const Args& a, const Sched& s, int
 // every other task is an unfolded worker.
 //   slice     K pass over its gists (routing keys; with the all-gists set also
 //             the blocks' softmax probabilities against their maximum), keys
-//             out and -- but for the selector -- bucket-sorted and published,
-//             counted in (cntA); then its V pass.
+//             out and -- but for the selector -- bucket-sorted and published;
+//             then its V pass, each wavefront counting in (cntA) once its
+//             stores have landed (only the select's slower paths read cntA).
 //   selector  keeps its slice's keys in registers and runs the top-k select
 //             over the slices' sorted keys as soon as they are published
 //             (select_fused), which writes the selection and each selected
@@ -1512,21 +1529,28 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         if (selector) select_prefetch<kListGists>(a, c, n, nA, pre);
         // thread t takes key slot t % 64 of wavefront t / 64
         static_assert(NBW * 32 * 4 <= kThreads, "one key slot per thread");
-        __syncthreads();
+        lds_barrier();
         const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
         const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
         const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
-        __syncthreads();  // the stash is read
+        lds_barrier();  // the stash is read (the key stores need not have landed)
         if (!selector) {
             uint64_t* pairs = a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
             uint64_t* lead = nA > kRecSlices ? nullptr : unit_lead(a, u) + idx * kFSelL;
             bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
-            drain();
-            __syncthreads();
-            if (threadIdx.x == 0) add_dev(unit_cntA(a, u), 1u);
-            // V pass over this slice's gists
-            if (attn) wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile);
+            // V pass over this slice's gists; each wavefront counts itself in
+            // (cntA) once its stores have landed, which the wait for its first
+            // V block covers
+            auto count_in = [&]() {
+                if (lane == 0) add_dev(unit_cntA(a, u), 1u);
+            };
+            if (attn) {
+                wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, count_in);
+            } else {
+                drain();
+                count_in();
+            }
         } else {
             ownk = (uint64_t)order_key(kv) | ((uint64_t)(uint32_t)(p0 + kpos) << 32);
             ownv = kpos < cnt;
@@ -1538,10 +1562,10 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         // the select as soon as the slices' keys are in (only the K pass's
         // probabilities, running max and sum stay live across it: O is still
         // zero and is re-initialised after)
-        __syncthreads();
+        lds_barrier();
         __builtin_amdgcn_s_setprio(2);  // everything of the unit waits for the select
         for (int i = n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-        select_fused<kListGists>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, []() {});
+        select_fused<kListGists>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
         if (nA <= kRecSlices) {  // the leading keys back to zero: each has been read
             uint64_t* lead = unit_lead(a, u);
             for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
@@ -1550,10 +1574,10 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        __syncthreads();  // the select's LDS is free for the V tiles
+        lds_barrier();  // the select's LDS is free for the V tiles
 #pragma unroll
         for (int db = 0; db < WaveAttnL<D>::DB; ++db) wa.o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        if (attn && cnt > 0) wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile);
+        if (attn && cnt > 0) wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, []() {});
     }
 
     // unfolded blocks of this wavefront (workers)
@@ -1607,7 +1631,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     }
     // publish this task's partial (slot idx) and count in; the last to count
     // in merges
-    __syncthreads();
+    lds_barrier();
     {
         float gacc[EJ];
 #pragma unroll
@@ -1639,8 +1663,9 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         merge_part<D, EJ / R>(a, u, S, rank, R, out);
     }
     // the last merger to finish returns the record to zero (every task has
-    // read the selection before counting in, every merger has seen the count)
-    __syncthreads();
+    // read the selection before counting in, every merger has seen the count;
+    // the output's stores need not have landed)
+    lds_barrier();
     if (threadIdx.x == 0) wsum[0] = (int)add_dev(unit_cntP(a, u), 1u);
     __syncthreads();
     if (wsum[0] != (few ? 0 : R - 1)) return;

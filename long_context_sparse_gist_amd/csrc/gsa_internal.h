@@ -8,6 +8,17 @@
 
 namespace gsa {
 
+// Block barrier that orders LDS accesses only.  __syncthreads() also makes the
+// wavefronts wait for every global load and store they have in flight (its
+// fences cover all memory); where a barrier guards nothing but LDS data, that
+// wait costs a memory round trip for nothing.  Global accesses are not
+// ordered across this barrier.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr unsigned kFlagSumProbs = 0x1u;
 constexpr unsigned kFlagSelectedGists = 0x2u;
 constexpr unsigned kFlagTopP = 0x4u;

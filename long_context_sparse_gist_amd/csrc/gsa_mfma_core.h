@@ -486,15 +486,23 @@ struct WaveAttnL {
         }
     }
 
-    // V half: block j's V rows through the tile, O += P[j] . V.
-    template <int NBW>
+    // V half: block j's V rows through the tile, O += P[j] . V.  landed() runs
+    // (in every lane) once every earlier store of this wavefront has landed:
+    // after the first block's wait, which covers them, or at once without
+    // blocks.
+    template <int NBW, typename Landed>
     __device__ inline void vpass(const __bf16* vbase, const size_t (&off)[NBW][2], int nbw,
-                                 const bf16x8_t (&P)[NBW], unsigned char* tile) {
+                                 const bf16x8_t (&P)[NBW], unsigned char* tile, Landed landed) {
+        if (nbw <= 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            landed();
+        }
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             if (j < nbw) {
                 load_v(vbase, off[j][0], off[j][1], tile);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tile is loaded
+                if (j == 0) landed();
                 pv(P[j], tile);
                 // the next block's loads overwrite the tile: its reads are done
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -55,7 +55,7 @@ __device__ inline int block_excl_scan(int x, int* total, int* wsum) {
         if (lane >= off) incl += y;
     }
     if (lane == 63) wsum[w] = incl;
-    __syncthreads();
+    lds_barrier();
     int base = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NT / 64; ++i) {
@@ -63,7 +63,7 @@ __device__ inline int block_excl_scan(int x, int* total, int* wsum) {
         base += (i < w) ? v : 0;
         tot += v;
     }
-    __syncthreads();
+    lds_barrier();
     *total = tot;
     return base + incl - x;
 }
