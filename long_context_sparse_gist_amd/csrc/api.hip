@@ -25,6 +25,10 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr size_t kCtlWords = GSA_WORKSPACE_CONTROL_BYTES / 4;
 constexpr size_t kHdrWords = 4096;  // header: error word
 constexpr long kMaxFusedUnits = 512;
+// Workgroups of the single-launch kernel resident at once on an MI355X (256
+// compute units, 4 each): the flat plan adds tasks that only stream unfolded
+// blocks (and wait for the select first) only while the whole grid fits.
+constexpr long kFusedSlots = 1024;
 static_assert(kHdrWords + (size_t)kMaxFusedUnits * gsa::kUnitRec <= kCtlWords, "control block");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -153,15 +157,23 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         pl.S2 = pl.S2 > 0 ? pl.S2 : 1;
         if (pl.hier) pl.Sc = pl.Sc > 0 ? pl.Sc : 1;
     }
+    pl.sc.flat = 0;
     if (pl.fused && !pl.hier) {
         // flat GSA: S tasks per unit, the gist slices first (the last of them
         // selects); every other task streams at most one 32-row block of the
-        // unfolded list per wavefront (4 per task) at full length
+        // unfolded list per wavefront (4 per task) at full length.  That
+        // needs the whole grid resident at once (a task holds its slot while
+        // it waits for its unit's select); else every unit's gist slices go
+        // first and the unfolded tasks after them.
         const long ublocks = (cap2 + 31) / 32;
         const long need = 1 + (ublocks + 3) / 4;  // the selector does no unfolded block
-        if (need > pl.S1) pl.S1 = (int)need;
-        pl.S2 = 0;
-        TB = 32;
+        const long S = need > pl.S1 ? need : pl.S1;
+        if (units * S <= kFusedSlots) {
+            pl.sc.flat = 1;
+            pl.S1 = (int)S;
+            pl.S2 = 0;
+            TB = 32;
+        }
     }
     a.S1 = pl.S1;
     a.SL = TA;

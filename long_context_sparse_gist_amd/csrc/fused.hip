@@ -380,7 +380,7 @@ struct NoDrain {
 // sorted: every thread brings its key (ownk: order key | list index << 32,
 // ownv: present), so that slice is complete among the candidates.  own < 0:
 // the caller owns no slice (every slice published its sorted keys).
-template <int KIND, typename Drained>
+template <int KIND, int PER = 1, typename Drained>
 __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, const ListCtx& c, int n, int nA,
                                              const float* keys, unsigned char* smem, SelPre& pre, int own,
                                              uint64_t ownk, bool ownv, Drained drained) {
@@ -418,9 +418,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
         drain();
-        // (a flat gist slice counts in once per wavefront)
-        const unsigned per = KIND == kListGists ? 4u : 1u;
-        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), per * (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
+        // (PER counts per slice: a slice that counts in per wavefront, 4)
+        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)PER * (own >= 0 ? nA - 1 : nA), sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) {
@@ -1565,7 +1564,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         lds_barrier();
         __builtin_amdgcn_s_setprio(2);  // everything of the unit waits for the select
         for (int i = n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-        select_fused<kListGists>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
+        select_fused<kListGists, 4>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
         if (nA <= kRecSlices) {  // the leading keys back to zero: each has been read
             uint64_t* lead = unit_lead(a, u);
             for (int i = threadIdx.x; i < nA * kFSelL; i += kThreads) {
@@ -1686,7 +1685,7 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     __shared__ int s_flag;
     const int nA = s.units * s.S1, nC = s.units * s.S3;
     const int t = blockIdx.x;
-    if (!HIER) {
+    if constexpr (!HIER && NBB == 0) {  // flat GSA, every task a gist slice or unfolded blocks
         const int u = t / s.S1;
         task_flat<D, EJ>(a, s, u, t - u * s.S1, smem, cs, fh, wsum);
     } else if (t < nA) {
@@ -1706,8 +1705,14 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
 namespace {
 template <int D, int EJ>
 void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
+    // NBB: 32-token blocks per wavefront of an unfolded task; 0: the flat
+    // kernel whose every task is a gist slice or a set of unfolded blocks
     if (s.hier)
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    else if (s.flat)
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 0>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    else if (s.TB == 2 * kFusedTB)
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 2>), dim3(s.total), dim3(kThreads), lds, st, a, s);
     else
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
 }

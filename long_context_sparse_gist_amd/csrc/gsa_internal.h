@@ -151,6 +151,9 @@ struct Sched {
     int TA, TB;        // tokens per task
     int total;         // workgroups
     int hier;          // H-GSA
+    int flat;          // flat GSA, one launch: 1 = every task owns a gist slice or only
+                       // unfolded blocks (S1 tasks per unit, the grid resident at once),
+                       // 0 = gist slices of every unit first, then unfolded tasks
 };
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront);

@@ -34,6 +34,15 @@ SMALL = {
     "b2-g16-d64-c4": gi.Workload("b2-g16-d64-c4", gi.BF16, 2, 16, 1, 64, 4, 700, 50, 64),
     "f32-b2-g3-d64": gi.Workload("f32-b2-g3-d64", gi.F32, 2, 6, 2, 64, 16, 200, 12, 16,
                                  plant="align", plant_count=3),
+    # 512 units: just as many single-launch tasks as the GPU holds at once
+    # (two per unit), then more, so that the plan puts every unit's gist
+    # slices first and the unfolded tasks after
+    "b128-g2-d64-c4-fit": gi.Workload("b128-g2-d64-c4-fit", gi.BF16, 128, 8, 4, 64, 4, 300, 20, 16,
+                                      plant="align", plant_count=3),
+    "b128-g2-d64-c4-many": gi.Workload("b128-g2-d64-c4-many", gi.BF16, 128, 8, 4, 64, 4, 300, 40, 16,
+                                       plant="align", plant_count=3),
+    "b64-g2-d128-c8-many": gi.Workload("b64-g2-d128-c8-many", gi.BF16, 64, 16, 8, 128, 8, 270, 24, 16,
+                                       plant="doc_bias", n_docs=3),
 }
 
 
