@@ -834,8 +834,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
 // meta-gists or the candidate gists (H-GSA).  Scores the rows (routing keys),
 // attends them when the set needs them (all gists, all meta-gists), publishes
 // the keys sorted by bucket and its partial.  The list's last slice runs the
-// list's select as soon as its partial is written: it counts the partial in
-// at the select's first barrier, once its stores have completed anyway.
+// list's select as soon as its partial is written, and counts the partial in
+// after the select.
 template <int D, int EJ, int KIND>
 __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
                                             unsigned char* smem, CombineSmem& cs, int* wsum) {
@@ -988,12 +988,12 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         // thread t takes key slot t % 64 of wavefront t / 64 (slots past NBW * 32
         // hold no row: kpos >= cnt there)
         static_assert(NBW * 32 * 4 <= kThreads, "one key slot per thread");
-        __syncthreads();
+        lds_barrier();
         const int ws = threadIdx.x >> 6, slot = threadIdx.x & 63;
         const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
         const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
-        __syncthreads();  // the tiles are free
+        lds_barrier();  // the tiles are free (the key stores need not have landed)
         uint64_t* pairs = cand ? a.spairs_c + ((size_t)u * s.S3 + idx) * kFusedTA
                                : a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
         uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
@@ -1028,15 +1028,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     __builtin_amdgcn_s_setprio(2);
     if (kind == kListGists)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
-    // the partial's count: by thread 0 once every wavefront has drained
-    const bool partial = attn && cnt > 0;
-    bool counted = false;
-    auto count_partial = [&]() {
-        if (partial && threadIdx.x == 0) add_dev(unit_cntP(a, u), 1u);
-        counted = true;
-    };
     if (!prefetched) select_prefetch<KIND>(a, c, n, nA, pre);
-    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, count_partial);
+    // (the select does not wait for this slice's partial to land: it is
+    // counted in after the select, cntP, where only the merge reads it)
+    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
@@ -1050,8 +1045,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     // unit's merging task resets the record only after every select says so
     drain();
     __syncthreads();
-    if (!counted) count_partial();
-    if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
+    if (threadIdx.x == 0) {
+        if (attn && cnt > 0) add_dev(unit_cntP(a, u), 1u);  // the partial
+        add_dev(unit_cntS(a, u), 1u);
+    }
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
