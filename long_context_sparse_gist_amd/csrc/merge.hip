@@ -4,7 +4,8 @@
 //     M = max_i m_i,  lambda = sum_i l_i 2^(m_i - M),
 //     out = (sum_i acc_i 2^(m_i - M)) / lambda
 // with m_i in the exp2 domain.  An empty attention set gives a zero output.
-// One workgroup per (head, unit); 4 slot groups x 64 column pairs.
+// One workgroup per (head, unit); 4 slot groups x 64 column pairs, each slot
+// group folding its slots in one streaming pass (running maximum, rescaled).
 #include "gsa_lists.h"
 
 namespace gsa {
@@ -28,45 +29,55 @@ __global__ __launch_bounds__(256) void merge_kernel(Args a, int hier) {
     const float* acc = a.part_acc + (size_t)u * a.NS * G * D;
     auto slot = [&](int i) { return i < n1 ? i : a.S1 + (i - n1); };
     const int sg = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool col = 2 * lane < D;
 
-    // maximum and normaliser of head h
-    float m = -INFINITY;
-    for (int i = threadIdx.x; i < ns; i += blockDim.x) m = fmaxf(m, ml[(size_t)slot(i) * G + h].x);
+    // one streaming pass per slot group (slots sg, sg + 4, ...): a running
+    // maximum, normaliser and column pair, rescaled as the maximum grows (the
+    // loads of consecutive slots are independent, so they are in flight
+    // together); then the four groups are combined
+    constexpr int kBatch = 16;  // slots of a group loaded before they are folded
+    float m = -INFINITY, l = 0.f;
+    float2 o = make_float2(0.f, 0.f);
+    for (int i0 = sg; i0 < ns; i0 += kBatch * kSlotGroups) {
+        float2 v[kBatch], x[kBatch];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) s_m[sg] = m;
-    __syncthreads();
-    float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    float l = 0.f;
-    if (M != -INFINITY)
-        for (int i = threadIdx.x; i < ns; i += blockDim.x) {
-            float2 v = ml[(size_t)slot(i) * G + h];
-            l += v.y * exp2f(v.x - M);
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + kSlotGroups * k;
+            v[k] = make_float2(-INFINITY, 0.f);
+            x[k] = make_float2(0.f, 0.f);
+            if (i < ns) {
+                const size_t s = (size_t)slot(i);
+                v[k] = ml[s * G + h];
+                if (col) x[k] = *(const float2*)(acc + (s * G + h) * D + 2 * lane);
+            }
         }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) s_l[sg] = l;
-    __syncthreads();
-    const float lam = s_l[0] + s_l[1] + s_l[2] + s_l[3];
-
-    // weighted column sums: thread (sg, lane) owns columns 2*lane, 2*lane+1
-    float2 o = make_float2(0.f, 0.f);
-    if (M != -INFINITY && 2 * lane < D) {
-#pragma unroll 8
-        for (int i = sg; i < ns; i += kSlotGroups) {
-            size_t s = (size_t)slot(i);
-            float sc = exp2f(ml[s * G + h].x - M);
-            float2 v = *(const float2*)(acc + (s * G + h) * D + 2 * lane);
-            o.x += v.x * sc;
-            o.y += v.y * sc;
+        for (int k = 0; k < kBatch; ++k) {
+            if (v[k].x == -INFINITY) continue;  // an empty split (or none)
+            const float mn = fmaxf(m, v[k].x);
+            const float fo = m == -INFINITY ? 0.f : exp2f(m - mn);
+            const float fv = exp2f(v[k].x - mn);
+            l = l * fo + v[k].y * fv;
+            o.x = o.x * fo + x[k].x * fv;
+            o.y = o.y * fo + x[k].y * fv;
+            m = mn;
         }
     }
-    red[sg][lane] = o;
+    if (lane == 0) s_m[sg] = m;
     __syncthreads();
-    if (sg == 0 && 2 * lane < D) {
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+    if (lane == 0) s_l[sg] = l * f;
+    red[sg][lane] = make_float2(o.x * f, o.y * f);
+    __syncthreads();
+    if (sg == 0 && col) {
+        const float lam = s_l[0] + s_l[1] + s_l[2] + s_l[3];
         float2 t = red[0][lane];
-        for (int j = 1; j < kSlotGroups; ++j) { t.x += red[j][lane].x; t.y += red[j][lane].y; }
-        float inv = (M != -INFINITY) ? 1.f / lam : 0.f;
+        for (int j = 1; j < kSlotGroups; ++j) {
+            t.x += red[j][lane].x;
+            t.y += red[j][lane].y;
+        }
+        const float inv = (M != -INFINITY && lam > 0.f) ? 1.f / lam : 0.f;
         T* out = (T*)a.out + ((size_t)c.b * a.Hq + (size_t)c.g * G + h) * D;
         out[2 * lane] = (T)(t.x * inv);
         out[2 * lane + 1] = (T)(t.y * inv);

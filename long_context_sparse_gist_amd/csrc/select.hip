@@ -94,6 +94,9 @@ __device__ void sum_probs_keys(const Args& a, int u, int n, float* kw, float* re
 // each workgroup folds its unit's gist attention partials into every head's
 // softmax maximum and normaliser (base-2 domain) and writes the keys of its
 // part of the gists.  A few parts per unit: the fold is repeated per part.
+// The logits of the part's keys are loaded first, so that their round trip
+// overlaps the fold's; each thread holds its splits' (max, sum) pairs for both
+// reductions.
 __global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
     __shared__ float red[16 * (kThreads / 64)];
     const int u = blockIdx.y;
@@ -105,33 +108,67 @@ __global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
     const int G = a.G;    // <= 16
     const int ns = (n + a.SL - 1) / a.SL;
     const float2* ml = a.part_ml + (size_t)u * a.NS * G;
-    float m[16], l[16];
+    const size_t hs = a.key_stride;
+    const float* zl = a.hlog + (size_t)u * G * hs;
+    float* kw = a.keys + (size_t)u * hs;
+    const int end = min(n, p0 + per);
+    // this thread's keys: gists p0 + tid + kThreads * q (q < KQ); more than
+    // KQ per thread loop below
+    constexpr int KQ = 2;
+    float zv[KQ][16];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
+    for (int q = 0; q < KQ; ++q) {
+        const int i = p0 + threadIdx.x + q * kThreads;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) zv[q][h] = (h < G && i < end) ? zl[h * hs + i] : 0.f;
     }
-    for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
+    // the splits' pairs: sp = tid + kThreads * r (r < SR)
+    constexpr int SR = 2;
+    float m[16], l[16];
+    float2 pr[SR][16];
+#pragma unroll
+    for (int r = 0; r < SR; ++r) {
+        const int sp = threadIdx.x + r * kThreads;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            pr[r][h] = (h < G && sp < ns) ? ml[(size_t)sp * G + h] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) m[h] = fmaxf(pr[0][h].x, pr[1][h].x);
+    for (int sp = threadIdx.x + SR * kThreads; sp < ns; sp += kThreads) {
 #pragma unroll
         for (int h = 0; h < 16; ++h)
             if (h < G) m[h] = fmaxf(m[h], ml[(size_t)sp * G + h].x);
     }
     block_reduce16(m, true, red);
-    for (int sp = threadIdx.x; sp < ns; sp += kThreads) {
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        l[h] = 0.f;
+#pragma unroll
+        for (int r = 0; r < SR; ++r)
+            if (pr[r][h].x != -INFINITY) l[h] += pr[r][h].y * exp2f(pr[r][h].x - m[h]);
+    }
+    for (int sp = threadIdx.x + SR * kThreads; sp < ns; sp += kThreads) {
 #pragma unroll
         for (int h = 0; h < 16; ++h)
             if (h < G) l[h] += ml[(size_t)sp * G + h].y * exp2f(ml[(size_t)sp * G + h].x - m[h]);
     }
     block_reduce16(l, false, red);
-    const size_t hs = a.key_stride;
-    const float* z = a.hlog + (size_t)u * G * hs;
-    float* kw = a.keys + (size_t)u * hs;
-    const int end = min(n, p0 + per);
-    for (int i = p0 + threadIdx.x; i < end; i += kThreads) {
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+        const int i = p0 + threadIdx.x + q * kThreads;
+        if (i >= end) continue;
         float key = 0.f;
 #pragma unroll
         for (int h = 0; h < 16; ++h)
-            if (h < G) key += exp2f(z[h * hs + i] * 1.4426950408889634f - m[h]) / l[h];
+            if (h < G) key += exp2f(zv[q][h] * 1.4426950408889634f - m[h]) / l[h];
+        kw[i] = key;
+    }
+    for (int i = p0 + threadIdx.x + KQ * kThreads; i < end; i += kThreads) {
+        float key = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h < G) key += exp2f(zl[h * hs + i] * 1.4426950408889634f - m[h]) / l[h];
         kw[i] = key;
     }
 }
@@ -163,14 +200,19 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Args a, int mode) {
 // -1 padded) to the shortest prefix of key order (largest first, ties to the
 // lower id, NaN last) whose selection probabilities reach top_p, rewrites it
 // ascending and stores its length in nsel.  A chunk's selection probability
-// is the softmax of its key over the sequence's gists (NaN: 0).  The prefix
-// is summed in key order (chunks of ranks per lane, then a prefix over lanes).
+// is the softmax of its key over the sequence's gists (NaN: 0).  The softmax
+// maximum and normaliser come from one streaming pass over the keys (each
+// thread rescales its running sum as its maximum grows); entry ranks are
+// counted by every thread over a share of the others; the prefix is summed in
+// key order (chunks of ranks per lane, then a prefix over lanes) and the kept
+// entries are packed with a block scan.
 __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
     __shared__ uint32_t okey[kTopPMaxK];
     __shared__ int oid[kTopPMaxK];
     __shared__ float wr[kTopPMaxK];  // selection weights in key order
     __shared__ int rk[kTopPMaxK];    // key-order rank of selection entry i
     __shared__ float red[kThreads / 64];
+    __shared__ int wsum[kThreads / 64];
     __shared__ int s_need;
     const int u = blockIdx.x, tid = threadIdx.x;
     int n, tail;
@@ -178,30 +220,74 @@ __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
     const int kk = min(a.top_k, n);
     const float* kw = a.keys + (size_t)u * a.key_stride;
     int32_t* sel = a.sel + (size_t)u * a.top_k;
-    float m = -INFINITY;
-#pragma unroll 4
-    for (int i = tid; i < n; i += kThreads)
-        if (!isnan(kw[i])) m = fmaxf(m, kw[i]);
-    m = block_reduce(m, true, red);
-    const bool usable = isfinite(m);
-    float z = 0.f;
-    if (usable) {
-#pragma unroll 4
-        for (int i = tid; i < n; i += kThreads) z += isnan(kw[i]) ? 0.f : expf(kw[i] - m);
+    // the selection's entries and keys (loads issued with the key pass's)
+    constexpr int EPT = kTopPMaxK / kThreads;  // entries per thread: i = EPT * tid + e
+    int myid[EPT];
+    float mykey[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = EPT * tid + e;
+        myid[e] = i < kk ? sel[i] : 0;
     }
-    z = block_reduce(z, false, red);
-    for (int i = tid; i < kk; i += kThreads) {
-        const int id = sel[i];
-        oid[i] = id;
-        okey[i] = order_key(kw[id]);
+    // running maximum and sum of exp over this thread's keys
+    constexpr int kBatch = 16;
+    float m = -INFINITY, z = 0.f;
+    for (int i0 = tid; i0 < n; i0 += kBatch * kThreads) {
+        float v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + k * kThreads;
+            v[k] = i < n ? kw[i] : NAN;
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (!isnan(v[k])) bm = fmaxf(bm, v[k]);
+        if (bm == -INFINITY) continue;  // nothing above -inf in the batch
+        const float mn = fmaxf(m, bm);
+        float zb = 0.f;
+        if (isfinite(mn)) {
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) zb += isnan(v[k]) ? 0.f : expf(v[k] - mn);
+        }
+        z = (m == -INFINITY || !isfinite(mn) ? 0.f : z * expf(m - mn)) + zb;
+        m = mn;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = EPT * tid + e;
+        mykey[e] = i < kk ? kw[myid[e]] : 0.f;
+        if (i < kk) {
+            oid[i] = myid[e];
+            okey[i] = order_key(mykey[e]);
+            rk[i] = 0;
+        }
+    }
+    const float M = block_reduce(m, true, red);
+    const bool usable = isfinite(M);
+    z = block_reduce(usable && m != -INFINITY ? z * expf(m - M) : 0.f, false, red);
+    __syncthreads();  // okey, oid, rk in place
+    // ranks: thread t counts, for entry t % kk (and those kThreads apart),
+    // the entries of its share of the others that come first in key order
+    {
+        const int reps = kk > 0 ? max(1, kThreads / kk) : 1;  // threads per entry
+        const int i0 = tid % max(kk, 1), part = tid / max(kk, 1);
+        if (kk > 0 && part < reps) {
+            const int per = (kk + reps - 1) / reps, jb = part * per, je = min(kk, jb + per);
+            for (int i = i0; i < kk; i += kThreads) {
+                const uint32_t oi = okey[i];
+                const int di = oid[i];
+                int r = 0;
+                for (int j = jb; j < je; ++j) r += okey[j] > oi || (okey[j] == oi && oid[j] < di);
+                atomicAdd(&rk[i], r);
+            }
+        }
     }
     __syncthreads();
-    for (int i = tid; i < kk; i += kThreads) {
-        int r = 0;
-        for (int j = 0; j < kk; ++j) r += okey[j] > okey[i] || (okey[j] == okey[i] && oid[j] < oid[i]);
-        rk[i] = r;
-        const float key = kw[oid[i]];
-        wr[r] = (usable && !isnan(key)) ? expf(key - m) : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = EPT * tid + e;
+        if (i < kk) wr[rk[i]] = (usable && !isnan(mykey[e])) ? expf(mykey[e] - M) : 0.f;
     }
     __syncthreads();
     if (tid < 64) {
@@ -240,11 +326,15 @@ __global__ __launch_bounds__(kThreads) void topp_trim_kernel(Args a) {
     __syncthreads();
     const int need = s_need;
     // keep the entries ranked below `need`, in their (ascending id) order
-    for (int i = tid; i < kk; i += kThreads) {
-        if (rk[i] >= need) continue;
-        int pos = 0;
-        for (int j = 0; j < i; ++j) pos += rk[j] < need;
-        sel[pos] = oid[i];
+    int keep = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < kk && rk[EPT * tid + e] < need) ? 1 : 0;
+    int tot;
+    int pos = block_excl_scan<kThreads>(keep, &tot, wsum);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = EPT * tid + e;
+        if (i < kk && rk[i] < need) sel[pos++] = myid[e];
     }
     for (int i = need + tid; i < a.top_k; i += kThreads) sel[i] = -1;
 }
