@@ -136,9 +136,18 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         const long ksel = p->top_k < kc ? p->top_k : kc;
         const long kmeta = pl.hier ? (m->top_k_meta < cap1 ? m->top_k_meta : cap1) : 0;
         // (the sum-of-probabilities key needs every gist's logits before any key:
-        // multi-launch path)
+        // multi-launch path.  Top-p runs in the single launch with the all-gists
+        // set when its grid is resident at once (the per-slice layout) and the
+        // record holds every slice's (max, sum) pair; else multi-launch)
+        bool topp_ok = false;
+        if ((p->flags & GSA_SELECT_TOP_P) && !pl.hier && !(p->flags & GSA_SET_SELECTED_GISTS)) {
+            const long nA = (M + gsa::kFusedTA - 1) / gsa::kFusedTA;
+            const long need = 1 + ((cap2 + 31) / 32 + 3) / 4;
+            topp_ok = nA <= gsa::kTopPSlices && units * (need > nA ? need : nA) <= kFusedSlots;
+        }
         pl.fused = pl.mfma && units * (pl.hier ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
-                   kmeta <= gsa::kRecMeta && !(p->flags & (GSA_SCORE_SUM_PROBS | GSA_SELECT_TOP_P));
+                   kmeta <= gsa::kRecMeta && !(p->flags & GSA_SCORE_SUM_PROBS) &&
+                   (!(p->flags & GSA_SELECT_TOP_P) || topp_ok);
         a.recs_per_unit = pl.hier ? 2 : 1;
     }
     // H-GSA's meta slices and candidate tasks take half as many rows: its

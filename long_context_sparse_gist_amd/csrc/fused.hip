@@ -511,8 +511,165 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     };
     for (int i = keff + tid; i < k; i += kThreads) st_dev(out + i, (int32_t)-1);
     if (keff == 0) return fast;
+    // Top-p (flat GSA, per-slice layout): the top-k selection in idl
+    // (ascending list indices, keff of them, in LDS) is cut to the shortest
+    // prefix of key order (larger first, ties to the lower index, NaN last)
+    // whose selection probabilities -- the softmax of the keys over the
+    // sequence's gists, from every slice's (max, sum of exp) pair -- reach
+    // top_p; the kept entries are emitted ascending, the others get -1 and a
+    // row offset that marks them skipped.
+    constexpr bool kTopP = KIND == kListGists && PER == 4;
+    const bool topp = kTopP && (a.flags & kFlagTopP);
+    auto topp_emit = [&](const int* idl) {
+        float* fred = (float*)sh.hist;                  // wavefront partials
+        uint32_t* tk = (uint32_t*)sh.uh;                // order keys of the selection
+        int* trk = (int*)sh.uh + kRecRowOffs;           // their ranks in key order
+        float* twr = (float*)sh.cidx;                   // selection weights by rank
+        static_assert(2 * kRecRowOffs <= kBins && kRecRowOffs <= kFSelCand, "top-p arrays");
+        auto bmax = [&](float x) {
+            for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+            lds_barrier();
+            if (lane == 0) fred[w] = x;
+            lds_barrier();
+            return fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+        };
+        auto bsum = [&](float x) {
+            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+            lds_barrier();
+            if (lane == 0) fred[w] = x;
+            lds_barrier();
+            return (fred[0] + fred[1]) + (fred[2] + fred[3]);
+        };
+        // the slices' pairs (each written right after its K pass)
+        const uint64_t* tp = unit_topp(a, u);
+        float pm = -INFINITY, pz = 0.f;
+        if (tid < nA) {
+            uint64_t x = ld_dev(tp + tid);
+            for (unsigned it = 0; x == 0ull; ++it) {
+                if (it >= kSpinLimit) {  // never expected: report, count the slice empty
+                    st_dev(sc.err, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                x = ld_dev(tp + tid);
+            }
+            if (x != 0ull) {
+                pm = __uint_as_float((uint32_t)x);
+                const float zz = __uint_as_float((uint32_t)(x >> 32));
+                pz = zz > 0.f ? zz : 0.f;
+            }
+        }
+        const float M = bmax(pm);
+        const bool usable = isfinite(M);
+        const float Z = bsum(usable && pm != -INFINITY ? pz * expf(pm - M) : 0.f);
+        // the selected keys: every other slice's wavefronts have counted in,
+        // so their key stores have landed
+        drain();
+        if (nA > 1) wait_at_least<8>(unit_cntA(a, u), (unsigned)PER * (nA - 1), sc.err);
+        __syncthreads();
+        constexpr int EPT = kRecRowOffs / kThreads;
+        float kvs[EPT];
+        int ids_[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = EPT * tid + e;
+            ids_[e] = i < keff ? idl[i] : 0;
+            kvs[e] = i < keff ? ld_dev(keys + ids_[e]) : 0.f;
+            if (i < keff) {
+                tk[i] = order_key(kvs[e]);
+                trk[i] = 0;
+            }
+        }
+        lds_barrier();
+        {
+            // entry t % keff's rank, counted by threads over shares of the
+            // others (multiples of 4 entries, read 16 bytes at a time: one LDS
+            // read per 4 compares, several in flight)
+            const int reps = max(1, kThreads / keff), i0 = tid % keff, part = tid / keff;
+            if (part < reps) {
+                const int per = (((keff + reps - 1) / reps) + 3) & ~3;
+                const int jb = min(keff, part * per), je = min(keff, jb + per);
+                for (int i = i0; i < keff; i += kThreads) {
+                    const uint32_t oi = tk[i];
+                    const int di = idl[i];
+                    auto before = [&](uint32_t kj, int dj) { return (kj > oi || (kj == oi && dj < di)) ? 1 : 0; };
+                    int r = 0, j = jb;
+#pragma unroll 4
+                    for (; j + 4 <= je; j += 4) {
+                        const uint4 kq = *(const uint4*)&tk[j];
+                        const int4 iq = *(const int4*)&idl[j];
+                        r += before(kq.x, iq.x) + before(kq.y, iq.y) + before(kq.z, iq.z) + before(kq.w, iq.w);
+                    }
+                    for (; j < je; ++j) r += before(tk[j], idl[j]);
+                    atomicAdd(&trk[i], r);
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = EPT * tid + e;
+            if (i < keff) twr[trk[i]] = (usable && !isnan(kvs[e])) ? expf(kvs[e] - M) : 0.f;
+        }
+        lds_barrier();
+        if (w == 0) {
+            // lane l sums ranks [l*per, (l+1)*per); a prefix over the lanes
+            // finds the chunk where the running sum reaches the target; that
+            // lane walks its chunk to the cut
+            const int per = (keff + 63) / 64, b0 = lane * per, e0 = min(keff, b0 + per);
+            float cs = 0.f;
+            for (int r = b0; r < e0; ++r) cs += twr[r];
+            float incl = cs;
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const float target = a.top_p * Z;
+            const uint64_t hit = __ballot(usable && b0 < e0 && incl >= target);
+            int need = keff;
+            if (hit) {
+                const int lc = __ffsll((unsigned long long)hit) - 1;
+                int nl = e0;  // (rounding: the chunk's end if the walk falls short)
+                float cum = incl - cs;
+                for (int r = b0; r < e0; ++r) {
+                    cum += twr[r];
+                    if (cum >= target) {
+                        nl = r + 1;
+                        break;
+                    }
+                }
+                need = __shfl(nl, lc);
+            }
+            if (lane == 0) sh.ncand = need;
+        }
+        lds_barrier();
+        const int need = sh.ncand;
+        int keep = 0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < keff && trk[EPT * tid + e] < need) ? 1 : 0;
+        int ktot;
+        int pos = block_excl_scan<kThreads>(keep, &ktot, sh.wsum);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = EPT * tid + e;
+            if (i < keff && trk[i] < need) emit(pos++, ids_[e]);
+        }
+        for (int i = need + tid; i < keff; i += kThreads) {
+            st_dev(out + i, (int32_t)-1);
+            st_dev(ro + i, (int64_t)kRowSkip);
+        }
+    };
     if (keff == n) {
         park_kept();
+        if constexpr (kTopP) {
+            if (topp) {
+                int* idl = (int*)sh.ckey;
+                for (int i = tid; i < n; i += kThreads) idl[i] = i;
+                lds_barrier();
+                topp_emit(idl);
+                return fast;
+            }
+        }
         for (int i = tid; i < n; i += kThreads) emit(i, i);
         return fast;
     }
@@ -712,6 +869,17 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         }
         __syncthreads();  // the LDS is the select's no more
         park_kept();
+        if constexpr (kTopP) {
+            if (topp) {
+                int* idl = (int*)sh.ckey;
+#pragma unroll
+                for (int j = 0; j < kRecRowOffs / kThreads; ++j)
+                    if (tid + j * kThreads < keff) idl[tid + j * kThreads] = mi[j];
+                lds_barrier();
+                topp_emit(idl);
+                return fast;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kRecRowOffs / kThreads; ++j)
             if (tid + j * kThreads < keff) emit(tid + j * kThreads, mi[j]);
@@ -826,6 +994,12 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     }  // wavefront 0
     lds_barrier();
     park_kept();
+    if constexpr (kTopP) {
+        if (topp) {
+            topp_emit(ids);
+            return fast;
+        }
+    }
     for (int i = tid; i < keff; i += kThreads) emit(i, ids[i]);
     return fast;
 }
@@ -1475,6 +1649,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     const bool selector = idx == sel;
     const int cnt = max(0, min(kFusedTA, n - p0));
     const bool attn = !(a.flags & kFlagSelectedGists);
+    const bool topp = a.flags & kFlagTopP;  // (with the all-gists set only)
     const int ulen = c.ns * C + c.tail + (attn ? 0 : c.ns);  // unfolded list
     const int nUB = (ulen + 31) / 32;
     const int widx = idx < sel ? idx : idx - 1;
@@ -1530,6 +1705,24 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         const int kpos = 32 * (ws + 4 * (slot >> 5)) + (slot & 31);
         const float kv = kpos < cnt ? ((const float*)(smem + Lds::stash(D)))[64 * ws + slot] : 0.f;
         if (kpos < cnt) st_dev(keys + p0 + kpos, kv);
+        if (topp) {
+            // this slice's softmax maximum and sum of exp over its keys (NaN
+            // keys left out), for the top-p cut
+            const bool ok = kpos < cnt && !isnan(kv);
+            float x = ok ? kv : -INFINITY;
+            for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+            if (lane == 0) fh.m[w] = x;
+            lds_barrier();
+            const float ms = fmaxf(fmaxf(fh.m[0], fh.m[1]), fmaxf(fh.m[2], fh.m[3]));
+            float z = ok && isfinite(ms) ? expf(kv - ms) : 0.f;
+            for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+            if (lane == 0) fh.l[w] = z;
+            lds_barrier();
+            const float zs = (fh.l[0] + fh.l[1]) + (fh.l[2] + fh.l[3]);
+            if (threadIdx.x == 0)
+                st_dev(unit_topp(a, u) + idx,
+                       ((uint64_t)__float_as_uint(zs > 0.f ? zs : -1.f) << 32) | __float_as_uint(ms));
+        }
         lds_barrier();  // the stash is read (the key stores need not have landed)
         if (!selector) {
             uint64_t* pairs = a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
@@ -1594,7 +1787,16 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
                 jr[t] = -1;
                 add[t] = 0;
                 o[t] = 1;
-                if (p < raw) {
+                if (topp) {
+                    // top-p: the raw tail first, then the selected chunks'
+                    // rows, so that the rows the cut keeps come first
+                    if (p < c.tail) {
+                        o[t] = tail_off + (int64_t)p * D + 1;
+                    } else {
+                        jr[t] = (p - c.tail) / C;
+                        add[t] = (int64_t)(p - c.tail - jr[t] * C) * D;
+                    }
+                } else if (p < raw) {
                     jr[t] = p / C;
                     add[t] = (int64_t)(p - jr[t] * C) * D;
                 } else if (p < raw + c.tail) {
@@ -1618,7 +1820,24 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
                 for (int t = 0; t < 2; ++t)
                     if (o[t] == 0) o[t] = ld_dev(ro + jr[t]);
             }
-            unval[0] = min(32, ulen - 32 * jb);
+            if (topp) {
+                // rows of chunks the cut dropped (and rows past the end) are
+                // the block's last: its length is the count of the others
+                int nv = 0;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bool valid = 32 * jb + 16 * t + lr < ulen && !((uint64_t)o[t] & kRowSkip);
+                    nv += __popcll(__ballot(valid && lg == 0));
+                    if (!valid) {  // an in-range row
+                        o[t] = 1;
+                        add[t] = 0;
+                    }
+                }
+                if (nv == 0) continue;
+                unval[0] = nv;
+            } else {
+                unval[0] = min(32, ulen - 32 * jb);
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) uoff[0][t] = (size_t)(o[t] - 1 + add[t]);
             wa.template stream<1>((const __bf16*)a.kc, (const __bf16*)a.vc, uoff, unval, 1, true,
@@ -1666,6 +1885,8 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     __syncthreads();
     if (wsum[0] != (few ? 0 : R - 1)) return;
     for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
+    if (topp)
+        for (int i = threadIdx.x; i < nA; i += kThreads) st_dev(unit_topp(a, u) + i, 0ull);
     if (threadIdx.x == 0) {
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);

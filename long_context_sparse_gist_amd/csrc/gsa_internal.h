@@ -184,6 +184,13 @@ constexpr int kRecMeta = kRecRowOffs;
 constexpr int kUnitRec = 6272;
 static_assert(64 + 2 * kRecRowOffs + 2 * kRecSlices * kRecLead <= kUnitRec, "control record");
 constexpr uint64_t kRowPastGroups = 1ull << 62;  // row-offset flag (H-GSA)
+constexpr uint64_t kRowSkip = 1ull << 61;        // row-offset flag: a chunk cut by top-p
+// Top-p in the single launch: each gist slice's (softmax maximum, sum of exp)
+// of its keys, one 64-bit word per slice after the leading keys of the record
+// (nonzero once written: the sum's bits, or those of -1 for none, above the
+// maximum's).
+constexpr int kRecTopP = 64 + 2 * kRecRowOffs + 2 * kRecSlices * kRecLead;
+constexpr int kTopPSlices = (kUnitRec - kRecTopP) / 2;
 // records per unit: 1 (flat GSA) or 2 (H-GSA)
 __device__ inline unsigned* unit_rec(const Args& a, int u, int second = 0) {
     return a.urec + ((size_t)u * a.recs_per_unit + second) * kUnitRec;
@@ -195,6 +202,7 @@ __device__ inline unsigned* unit_cntS(const Args& a, int u) { return unit_rec(a,
 __device__ inline unsigned* unit_cntP(const Args& a, int u) { return unit_rec(a, u) + 56; }  // selecting slice's partial published
 __device__ inline int64_t* unit_rowoff(const Args& a, int u) { return (int64_t*)(unit_rec(a, u) + 64); }
 __device__ inline uint64_t* unit_lead(const Args& a, int u) { return (uint64_t*)(unit_rec(a, u) + 64 + 2 * kRecRowOffs); }
+__device__ inline uint64_t* unit_topp(const Args& a, int u) { return (uint64_t*)(unit_rec(a, u) + kRecTopP); }
 __device__ inline uint64_t* unit_lead_c(const Args& a, int u) {
     return (uint64_t*)(unit_rec(a, u, 1) + 64 + 2 * kRecRowOffs);
 }
