@@ -352,17 +352,19 @@ def main():
     if args.top_p > 0.0 and (wl.hgsa or hier or (flags & gsa.GSA_SCORE_SUM_PROBS)):
         print("--top-p applies to the flat workloads with the default key", file=sys.stderr)
         sys.exit(2)
-    # one launch per call (the bf16 default key, flat or two-level; top-p with the
-    # all-gists set while the flat grid -- max(gist slices, 1 + ceil(unfolded
+    # one launch per call (the bf16 default key, flat or two-level; top-p and the
+    # sum-of-probabilities key with the all-gists set while the flat grid -- max(gist slices, 1 + ceil(unfolded
     # blocks / 4)) tasks per unit -- is resident at once on 1024 slots and a unit
     # has at most 32 gist slices, as the library plans it); else the
     # multi-launch kernels
-    single = hier is None and wl.dtype == gi.BF16 and not (flags & gsa.GSA_SCORE_SUM_PROBS)
-    if single and args.top_p > 0.0:
+    single = hier is None and wl.dtype == gi.BF16
+    if single and (args.top_p > 0.0 or (flags & gsa.GSA_SCORE_SUM_PROBS)):
+        # (the sum-of-probabilities key likewise, up to 64 gist slices per unit)
         n_a = -(-wl.num_chunks // 256)
         cap2 = min(wl.top_k, wl.num_chunks) * wl.chunk_size + wl.chunk_size - 1
         need = 1 + -(-(-(-cap2 // 32)) // 4)
-        single = not (flags & gsa.GSA_SET_SELECTED_GISTS) and not wl.hgsa and n_a <= 32 \
+        single = not (flags & gsa.GSA_SET_SELECTED_GISTS) and not wl.hgsa \
+            and n_a <= (32 if args.top_p > 0.0 else 64) \
             and wl.batch * wl.num_kv_heads * max(n_a, need) <= 1024
     seed = 1010 if hier is not None else gi.seed_of(gi.WORKLOADS.index(wl))
     peak_copy = copy_peak_gbps(dev)

@@ -418,8 +418,14 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // done, and for this slice's own stores to have landed
     auto wait_slices = [&]() {
         drain();
-        // (PER counts per slice: a slice that counts in per wavefront, 4)
-        wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)PER * (own >= 0 ? nA - 1 : nA), sc.err);
+        // (PER counts per slice: a slice that counts in per wavefront, 4; with
+        // the sum-of-probabilities key there the slices' keys come after their
+        // V passes and count in on cntS, once per slice)
+        if (PER == 4 && KIND == kListGists && (a.flags & kFlagSumProbs))
+            wait_at_least<8>(unit_cntS(a, u), (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
+        else
+            wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)PER * (own >= 0 ? nA - 1 : nA),
+                             sc.err);
         __syncthreads();
     };
     if (!fast && n > 0) {
@@ -540,8 +546,20 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             lds_barrier();
             return (fred[0] + fred[1]) + (fred[2] + fred[3]);
         };
-        // the slices' pairs (each written right after its K pass)
+        // the slices' pairs (each written right after its K pass), and (thread
+        // 64, at the same time) every other slice's wavefronts counted in, so
+        // that their key stores have landed
         const uint64_t* tp = unit_topp(a, u);
+        if (tid == 64 && nA > 1) {
+            unsigned it = 0;
+            while (ld_dev(unit_cntA(a, u)) < (unsigned)PER * (nA - 1)) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++it >= kSpinLimit) {  // never expected: report, read the keys there are
+                    st_dev(sc.err, 1u);
+                    break;
+                }
+            }
+        }
         float pm = -INFINITY, pz = 0.f;
         if (tid < nA) {
             uint64_t x = ld_dev(tp + tid);
@@ -562,10 +580,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         const float M = bmax(pm);
         const bool usable = isfinite(M);
         const float Z = bsum(usable && pm != -INFINITY ? pz * expf(pm - M) : 0.f);
-        // the selected keys: every other slice's wavefronts have counted in,
-        // so their key stores have landed
+        // the selected keys (this slice's own stores drained too)
         drain();
-        if (nA > 1) wait_at_least<8>(unit_cntA(a, u), (unsigned)PER * (nA - 1), sc.err);
         __syncthreads();
         constexpr int EPT = kRecRowOffs / kThreads;
         float kvs[EPT];
@@ -1621,7 +1637,7 @@ __device__ __forceinline__ void merge_part(const Args& a, int u, int S, int jr, 
     }
 }
 
-template <int D, int EJ>
+template <int D, int EJ, bool PROBS>
 __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, int idx, unsigned char* smem,
                                           CombineSmem& cs, FoldHdr& fh, int* wsum) {
     constexpr int NBW = kFusedTA / 128;  // 32-row gist blocks per wavefront
@@ -1649,7 +1665,8 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     const bool selector = idx == sel;
     const int cnt = max(0, min(kFusedTA, n - p0));
     const bool attn = !(a.flags & kFlagSelectedGists);
-    const bool topp = a.flags & kFlagTopP;  // (with the all-gists set only)
+    const bool topp = a.flags & kFlagTopP;      // (with the all-gists set only)
+    constexpr bool probs = PROBS;  // the sum-of-probabilities key (with the all-gists set only)
     const int ulen = c.ns * C + c.tail + (attn ? 0 : c.ns);  // unfolded list
     const int nUB = (ulen + 31) / 32;
     const int widx = idx < sel ? idx : idx - 1;
@@ -1676,7 +1693,22 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         }
         float* stash = (float*)(smem + Lds::stash(D)) + 64 * w;
         const float tau = a.tau;
+        // sum-of-probabilities key: this lane's raw scores (head lr, token
+        // 16t + 4lg + r of block j), kept until every slice's per-head
+        // maximum and sum are known
+        float zk[NBW][8];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zk[j][e] = 0.f;
         auto on_scores = [&](int j, const f32x4_t sc[2]) {
+            if (probs) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) zk[j][4 * t + r] = sc[t][r];
+                return;
+            }
             // routing keys: tau * sum over the group's heads (padding heads are 0)
             float kv = 0.f;
             int kt = -1;
@@ -1697,6 +1729,99 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         else
             wa.template stream<NBW>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, false,
                                     a.tau_log2e, lr, lg, tile, on_scores);
+        if (probs) {
+            // the sum-of-probabilities key (each head's softmax of the logits
+            // z = tau q.k over the sequence's gists, summed over the group):
+            // (1) this slice's per-head maximum and sum of exp, published
+            auto zvalid = [&](int j, int e) { return 16 * (e >> 2) + 4 * lg + (e & 3) < nval[j]; };
+            float hm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (zvalid(j, e)) hm = fmaxf(hm, zk[j][e] * tau);
+            hm = fmaxf(hm, __shfl_xor(hm, 16));
+            hm = fmaxf(hm, __shfl_xor(hm, 32));
+            if (lg == 0) cs.wm[w][lr] = hm;
+            lds_barrier();
+            const float Mh = fmaxf(fmaxf(cs.wm[0][lr], cs.wm[1][lr]), fmaxf(cs.wm[2][lr], cs.wm[3][lr]));
+            float hl = 0.f;
+            if (isfinite(Mh)) {
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (zvalid(j, e)) hl += expf(zk[j][e] * tau - Mh);
+            }
+            hl += __shfl_xor(hl, 16);
+            hl += __shfl_xor(hl, 32);
+            if (lg == 0) cs.wl[w][lr] = hl;
+            lds_barrier();
+            if (w == 0 && lg == 0 && lr < G) {
+                float* sp = (float*)(a.sp_ml + ((size_t)u * s.S1 + idx) * G + lr);
+                st_dev(sp, Mh);
+                st_dev(sp + 1, (cs.wl[0][lr] + cs.wl[1][lr]) + (cs.wl[2][lr] + cs.wl[3][lr]));
+            }
+            // (2) the V pass while the other slices' pairs land (each
+            // wavefront counts itself in, cntA, once its stores have landed);
+            // the selector, whose V pass follows its select, counts in at once
+            if (!selector) {
+                wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, [&]() {
+                    if (lane == 0) add_dev(unit_cntA(a, u), 1u);
+                });
+            } else {
+                drain();
+                __syncthreads();
+                if (threadIdx.x == 0) add_dev(unit_cntA(a, u), 4u);
+            }
+            // (3) every slice's pairs: each head's maximum and sum over the sequence
+            if (threadIdx.x == 0) {
+                unsigned it = 0;
+                while (ld_dev(unit_cntA(a, u)) < 4u * (unsigned)nA) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++it >= kSpinLimit) {  // never expected: report, fold what is there
+                        st_dev(s.err, 1u);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+            float2* pl = (float2*)smem;  // (the V tiles are free)
+            for (int i = threadIdx.x; i < nA * G; i += kThreads) {
+                const float* sp = (const float*)(a.sp_ml + (size_t)u * s.S1 * G + i);
+                pl[i] = make_float2(ld_dev(sp), ld_dev(sp + 1));
+            }
+            lds_barrier();
+            if (threadIdx.x < (unsigned)G) {
+                float M = -INFINITY, L = 0.f;
+                for (int sl = 0; sl < nA; ++sl) M = fmaxf(M, pl[sl * G + threadIdx.x].x);
+                if (isfinite(M))
+                    for (int sl = 0; sl < nA; ++sl) {
+                        const float2 v = pl[sl * G + threadIdx.x];
+                        if (v.x != -INFINITY) L += v.y * expf(v.x - M);
+                    }
+                cs.wm[0][threadIdx.x] = M;
+                cs.wl[0][threadIdx.x] = L;
+            }
+            lds_barrier();
+            // (4) the keys: the sum over the heads of each head's probability
+            const float Mg = lr < G ? cs.wm[0][lr] : 0.f, Lg = lr < G ? cs.wl[0][lr] : 0.f;
+            const bool hok = lr < G && isfinite(Mg) && Lg > 0.f;
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                float kvp = 0.f;
+                int kt = -1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = rowsum16(hok ? expf(zk[j][e] * tau - Mg) / Lg : 0.f);
+                    if (e == lr) {
+                        kvp = x;
+                        kt = 16 * (e >> 2) + 4 * lg + (e & 3);
+                    }
+                }
+                if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kvp;
+            }
+        }
         if (selector) select_prefetch<kListGists>(a, c, n, nA, pre);
         // thread t takes key slot t % 64 of wavefront t / 64
         static_assert(NBW * 32 * 4 <= kThreads, "one key slot per thread");
@@ -1734,7 +1859,11 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
             auto count_in = [&]() {
                 if (lane == 0) add_dev(unit_cntA(a, u), 1u);
             };
-            if (attn) {
+            if (probs) {  // (the V pass is done) the keys have landed: count in, cntS
+                drain();
+                __syncthreads();
+                if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
+            } else if (attn) {
                 wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, count_in);
             } else {
                 drain();
@@ -1891,6 +2020,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);
         st_dev(unit_cntP(a, u), 0u);
+        st_dev(unit_cntS(a, u), 0u);
     }
 }
 
@@ -1903,9 +2033,9 @@ __global__ __launch_bounds__(kThreads, 4) void gsa_fused_kernel(Args a, Sched s)
     __shared__ int s_flag;
     const int nA = s.units * s.S1, nC = s.units * s.S3;
     const int t = blockIdx.x;
-    if constexpr (!HIER && NBB == 0) {  // flat GSA, every task a gist slice or unfolded blocks
+    if constexpr (!HIER && (NBB == 0 || NBB == 3)) {  // flat GSA, every task a gist slice or unfolded blocks
         const int u = t / s.S1;
-        task_flat<D, EJ>(a, s, u, t - u * s.S1, smem, cs, fh, wsum);
+        task_flat<D, EJ, NBB == 3>(a, s, u, t - u * s.S1, smem, cs, fh, wsum);
     } else if (t < nA) {
         const int u = t / s.S1;
         task_slices<D, EJ, HIER ? kListMeta : kListGists>(a, s, u, t - u * s.S1, smem, cs, wsum);
@@ -1924,9 +2054,12 @@ namespace {
 template <int D, int EJ>
 void launch_fused_t(const Args& a, const Sched& s, int lds, hipStream_t st) {
     // NBB: 32-token blocks per wavefront of an unfolded task; 0: the flat
-    // kernel whose every task is a gist slice or a set of unfolded blocks
+    // kernel whose every task is a gist slice or a set of unfolded blocks, 3:
+    // the same with the sum-of-probabilities key
     if (s.hier)
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, true, 1>), dim3(s.total), dim3(kThreads), lds, st, a, s);
+    else if (s.flat && (a.flags & kFlagSumProbs))
+        hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 3>), dim3(s.total), dim3(kThreads), lds, st, a, s);
     else if (s.flat)
         hipLaunchKernelGGL((gsa_fused_kernel<D, EJ, false, 0>), dim3(s.total), dim3(kThreads), lds, st, a, s);
     else if (s.TB == 2 * kFusedTB)

@@ -58,6 +58,8 @@ struct Args {
     int32_t* cand;    // [units][cand_stride] candidate chunk ids (H-GSA)
     int cand_stride;
     float2* part_ml;  // [units][NS][G] (max in exp2 domain, sum)
+    float2* sp_ml;    // sum-of-probabilities key, single launch: [units][S1][G] each gist
+                      // slice's per-head logit maximum and sum of exp (natural units)
     float* part_acc;  // [units][NS][G][D]
     int NS;           // partial slots per unit
     int S1;           // token-list splits of the "all gists" / meta list
