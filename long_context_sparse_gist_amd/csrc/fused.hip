@@ -419,10 +419,10 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     auto wait_slices = [&]() {
         drain();
         // (PER counts per slice: a slice that counts in per wavefront, 4; with
-        // the sum-of-probabilities key there the slices' keys come after their
-        // V passes and count in on cntS, once per slice)
+        // the sum-of-probabilities key there cntA counts the slices' per-head
+        // pairs and cntS their keys)
         if (PER == 4 && KIND == kListGists && (a.flags & kFlagSumProbs))
-            wait_at_least<8>(unit_cntS(a, u), (unsigned)(own >= 0 ? nA - 1 : nA), sc.err);
+            wait_at_least<8>(unit_cntS(a, u), (unsigned)PER * (own >= 0 ? nA - 1 : nA), sc.err);
         else
             wait_at_least<8>(cand ? unit_cntC(a, u) : unit_cntA(a, u), (unsigned)PER * (own >= 0 ? nA - 1 : nA),
                              sc.err);
@@ -1762,22 +1762,16 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
                 st_dev(sp, Mh);
                 st_dev(sp + 1, (cs.wl[0][lr] + cs.wl[1][lr]) + (cs.wl[2][lr] + cs.wl[3][lr]));
             }
-            // (2) the V pass while the other slices' pairs land (each
-            // wavefront counts itself in, cntA, once its stores have landed);
-            // the selector, whose V pass follows its select, counts in at once
-            if (!selector) {
-                wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, [&]() {
-                    if (lane == 0) add_dev(unit_cntA(a, u), 1u);
-                });
-            } else {
-                drain();
-                __syncthreads();
-                if (threadIdx.x == 0) add_dev(unit_cntA(a, u), 4u);
-            }
-            // (3) every slice's pairs: each head's maximum and sum over the sequence
+            // (2) counted in (cntA) once the pair has landed; (3) every
+            // slice's pairs: each head's maximum and sum over the sequence (the
+            // keys, and the select, wait for the slowest slice's K pass: the V
+            // passes, which do not, follow)
+            drain();
+            __syncthreads();
             if (threadIdx.x == 0) {
+                add_dev(unit_cntA(a, u), 1u);
                 unsigned it = 0;
-                while (ld_dev(unit_cntA(a, u)) < 4u * (unsigned)nA) {
+                while (ld_dev(unit_cntA(a, u)) < (unsigned)nA) {
                     __builtin_amdgcn_s_sleep(2);
                     if (++it >= kSpinLimit) {  // never expected: report, fold what is there
                         st_dev(s.err, 1u);
@@ -1786,7 +1780,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
                 }
             }
             __syncthreads();
-            float2* pl = (float2*)smem;  // (the V tiles are free)
+            float2* pl = (float2*)smem;  // (the V tiles are not in use yet)
             for (int i = threadIdx.x; i < nA * G; i += kThreads) {
                 const float* sp = (const float*)(a.sp_ml + (size_t)u * s.S1 * G + i);
                 pl[i] = make_float2(ld_dev(sp), ld_dev(sp + 1));
@@ -1859,10 +1853,10 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
             auto count_in = [&]() {
                 if (lane == 0) add_dev(unit_cntA(a, u), 1u);
             };
-            if (probs) {  // (the V pass is done) the keys have landed: count in, cntS
-                drain();
-                __syncthreads();
-                if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
+            if (probs) {  // the V pass, each wavefront counting its keys in on cntS
+                wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, [&]() {
+                    if (lane == 0) add_dev(unit_cntS(a, u), 1u);
+                });
             } else if (attn) {
                 wa.template vpass<NBW>((const __bf16*)a.vc, off, nbw, P, tile, count_in);
             } else {
