@@ -1024,8 +1024,8 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
 // meta-gists or the candidate gists (H-GSA).  Scores the rows (routing keys),
 // attends them when the set needs them (all gists, all meta-gists), publishes
 // the keys sorted by bucket and its partial.  The list's last slice runs the
-// list's select as soon as its partial is written, and counts the partial in
-// after the select.
+// list's select as soon as its partial is written: it counts the partial in
+// at the select's first barrier, once its stores have completed anyway.
 template <int D, int EJ, int KIND>
 __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u, int idx,
                                             unsigned char* smem, CombineSmem& cs, int* wsum) {
@@ -1218,10 +1218,17 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     __builtin_amdgcn_s_setprio(2);
     if (kind == kListGists)
         for (int i = c.n + threadIdx.x; i < a.num_chunks; i += kThreads) keys[i] = -INFINITY;
+    // the partial's count (cntP): by thread 0 once every wavefront has
+    // drained, at the select's first barrier (the unfolded task that folds
+    // this partial waits for it)
+    const bool partial = attn && cnt > 0;
+    bool counted = false;
+    auto count_partial = [&]() {
+        if (partial && threadIdx.x == 0) add_dev(unit_cntP(a, u), 1u);
+        counted = true;
+    };
     if (!prefetched) select_prefetch<KIND>(a, c, n, nA, pre);
-    // (the select does not wait for this slice's partial to land: it is
-    // counted in after the select, cntP, where only the merge reads it)
-    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
+    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, count_partial);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
@@ -1235,10 +1242,8 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     // unit's merging task resets the record only after every select says so
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        if (attn && cnt > 0) add_dev(unit_cntP(a, u), 1u);  // the partial
-        add_dev(unit_cntS(a, u), 1u);
-    }
+    if (!counted) count_partial();
+    if (threadIdx.x == 0) add_dev(unit_cntS(a, u), 1u);
 }
 
 // Combine the 4 wavefronts' online-softmax states with the folded gist state
