@@ -7,9 +7,10 @@
 // into the paged cache.
 //
 // Many queries share the same gist rows, so this is a dense contraction and
-// runs on MFMA.  A workgroup owns 128 columns of one (batch, kv-head) unit --
-// column j is query t = j / G, head j % G of the GQA group -- as 8 blocks of 16
-// (two per wavefront).  It streams key blocks of 32 rows: first the gists of
+// runs on MFMA.  A workgroup owns 64 columns of one (batch, kv-head) unit --
+// column j is query t = j / G, head j % G of the GQA group -- as 4 blocks of 16
+// (one per wavefront: few enough registers for 4 workgroups per compute unit,
+// whose loads hide each other's latency).  It streams key blocks of 32 rows: first the gists of
 // every chunk up to the last query's, then the slots of the chunks its
 // queries lie in.  Each block's K and V rows go from global memory straight
 // into LDS (global_load_lds, the four wavefronts sharing the loads and the
@@ -39,7 +40,7 @@ struct PrefillArgs {
 namespace {
 
 constexpr int kPThreads = 256;
-constexpr int kNCB = 2;                   // 16-column blocks per wavefront
+constexpr int kNCB = 1;                   // 16-column blocks per wavefront
 constexpr int kPCols = 4 * kNCB * 16;     // columns per workgroup
 constexpr int kPBtLds = 7936;             // block-table entries kept in LDS (64 KB in all at d = 128)
 
@@ -79,7 +80,7 @@ __device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, siz
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int KK = D / 32, DB = D / 16, CPR = D / 8, TILE = PTiles<D>::TILE;
     unsigned char* ktile = smem;             // 2 buffers
