@@ -1133,11 +1133,27 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
     bool ownv = false;
     float* keys = meta ? a.mkeys + (size_t)u * a.max_meta
                 : cand ? a.ckeys + (size_t)u * a.cand_stride : a.keys + (size_t)u * a.key_stride;
+    WaveAttnL<D> wa;
+    unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
+    bf16x8_t mP[NBW];  // meta slices: the K pass's probabilities (the PV operand)
+    int nbw = 0;
+    // this slice's partial (its wavefronts' states combined; stores in flight)
+    auto publish = [&]() {
+        const size_t pbase = ((size_t)u * a.NS + idx) * G;
+        combine_waves<D>(
+            wa, a.tau_log2e, G, (float*)smem, cs,
+            [&](int h, int d, float v) { st_dev(a.part_acc + (pbase + h) * D + d, v); },
+            [&](int h, float m2, float l) {
+                float* p = (float*)(a.part_ml + pbase + h);
+                st_dev(p, m2);
+                st_dev(p + 1, l);
+            });
+    };
 
     if (cnt > 0) {
         int nval[NBW];
         const int nblk = (cnt + 31) / 32;
-        const int nbw = nblk > w ? (nblk - w + 3) / 4 : 0;
+        nbw = nblk > w ? (nblk - w + 3) / 4 : 0;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             nval[j] = max(0, min(32, cnt - 32 * (w + 4 * j)));
@@ -1146,31 +1162,37 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             for (int t = 0; t < 2; ++t)
                 if (16 * t + lr >= nval[j]) off[j][t] = __shfl(off[j][0], lane & 48);
         }
-        WaveAttnL<D> wa;
         wa.init((const __bf16*)a.q + ((size_t)c.b * a.Hq + (size_t)c.g * G) * D, G, lr, lg);
-        unsigned char* tile = smem + (size_t)w * WaveAttnL<D>::TILE_BYTES;
         float* stash = (float*)(smem + Lds::stash(D)) + 64 * w;
         const float tau = a.tau;
-        wa.template stream<NBW>(
-            (const __bf16*)(meta ? a.km : a.kc), (const __bf16*)(meta ? a.vm : a.vc), off, nval, nbw, attn,
-            a.tau_log2e, lr, lg, tile, [&](int j, const f32x4_t sc[2]) {
-                // routing keys: tau * sum over the group's heads (padding heads are 0)
-                float kv = 0.f;
-                int kt = -1;
+        auto on_scores = [&](int j, const f32x4_t sc[2]) {
+            // routing keys: tau * sum over the group's heads (padding heads are 0)
+            float kv = 0.f;
+            int kt = -1;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = rowsum16(sc[t][r]);
-                        if (4 * t + r == lr) {
-                            kv = x * tau;
-                            kt = 16 * t + 4 * lg + r;
-                        }
+                for (int r = 0; r < 4; ++r) {
+                    float x = rowsum16(sc[t][r]);
+                    if (4 * t + r == lr) {
+                        kv = x * tau;
+                        kt = 16 * t + 4 * lg + r;
                     }
-                // park the key in LDS (no global store here: a store in
-                // flight would hold up the next wait on this wavefront's loads)
-                if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kv;
-            });
+                }
+            // park the key in LDS (no global store here: a store in
+            // flight would hold up the next wait on this wavefront's loads)
+            if (kt >= 0 && kt < nval[j]) stash[32 * j + kt] = kv;
+        };
+        if (meta) {
+            // meta slices: K rows first, keys out, then the V rows (every
+            // slice's K loads go ahead of any V load, so the meta select,
+            // which waits for all of a unit's keys, starts about half a
+            // stream earlier)
+            wa.template kpass<NBW>((const __bf16*)a.km, off, nval, nbw, a.tau_log2e, lg, mP, on_scores);
+        } else {
+            wa.template stream<NBW>((const __bf16*)a.kc, (const __bf16*)a.vc, off, nval, nbw, attn,
+                                    a.tau_log2e, lr, lg, tile, on_scores);
+        }
         if (selector) {
             select_prefetch<KIND>(a, c, n, nA, pre);
             prefetched = true;
@@ -1189,21 +1211,14 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         uint64_t* lead = nA > kRecSlices ? nullptr : (cand ? unit_lead_c(a, u) : unit_lead(a, u)) + idx * kFSelL;
         if (!selector) {
             bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+            // (the bucket sort's LDS is free: its last barrier)
+            if (meta) wa.template vpass<NBW>((const __bf16*)a.vm, off, nbw, mP, tile, []() {});
         } else {  // the select takes this slice's keys as they are
             ownk = (uint64_t)order_key(kv) | ((uint64_t)(uint32_t)(p0 + kpos) << 32);
             ownv = kpos < cnt;
         }
-        if (attn) {
-            const size_t pbase = ((size_t)u * a.NS + idx) * G;
-            combine_waves<D>(
-                wa, a.tau_log2e, G, (float*)smem, cs,
-                [&](int h, int d, float v) { st_dev(a.part_acc + (pbase + h) * D + d, v); },
-                [&](int h, float m2, float l) {
-                    float* p = (float*)(a.part_ml + pbase + h);
-                    st_dev(p, m2);
-                    st_dev(p + 1, l);
-                });
-        }
+        // (a meta selector's V rows and partial follow its select)
+        if (attn && !(meta && selector)) publish();
     }
     if (!selector) {
         drain();
@@ -1228,7 +1243,10 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
         counted = true;
     };
     if (!prefetched) select_prefetch<KIND>(a, c, n, nA, pre);
-    select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, count_partial);
+    if (meta)  // its partial is not made yet
+        select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, NoDrain{});
+    else
+        select_fused<KIND>(a, s, c, n, nA, keys, smem, pre, idx, ownk, ownv, count_partial);
     // return the leading keys in the record to zero: each has been read by the
     // select, or every slice is done (the select waited for it)
     if (nA <= kRecSlices) {
@@ -1237,6 +1255,16 @@ __device__ __forceinline__ void task_slices(const Args& a, const Sched& s, int u
             const int sl = i / kFSelL;
             if (i - sl * kFSelL < min(s.TA, n - sl * s.TA)) st_dev(lead + i, 0ull);
         }
+    }
+    if (meta && partial) {
+        // the V rows after the select (only the K pass's probabilities,
+        // running maximum and sum were live across it: O is still zero)
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();  // the select's LDS is free for the V tiles
+#pragma unroll
+        for (int db = 0; db < WaveAttnL<D>::DB; ++db) wa.o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        wa.template vpass<NBW>((const __bf16*)a.vm, off, nbw, mP, tile, []() {});
+        publish();
     }
     // the record entries this select wrote or cleared are in place: the
     // unit's merging task resets the record only after every select says so
