@@ -45,7 +45,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, off_spairs_c, off_hlog, off_nsel, off_spml, total;
+        off_spairs, off_spairs_c, off_hlog, off_nsel, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -140,19 +140,22 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
         // set when its grid is resident at once (the per-slice layout) and the
         // record holds every slice's (max, sum) pair; else multi-launch)
         // The sum-of-probabilities key likewise, with every slice's per-head
-        // maximum and sum in the workspace (keys after every slice's pairs)
+        // maximum and sum in a second record of the unit (keys after every
+        // slice's pairs)
         bool topp_ok = false, probs_ok = false;
         if (!pl.hier && !(p->flags & GSA_SET_SELECTED_GISTS)) {
             const long nA = (M + gsa::kFusedTA - 1) / gsa::kFusedTA;
             const long need = 1 + ((cap2 + 31) / 32 + 3) / 4;
             const bool resident = units * (need > nA ? need : nA) <= kFusedSlots;
             topp_ok = (p->flags & GSA_SELECT_TOP_P) && nA <= gsa::kTopPSlices && resident;
-            probs_ok = (p->flags & GSA_SCORE_SUM_PROBS) && nA <= gsa::kRecSlices && resident;
+            static_assert(gsa::kRecSlices * 16 <= gsa::kRecHeadPairs, "(slice, head) pairs of a record");
+            probs_ok = (p->flags & GSA_SCORE_SUM_PROBS) && nA <= gsa::kRecSlices && a.G <= 16 && resident;
         }
-        pl.fused = pl.mfma && units * (pl.hier ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
+        const bool two = pl.hier || probs_ok;  // records per unit
+        pl.fused = pl.mfma && units * (two ? 2 : 1) <= kMaxFusedUnits && ksel <= gsa::kRecRowOffs &&
                    kmeta <= gsa::kRecMeta && (!(p->flags & GSA_SCORE_SUM_PROBS) || probs_ok) &&
                    (!(p->flags & GSA_SELECT_TOP_P) || topp_ok);
-        a.recs_per_unit = pl.hier ? 2 : 1;
+        a.recs_per_unit = two ? 2 : 1;
     }
     // H-GSA's meta slices and candidate tasks take half as many rows: its
     // launch is a chain of latency-bound steps, not a bandwidth-bound stream
@@ -216,7 +219,6 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_spairs = off; off += align_up(sizeof(uint64_t) * fslices * gsa::kFusedTA);
     pl.off_spairs_c = off; off += align_up(sizeof(uint64_t) * (size_t)units * pl.sc.S3 * gsa::kFusedTA);
     const bool probs = !pl.hier && (p->flags & GSA_SCORE_SUM_PROBS);
-    pl.off_spml = off;  off += align_up(sizeof(float) * 2 * (probs && pl.fused ? (size_t)units * pl.S1 * a.G : 0));
     pl.off_hlog = off;  off += align_up(sizeof(float) * (probs && !pl.fused ? (size_t)units * a.G * M : 0));
     const bool topp = !pl.hier && (p->flags & GSA_SELECT_TOP_P);
     pl.off_nsel = off;  off += align_up(sizeof(int32_t) * (topp ? (size_t)units : 0));
@@ -461,7 +463,6 @@ gsa_status_t decode_flat(Plan& pl, const gsa_params_t* p, const gsa_kv_t* kv, co
     a.keys = scores ? scores : (float*)(ws + pl.off_keys);
     a.sel = sel_idx ? sel_idx : (int32_t*)(ws + pl.off_sel);
     a.hlog = (p->flags & GSA_SCORE_SUM_PROBS) && !pl.fused ? (float*)(ws + pl.off_hlog) : nullptr;
-    a.sp_ml = (float2*)(ws + pl.off_spml);
     a.top_p = (p->flags & GSA_SELECT_TOP_P) ? p->top_p : 0.f;
     a.nsel = nullptr;  // set once the top-p counts are written
     a.part_ml = (float2*)(ws + pl.off_ml);

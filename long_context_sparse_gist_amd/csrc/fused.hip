@@ -1790,33 +1790,28 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
             hl += __shfl_xor(hl, 32);
             if (lg == 0) cs.wl[w][lr] = hl;
             lds_barrier();
+            uint64_t* hp = unit_hpairs(a, u);
             if (w == 0 && lg == 0 && lr < G) {
-                float* sp = (float*)(a.sp_ml + ((size_t)u * s.S1 + idx) * G + lr);
-                st_dev(sp, Mh);
-                st_dev(sp + 1, (cs.wl[0][lr] + cs.wl[1][lr]) + (cs.wl[2][lr] + cs.wl[3][lr]));
+                const float Ls = (cs.wl[0][lr] + cs.wl[1][lr]) + (cs.wl[2][lr] + cs.wl[3][lr]);
+                st_dev(hp + idx * G + lr,
+                       ((uint64_t)(__float_as_uint(Ls) | 0x80000000u) << 32) | __float_as_uint(Mh));
             }
-            // (2) counted in (cntA) once the pair has landed; (3) every
-            // slice's pairs: each head's maximum and sum over the sequence (the
-            // keys, and the select, wait for the slowest slice's K pass: the V
-            // passes, which do not, follow)
-            drain();
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                add_dev(unit_cntA(a, u), 1u);
-                unsigned it = 0;
-                while (ld_dev(unit_cntA(a, u)) < (unsigned)nA) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++it >= kSpinLimit) {  // never expected: report, fold what is there
+            // (2) every slice's pairs, each word polled until written: each
+            // head's maximum and sum over the sequence (the keys, and the
+            // select, wait for the slowest slice's K pass: the V passes, which
+            // do not, follow)
+            float2* pl = (float2*)smem;  // (the V tiles are not in use yet)
+            for (int i = threadIdx.x; i < nA * G; i += kThreads) {
+                uint64_t x = ld_dev(hp + i);
+                for (unsigned it = 0; x == 0ull; ++it) {
+                    if (it >= kSpinLimit) {  // never expected: report, fold what is there
                         st_dev(s.err, 1u);
                         break;
                     }
+                    __builtin_amdgcn_s_sleep(2);
+                    x = ld_dev(hp + i);
                 }
-            }
-            __syncthreads();
-            float2* pl = (float2*)smem;  // (the V tiles are not in use yet)
-            for (int i = threadIdx.x; i < nA * G; i += kThreads) {
-                const float* sp = (const float*)(a.sp_ml + (size_t)u * s.S1 * G + i);
-                pl[i] = make_float2(ld_dev(sp), ld_dev(sp + 1));
+                pl[i] = make_float2(__uint_as_float((uint32_t)x), __uint_as_float((uint32_t)(x >> 32) & 0x7fffffffu));
             }
             lds_barrier();
             if (threadIdx.x < (unsigned)G) {
@@ -2043,6 +2038,8 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     for (int i = threadIdx.x; i < c.ns; i += kThreads) st_dev(unit_rowoff(a, u) + i, (int64_t)0);
     if (topp)
         for (int i = threadIdx.x; i < nA; i += kThreads) st_dev(unit_topp(a, u) + i, 0ull);
+    if (probs)
+        for (int i = threadIdx.x; i < nA * G; i += kThreads) st_dev(unit_hpairs(a, u) + i, 0ull);
     if (threadIdx.x == 0) {
         st_dev(unit_cntA(a, u), 0u);
         st_dev(unit_cntB(a, u), 0u);

@@ -58,8 +58,6 @@ struct Args {
     int32_t* cand;    // [units][cand_stride] candidate chunk ids (H-GSA)
     int cand_stride;
     float2* part_ml;  // [units][NS][G] (max in exp2 domain, sum)
-    float2* sp_ml;    // sum-of-probabilities key, single launch: [units][S1][G] each gist
-                      // slice's per-head logit maximum and sum of exp (natural units)
     float* part_acc;  // [units][NS][G][D]
     int NS;           // partial slots per unit
     int S1;           // token-list splits of the "all gists" / meta list
@@ -193,7 +191,13 @@ constexpr uint64_t kRowSkip = 1ull << 61;        // row-offset flag: a chunk cut
 // maximum's).
 constexpr int kRecTopP = 64 + 2 * kRecRowOffs + 2 * kRecSlices * kRecLead;
 constexpr int kTopPSlices = (kUnitRec - kRecTopP) / 2;
-// records per unit: 1 (flat GSA) or 2 (H-GSA)
+// The sum-of-probabilities key in the single launch: each gist slice's
+// per-head logit maximum and sum of exp (natural units), one 64-bit word per
+// (slice, head) from word 64 of the unit's second record: the maximum's bits,
+// above them the sum's with the sign bit set (nonzero once written).
+constexpr int kRecHeadPairs = (kUnitRec - 64) / 2;
+// records per unit: 1 (flat GSA), 2 (H-GSA; flat GSA with the
+// sum-of-probabilities key)
 __device__ inline unsigned* unit_rec(const Args& a, int u, int second = 0) {
     return a.urec + ((size_t)u * a.recs_per_unit + second) * kUnitRec;
 }
@@ -209,6 +213,7 @@ __device__ inline uint64_t* unit_lead_c(const Args& a, int u) {
     return (uint64_t*)(unit_rec(a, u, 1) + 64 + 2 * kRecRowOffs);
 }
 __device__ inline unsigned* unit_meta(const Args& a, int u) { return unit_rec(a, u, 1) + 64; }
+__device__ inline uint64_t* unit_hpairs(const Args& a, int u) { return (uint64_t*)(unit_rec(a, u, 1) + 64); }
 
 enum SelectMode { kSelGists = 0, kSelMeta = 1, kSelCand = 2 };
 hipError_t launch_select(const Args& a, int mode, hipStream_t st);
