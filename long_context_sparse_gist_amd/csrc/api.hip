@@ -29,6 +29,11 @@ constexpr long kMaxFusedUnits = 512;
 // compute units, 4 each): the flat plan adds tasks that only stream unfolded
 // blocks (and wait for the select first) only while the whole grid fits.
 constexpr long kFusedSlots = 1024;
+// V-pass pacing of the single launch: loads of scattered 256-byte rows reach
+// about 6.5 TB/s on an MI355X (6.5e6 bytes per microsecond); a launch's
+// workgroups start within about 1.5 us
+constexpr double kVHoldBytesPerUs = 6.5e6;
+constexpr double kVHoldRampUs = 1.5;
 static_assert(kHdrWords + (size_t)kMaxFusedUnits * gsa::kUnitRec <= kCtlWords, "control block");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -203,6 +208,18 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.sc.TB = TB;
     pl.sc.total = (int)(units * (pl.S1 + pl.sc.S3 + pl.S2));
     pl.sc.hier = pl.hier ? 1 : 0;
+    // V-pass pacing: the gist slices of the per-slice layout (K rows first)
+    // start their V rows only once every slice's K rows would have streamed
+    // (the launch's K bytes at the rate loads reach on this part, plus the
+    // dispatch ramp).  Otherwise the first slices' V loads take bandwidth
+    // from the last slices' K loads, which their units' selects wait for
+    // (about 1.4 us of the 128K-token qwen2 step; the wait is a clock
+    // compare, never a dependency).  H-GSA's meta slices gained nothing.
+    pl.sc.vhold = 0;
+    if (pl.fused && pl.sc.flat) {
+        const double kbytes = (double)units * (double)M * a.D * 2.0;
+        pl.sc.vhold = (unsigned)((kVHoldRampUs + kbytes / kVHoldBytesPerUs) * 100.0);
+    }
     a.key_stride = kv->num_chunks;
     a.cand_stride = pl.cand_cap;
     size_t off = 0;

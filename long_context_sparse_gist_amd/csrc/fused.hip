@@ -93,6 +93,10 @@ __device__ inline unsigned add_dev(unsigned* p, unsigned v) {
 }
 // wait until this thread's memory operations have completed
 __device__ inline void drain() { __builtin_amdgcn_s_waitcnt(0); }
+// wait until the 100 MHz wall clock reaches t (pacing only: no data depends on it)
+__device__ inline void hold_until(unsigned long long t) {
+    while (wall_clock64() < t) __builtin_amdgcn_s_sleep(8);
+}
 
 // Buffer view of `bytes` bytes at p (raw, 32-bit data format word).  A load at
 // an offset at or past the end reads 0 and touches no memory: the folds use
@@ -1703,6 +1707,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
     const int ulen = c.ns * C + c.tail + (attn ? 0 : c.ns);  // unfolded list
     const int nUB = (ulen + 31) / 32;
     const int widx = idx < sel ? idx : idx - 1;
+    const unsigned long long t_start = wall_clock64();
     float* keys = a.keys + (size_t)u * a.key_stride;
 
     WaveAttnL<D> wa;
@@ -1875,6 +1880,7 @@ __device__ __forceinline__ void task_flat(const Args& a, const Sched& s, int u, 
             uint64_t* pairs = a.spairs + ((size_t)u * s.S1 + idx) * kFusedTA;
             uint64_t* lead = nA > kRecSlices ? nullptr : unit_lead(a, u) + idx * kFSelL;
             bucket_slice(pairs, lead, p0, kv, kpos < cnt ? kpos : -1, smem, wsum);
+            hold_until(t_start + s.vhold);  // (V-pass pacing: the launch's K rows go first)
             // V pass over this slice's gists; each wavefront counts itself in
             // (cntA) once its stores have landed, which the wait for its first
             // V block covers

@@ -154,6 +154,9 @@ struct Sched {
     int flat;          // flat GSA, one launch: 1 = every task owns a gist slice or only
                        // unfolded blocks (S1 tasks per unit, the grid resident at once),
                        // 0 = gist slices of every unit first, then unfolded tasks
+    unsigned vhold;    // V-pass pacing of the per-slice layout's gist slices: a slice
+                       // starts its V rows no earlier than this many ticks of the 100 MHz
+                       // clock after it started (0: at once)
 };
 hipError_t launch_fused(const Args& a, const Sched& s, hipStream_t st);
 constexpr int kFusedTA = 256;  // gists per gist-slice task (two 32-token blocks per wavefront);
