@@ -530,7 +530,10 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // row offset that marks them skipped.
     constexpr bool kTopP = KIND == kListGists && PER == 4;
     const bool topp = kTopP && (a.flags & kFlagTopP);
-    auto topp_emit = [&](const int* idl) {
+    // place(tk): writes the order key of every selected entry at its index in
+    // idl (ascending) into tk, from keys held in registers, and says whether
+    // it did (else the keys are read back from memory)
+    auto topp_emit = [&](const int* idl, auto&& place) {
         float* fred = (float*)sh.hist;                  // wavefront partials
         uint32_t* tk = (uint32_t*)sh.uh;                // order keys of the selection
         int* trk = (int*)sh.uh + kRecRowOffs;           // their ranks in key order
@@ -584,20 +587,31 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         const float M = bmax(pm);
         const bool usable = isfinite(M);
         const float Z = bsum(usable && pm != -INFINITY ? pz * expf(pm - M) : 0.f);
-        // the selected keys (this slice's own stores drained too)
-        drain();
-        __syncthreads();
         constexpr int EPT = kRecRowOffs / kThreads;
         float kvs[EPT];
         int ids_[EPT];
+        if (place(tk)) {
+            lds_barrier();
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = EPT * tid + e;
-            ids_[e] = i < keff ? idl[i] : 0;
-            kvs[e] = i < keff ? ld_dev(keys + ids_[e]) : 0.f;
-            if (i < keff) {
-                tk[i] = order_key(kvs[e]);
-                trk[i] = 0;
+            for (int e = 0; e < EPT; ++e) {
+                const int i = EPT * tid + e;
+                ids_[e] = i < keff ? idl[i] : 0;
+                kvs[e] = i < keff ? order_key_value(tk[i]) : 0.f;
+                if (i < keff) trk[i] = 0;
+            }
+        } else {
+            // the selected keys from memory (this slice's own stores drained too)
+            drain();
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const int i = EPT * tid + e;
+                ids_[e] = i < keff ? idl[i] : 0;
+                kvs[e] = i < keff ? ld_dev(keys + ids_[e]) : 0.f;
+                if (i < keff) {
+                    tk[i] = order_key(kvs[e]);
+                    trk[i] = 0;
+                }
             }
         }
         lds_barrier();
@@ -669,14 +683,22 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < keff && trk[EPT * tid + e] < need) ? 1 : 0;
         int ktot;
         int pos = block_excl_scan<kThreads>(keep, &ktot, sh.wsum);
+        // the kept entries ascending into LDS (the weights' place), then one
+        // entry per thread out, the cut ones marked skipped
+        int* kept_ids = (int*)sh.cidx;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int i = EPT * tid + e;
-            if (i < keff && trk[i] < need) emit(pos++, ids_[e]);
+            if (i < keff && trk[i] < need) kept_ids[pos++] = ids_[e];
         }
-        for (int i = need + tid; i < keff; i += kThreads) {
-            st_dev(out + i, (int32_t)-1);
-            st_dev(ro + i, (int64_t)kRowSkip);
+        lds_barrier();
+        for (int i = tid; i < keff; i += kThreads) {
+            if (i < need) {
+                emit(i, kept_ids[i]);
+            } else {
+                st_dev(out + i, (int32_t)-1);
+                st_dev(ro + i, (int64_t)kRowSkip);
+            }
         }
     };
     if (keff == n) {
@@ -686,7 +708,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 int* idl = (int*)sh.ckey;
                 for (int i = tid; i < n; i += kThreads) idl[i] = i;
                 lds_barrier();
-                topp_emit(idl);
+                topp_emit(idl, [](uint32_t*) { return false; });
                 return fast;
             }
         }
@@ -784,6 +806,9 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
         }
     };
     bool general = !fast;
+    uint32_t rk[KR];  // this thread's share of the second round's parked keys
+    int ri[KR];
+    int nr2k = 0;      // how many were parked (0: no second round)
     if (fast) {
         constexpr bool kDrain = !__is_same(Drained, NoDrain);
         if (kDrain) {
@@ -852,11 +877,10 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             __syncthreads();
             find_boundary();  // exact from bT up: b0
             const int nr2 = sh.nr2;
+            nr2k = nr2 <= kFSelCand ? nr2 : 0;
             if (nr2 > kFSelCand) {
                 general = true;
             } else {
-                uint32_t rk[KR];  // this thread's share of the parked keys
-                int ri[KR];
 #pragma unroll
                 for (int j = 0; j < KR; ++j) {
                     const int q = tid + j * kThreads;
@@ -896,7 +920,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 for (int j = 0; j < kRecRowOffs / kThreads; ++j)
                     if (tid + j * kThreads < keff) idl[tid + j * kThreads] = mi[j];
                 lds_barrier();
-                topp_emit(idl);
+                topp_emit(idl, [](uint32_t*) { return false; });
                 return fast;
             }
         }
@@ -1002,9 +1026,11 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             c2 += __popcll(sb[i]);
         }
         int pos = wave_prefix_incl_dpp(c2) - c2;
+        int* wpre = (int*)sh.tiebits;  // (top-p) selected ids before each bitmap word
 #pragma unroll
         for (int i = 0; i < WL; ++i) {
             uint64_t x = sb[i];
+            if (kTopP && topp) wpre[WL * lane + i] = pos;
             while (x) {
                 const int bit = __ffsll((unsigned long long)x) - 1;
                 x &= x - 1ull;
@@ -1016,7 +1042,23 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     park_kept();
     if constexpr (kTopP) {
         if (topp) {
-            topp_emit(ids);
+            // every selected entry is a candidate some thread holds (up front,
+            // of its own slice, or parked in the second round); its index in
+            // ids: the selected ids before its bitmap word and below it there
+            topp_emit(ids, [&](uint32_t* tk) {
+                const int* wpre = (const int*)sh.tiebits;
+                auto put = [&](uint32_t key, int id) {
+                    const uint64_t wb = sh.selbits[id >> 6], bit = 1ull << (id & 63);
+                    if (wb & bit) tk[wpre[id >> 6] + __popcll(wb & (bit - 1ull))] = key;
+                };
+#pragma unroll
+                for (int j = 0; j <= KQ; ++j)
+                    if (up_used(j) && up_valid(j)) put((uint32_t)up_key(j), (int)(up_key(j) >> 32));
+#pragma unroll
+                for (int j = 0; j < KR; ++j)
+                    if (tid + j * kThreads < nr2k) put(rk[j], ri[j]);
+                return true;
+            });
             return fast;
         }
     }

@@ -109,6 +109,11 @@ __device__ inline uint32_t order_key(float f) {
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// The float an order key was made from (0: a NaN; -0 comes back as +0).
+__device__ inline float order_key_value(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
 // Sum / max over the four 16-lane rows at one column (lanes l, l^16, l^32,
 // l^48); every one of them gets the result.  A lane swap between the wave's
