@@ -530,43 +530,24 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
     // row offset that marks them skipped.
     constexpr bool kTopP = KIND == kListGists && PER == 4;
     const bool topp = kTopP && (a.flags & kFlagTopP);
-    // place(tk): writes the order key of every selected entry at its index in
-    // idl (ascending) into tk, from keys held in registers, and says whether
-    // it did (else the keys are read back from memory)
+    // place(tc): writes every selected entry's order key << 32 | ~list index
+    // at its index in idl (ascending) into tc, from keys held in registers,
+    // and says whether it did (else the keys are read back from memory)
     auto topp_emit = [&](const int* idl, auto&& place) {
-        float* fred = (float*)sh.hist;                  // wavefront partials
-        uint32_t* tk = (uint32_t*)sh.uh;                // order keys of the selection
-        int* trk = (int*)sh.uh + kRecRowOffs;           // their ranks in key order
-        float* twr = (float*)sh.cidx;                   // selection weights by rank
+        float* fred = (float*)sh.hist;     // the softmax maximum and normaliser
+        uint64_t* tc = (uint64_t*)sh.uh;   // the selection: order key << 32 | ~list index
+        int* trk = (int*)sh.ckey;          // their ranks in key order (in idl's place)
+        float* twr = (float*)sh.cidx;      // selection weights by rank
         static_assert(2 * kRecRowOffs <= kBins && kRecRowOffs <= kFSelCand, "top-p arrays");
-        auto bmax = [&](float x) {
-            for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-            lds_barrier();
-            if (lane == 0) fred[w] = x;
-            lds_barrier();
-            return fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
-        };
-        auto bsum = [&](float x) {
-            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-            lds_barrier();
-            if (lane == 0) fred[w] = x;
-            lds_barrier();
-            return (fred[0] + fred[1]) + (fred[2] + fred[3]);
-        };
-        // the slices' pairs (each written right after its K pass), and (thread
-        // 64, at the same time) every other slice's wavefronts counted in, so
-        // that their key stores have landed
+        constexpr int EPT = kRecRowOffs / kThreads;
+        // this thread's entries of idl (each read by the thread that then
+        // zeroes its rank there)
+        int ids_[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) ids_[e] = EPT * tid + e < keff ? idl[EPT * tid + e] : 0;
+        // the slices' pairs, each written right after its K pass (all in
+        // wavefront 0: at most kTopPSlices slices)
         const uint64_t* tp = unit_topp(a, u);
-        if (tid == 64 && nA > 1) {
-            unsigned it = 0;
-            while (ld_dev(unit_cntA(a, u)) < (unsigned)PER * (nA - 1)) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++it >= kSpinLimit) {  // never expected: report, read the keys there are
-                    st_dev(sc.err, 1u);
-                    break;
-                }
-            }
-        }
         float pm = -INFINITY, pz = 0.f;
         if (tid < nA) {
             uint64_t x = ld_dev(tp + tid);
@@ -584,57 +565,71 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 pz = zz > 0.f ? zz : 0.f;
             }
         }
-        const float M = bmax(pm);
-        const bool usable = isfinite(M);
-        const float Z = bsum(usable && pm != -INFINITY ? pz * expf(pm - M) : 0.f);
-        constexpr int EPT = kRecRowOffs / kThreads;
-        float kvs[EPT];
-        int ids_[EPT];
-        if (place(tk)) {
-            lds_barrier();
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const int i = EPT * tid + e;
-                ids_[e] = i < keff ? idl[i] : 0;
-                kvs[e] = i < keff ? order_key_value(tk[i]) : 0.f;
-                if (i < keff) trk[i] = 0;
+        // the selected keys: from the threads' registers, or from memory once
+        // every other slice's wavefronts have counted in (their key stores
+        // have landed; this slice's own drained too)
+        if (!place(tc)) {
+            if (tid == 0 && nA > 1) {
+                unsigned it = 0;
+                while (ld_dev(unit_cntA(a, u)) < (unsigned)PER * (nA - 1)) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++it >= kSpinLimit) {  // never expected: report, read the keys there are
+                        st_dev(sc.err, 1u);
+                        break;
+                    }
+                }
             }
-        } else {
-            // the selected keys from memory (this slice's own stores drained too)
             drain();
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 const int i = EPT * tid + e;
-                ids_[e] = i < keff ? idl[i] : 0;
-                kvs[e] = i < keff ? ld_dev(keys + ids_[e]) : 0.f;
-                if (i < keff) {
-                    tk[i] = order_key(kvs[e]);
-                    trk[i] = 0;
-                }
+                if (i < keff)
+                    tc[i] = ((uint64_t)order_key(ld_dev(keys + ids_[e])) << 32) | (uint32_t)~ids_[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (EPT * tid + e < keff) trk[EPT * tid + e] = 0;
+        if (w == 0) {  // M: the largest key; Z: the sum of exp(key - M) over the gists
+            float x = pm;
+            for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+            float z = isfinite(x) && pm != -INFINITY ? pz * expf(pm - x) : 0.f;
+            for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+            if (lane == 0) {
+                fred[0] = x;
+                fred[1] = z;
             }
         }
         lds_barrier();
+        const float M = fred[0], Z = fred[1];
+        const bool usable = isfinite(M);
+        float kvs[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = EPT * tid + e;
+            kvs[e] = i < keff ? order_key_value((uint32_t)(tc[i] >> 32)) : 0.f;
+        }
         {
-            // entry t % keff's rank, counted by threads over shares of the
-            // others (multiples of 4 entries, read 16 bytes at a time: one LDS
-            // read per 4 compares, several in flight)
+            // entry t % keff's rank (the entries before it: larger keys, or
+            // equal ones of lower index: larger composites), counted by
+            // threads over shares of the others (multiples of 8 entries, read
+            // 16 bytes at a time, four reads in flight)
             const int reps = max(1, kThreads / keff), i0 = tid % keff, part = tid / keff;
             if (part < reps) {
-                const int per = (((keff + reps - 1) / reps) + 3) & ~3;
+                const int per = (((keff + reps - 1) / reps) + 7) & ~7;
                 const int jb = min(keff, part * per), je = min(keff, jb + per);
                 for (int i = i0; i < keff; i += kThreads) {
-                    const uint32_t oi = tk[i];
-                    const int di = idl[i];
-                    auto before = [&](uint32_t kj, int dj) { return (kj > oi || (kj == oi && dj < di)) ? 1 : 0; };
+                    const uint64_t ci = tc[i];
+                    auto gt = [&](unsigned lo, unsigned hi) { return ((((uint64_t)hi) << 32) | lo) > ci ? 1 : 0; };
                     int r = 0, j = jb;
-#pragma unroll 4
-                    for (; j + 4 <= je; j += 4) {
-                        const uint4 kq = *(const uint4*)&tk[j];
-                        const int4 iq = *(const int4*)&idl[j];
-                        r += before(kq.x, iq.x) + before(kq.y, iq.y) + before(kq.z, iq.z) + before(kq.w, iq.w);
+                    for (; j + 8 <= je; j += 8) {
+                        const uint4 q0 = *(const uint4*)&tc[j], q1 = *(const uint4*)&tc[j + 2];
+                        const uint4 q2 = *(const uint4*)&tc[j + 4], q3 = *(const uint4*)&tc[j + 6];
+                        r += gt(q0.x, q0.y) + gt(q0.z, q0.w) + gt(q1.x, q1.y) + gt(q1.z, q1.w) +
+                             gt(q2.x, q2.y) + gt(q2.z, q2.w) + gt(q3.x, q3.y) + gt(q3.z, q3.w);
                     }
-                    for (; j < je; ++j) r += before(tk[j], idl[j]);
+                    for (; j < je; ++j) r += tc[j] > ci ? 1 : 0;
                     atomicAdd(&trk[i], r);
                 }
             }
@@ -708,7 +703,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 int* idl = (int*)sh.ckey;
                 for (int i = tid; i < n; i += kThreads) idl[i] = i;
                 lds_barrier();
-                topp_emit(idl, [](uint32_t*) { return false; });
+                topp_emit(idl, [](uint64_t*) { return false; });
                 return fast;
             }
         }
@@ -920,7 +915,7 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 for (int j = 0; j < kRecRowOffs / kThreads; ++j)
                     if (tid + j * kThreads < keff) idl[tid + j * kThreads] = mi[j];
                 lds_barrier();
-                topp_emit(idl, [](uint32_t*) { return false; });
+                topp_emit(idl, [](uint64_t*) { return false; });
                 return fast;
             }
         }
@@ -1045,11 +1040,12 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             // every selected entry is a candidate some thread holds (up front,
             // of its own slice, or parked in the second round); its index in
             // ids: the selected ids before its bitmap word and below it there
-            topp_emit(ids, [&](uint32_t* tk) {
+            topp_emit(ids, [&](uint64_t* tc) {
                 const int* wpre = (const int*)sh.tiebits;
                 auto put = [&](uint32_t key, int id) {
                     const uint64_t wb = sh.selbits[id >> 6], bit = 1ull << (id & 63);
-                    if (wb & bit) tk[wpre[id >> 6] + __popcll(wb & (bit - 1ull))] = key;
+                    if (wb & bit)
+                        tc[wpre[id >> 6] + __popcll(wb & (bit - 1ull))] = ((uint64_t)key << 32) | (uint32_t)~id;
                 };
 #pragma unroll
                 for (int j = 0; j <= KQ; ++j)
