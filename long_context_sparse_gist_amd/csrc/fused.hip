@@ -635,16 +635,17 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
             }
         }
         lds_barrier();
+        // the weights by rank; wavefront 0 cuts: lane l sums ranks
+        // [l*per, (l+1)*per), a prefix over the lanes finds the chunk where
+        // the running sum reaches the target, and that lane walks its chunk
+        auto weights = [&]() {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = EPT * tid + e;
-            if (i < keff) twr[trk[i]] = (usable && !isnan(kvs[e])) ? expf(kvs[e] - M) : 0.f;
-        }
-        lds_barrier();
-        if (w == 0) {
-            // lane l sums ranks [l*per, (l+1)*per); a prefix over the lanes
-            // finds the chunk where the running sum reaches the target; that
-            // lane walks its chunk to the cut
+            for (int e = 0; e < EPT; ++e) {
+                const int i = EPT * tid + e;
+                if (i < keff) twr[trk[i]] = (usable && !isnan(kvs[e])) ? expf(kvs[e] - M) : 0.f;
+            }
+        };
+        auto cut = [&]() {  // (wavefront 0) the kept count, in every lane
             const int per = (keff + 63) / 64, b0 = lane * per, e0 = min(keff, b0 + per);
             float cs = 0.f;
             for (int r = b0; r < e0; ++r) cs += twr[r];
@@ -669,24 +670,52 @@ __device__ __forceinline__ bool select_fused(const Args& a, const Sched& sc, con
                 }
                 need = __shfl(nl, lc);
             }
-            if (lane == 0) sh.ncand = need;
-        }
-        lds_barrier();
-        const int need = sh.ncand;
-        int keep = 0;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < keff && trk[EPT * tid + e] < need) ? 1 : 0;
-        int ktot;
-        int pos = block_excl_scan<kThreads>(keep, &ktot, sh.wsum);
-        // the kept entries ascending into LDS (the weights' place), then one
-        // entry per thread out, the cut ones marked skipped
+            return need;
+        };
+        // then the kept entries ascending into LDS (the weights' place) and
+        // one entry per thread out, the cut ones marked skipped
         int* kept_ids = (int*)sh.cidx;
+        int need;
+        if (keff <= 64 * EPT) {
+            // every entry is wavefront 0's: no block barrier until the output
+            if (w == 0) {
+                weights();
+                lds_fence();
+                need = cut();
+                int keep = 0;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = EPT * tid + e;
-            if (i < keff && trk[i] < need) kept_ids[pos++] = ids_[e];
+                for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < keff && trk[EPT * tid + e] < need) ? 1 : 0;
+                int pos = wave_prefix_incl_dpp(keep) - keep;
+                lds_fence();  // (the cut's reads of the weights are done)
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    const int i = EPT * tid + e;
+                    if (i < keff && trk[i] < need) kept_ids[pos++] = ids_[e];
+                }
+                if (lane == 0) sh.ncand = need;
+            }
+        } else {
+            weights();
+            lds_barrier();
+            if (w == 0) {
+                need = cut();
+                if (lane == 0) sh.ncand = need;
+            }
+            lds_barrier();
+            need = sh.ncand;
+            int keep = 0;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) keep += (EPT * tid + e < keff && trk[EPT * tid + e] < need) ? 1 : 0;
+            int ktot;
+            int pos = block_excl_scan<kThreads>(keep, &ktot, sh.wsum);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const int i = EPT * tid + e;
+                if (i < keff && trk[i] < need) kept_ids[pos++] = ids_[e];
+            }
         }
         lds_barrier();
+        need = sh.ncand;
         for (int i = tid; i < keff; i += kThreads) {
             if (i < need) {
                 emit(i, kept_ids[i]);
