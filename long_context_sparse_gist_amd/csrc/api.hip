@@ -50,7 +50,7 @@ struct Plan {
     int S2;            // splits of the unfolded list
     int cand_cap;      // candidate list capacity (H-GSA)
     size_t off_ctl, off_keys, off_sel, off_selm, off_mkeys, off_ckeys, off_cand, off_ml, off_acc,
-        off_spairs, off_spairs_c, off_hlog, off_nsel, total;
+        off_spairs, off_spairs_c, off_hlog, off_hsum, off_nsel, total;
 };
 
 gsa_status_t check_params(const gsa_params_t* p, const gsa_kv_t* kv) {
@@ -237,6 +237,8 @@ void make_plan(const gsa_params_t* p, const gsa_kv_t* kv, const hgsa_meta_t* m, 
     pl.off_spairs_c = off; off += align_up(sizeof(uint64_t) * (size_t)units * pl.sc.S3 * gsa::kFusedTA);
     const bool probs = !pl.hier && (p->flags & GSA_SCORE_SUM_PROBS);
     pl.off_hlog = off;  off += align_up(sizeof(float) * (probs && !pl.fused ? (size_t)units * a.G * M : 0));
+    const bool hsum = probs && !pl.fused && pl.mfma;
+    pl.off_hsum = off;  off += align_up(sizeof(float) * (hsum ? (size_t)units * a.NS * a.G : 0));
     const bool topp = !pl.hier && (p->flags & GSA_SELECT_TOP_P);
     pl.off_nsel = off;  off += align_up(sizeof(int32_t) * (topp ? (size_t)units : 0));
     pl.total = off;
@@ -480,6 +482,7 @@ gsa_status_t decode_flat(Plan& pl, const gsa_params_t* p, const gsa_kv_t* kv, co
     a.keys = scores ? scores : (float*)(ws + pl.off_keys);
     a.sel = sel_idx ? sel_idx : (int32_t*)(ws + pl.off_sel);
     a.hlog = (p->flags & GSA_SCORE_SUM_PROBS) && !pl.fused ? (float*)(ws + pl.off_hlog) : nullptr;
+    a.hsum = a.hlog && pl.mfma ? (float*)(ws + pl.off_hsum) : nullptr;
     a.top_p = (p->flags & GSA_SELECT_TOP_P) ? p->top_p : 0.f;
     a.nsel = nullptr;  // set once the top-p counts are written
     a.part_ml = (float2*)(ws + pl.off_ml);

@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float s_max[kWaves][16];
     __shared__ float s_sum[kWaves][16];
+    __shared__ float s_esum[kWaves][16];
 
     const int u = blockIdx.y;
     const int split = blockIdx.x;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
 
     // probabilities as the PV A operand: row = head lr, k = 8*lg + j <-> token (t=j/4, row 4*lg + j%4)
     bf16x8_t P[NB];
-    float lsum = 0.f;
+    float lsum = 0.f, esum = 0.f;  // sums of the bf16 PV operand and of the unrounded probabilities
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
@@ -211,9 +212,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
                 float pv = (rel_of(blk, t, r) < count) ? exp2f(s[blk][t][r] * a.tau_log2e - m2) : 0.f;
                 __bf16 pb = (__bf16)pv;
                 lsum += (float)pb;
+                esum += pv;
                 P[blk][4 * t + r] = pb;
             }
     lsum = rows4_sum(lsum);
+    esum = rows4_sum(esum);
 
     f32x4_t o[DB];
 #pragma unroll
@@ -252,7 +255,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
             int h = 4 * lg + r;
             if (h < G) red[((size_t)w * 16 + h) * D + 16 * db + lr] = o[db][r];
         }
-    if (lg == 0) s_sum[w][lr] = lsum;
+    if (lg == 0) {
+        s_sum[w][lr] = lsum;
+        s_esum[w][lr] = esum;
+    }
     __syncthreads();
     const int slot = partial_slot(a, kind, split);
     const size_t pbase = ((size_t)u * a.NS + slot) * G;
@@ -272,6 +278,12 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(Args a, int kind, int hi
 #pragma unroll
         for (int i = 1; i < kWaves; ++i) mm = fmaxf(mm, s_max[i][h]);
         a.part_ml[pbase + h] = make_float2(mm * a.tau_log2e, l);
+        if (kind == kListGists && a.hsum) {
+            float le = 0.f;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) le += s_esum[i][h];
+            a.hsum[pbase + h] = le;
+        }
     }
 }
 

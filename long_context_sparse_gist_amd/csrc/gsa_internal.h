@@ -49,6 +49,8 @@ struct Args {
     float* keys;      // [units][key_stride] routing keys
     int key_stride;
     float* hlog;      // [units][G][key_stride] per-head gist logits (sum-of-probabilities key), else null
+    float* hsum;      // [units][NS][G] with hlog on the MFMA kernels: each gist split's per-head sum of
+                      // unrounded probabilities (part_ml's sum is of the bf16 PV operand), else null
     float top_p;      // top-p selection: probability mass to keep
     int32_t* nsel;    // [units] selected chunks per unit (top-p), else null: min(top_k, n)
     int32_t* sel;     // [units][top_k] selected chunk ids, ascending, -1 padded

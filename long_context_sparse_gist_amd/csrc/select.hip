@@ -108,6 +108,11 @@ __global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
     const int G = a.G;    // <= 16
     const int ns = (n + a.SL - 1) / a.SL;
     const float2* ml = a.part_ml + (size_t)u * a.NS * G;
+    // each split's normaliser: its sum of unrounded probabilities where the
+    // attention kernel kept one (the MFMA kernels' part_ml sums the bf16 PV
+    // operand), else part_ml's (exact on the fp32 kernels)
+    const float* es = a.hsum ? a.hsum + (size_t)u * a.NS * G : nullptr;
+    auto split_l = [&](int sp, int h, float y) { return es ? es[(size_t)sp * G + h] : y; };
     const size_t hs = a.key_stride;
     const float* zl = a.hlog + (size_t)u * G * hs;
     float* kw = a.keys + (size_t)u * hs;
@@ -130,8 +135,10 @@ __global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
     for (int r = 0; r < SR; ++r) {
         const int sp = threadIdx.x + r * kThreads;
 #pragma unroll
-        for (int h = 0; h < 16; ++h)
+        for (int h = 0; h < 16; ++h) {
             pr[r][h] = (h < G && sp < ns) ? ml[(size_t)sp * G + h] : make_float2(-INFINITY, 0.f);
+            if (h < G && sp < ns) pr[r][h].y = split_l(sp, h, pr[r][h].y);
+        }
     }
 #pragma unroll
     for (int h = 0; h < 16; ++h) m[h] = fmaxf(pr[0][h].x, pr[1][h].x);
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void probs_keys_kernel(Args a) {
     for (int sp = threadIdx.x + SR * kThreads; sp < ns; sp += kThreads) {
 #pragma unroll
         for (int h = 0; h < 16; ++h)
-            if (h < G) l[h] += ml[(size_t)sp * G + h].y * exp2f(ml[(size_t)sp * G + h].x - m[h]);
+            if (h < G) l[h] += split_l(sp, h, ml[(size_t)sp * G + h].y) * exp2f(ml[(size_t)sp * G + h].x - m[h]);
     }
     block_reduce16(l, false, red);
 #pragma unroll

@@ -103,6 +103,17 @@ def test_small_sum_probs_key(gpu, name, lens):
     GU.check_gsa(inp, res, flags=flags)
 
 
+def test_sum_probs_key_multi_launch(gpu):
+    # 512 units: the single launch would need two records per unit, so the
+    # MFMA multi-launch kernels run (keys from each gist split's unrounded sums)
+    wl = SMALL["b128-g2-d64-c4-fit"]
+    say(f"[parity] {wl.name} sum-of-probabilities key, multi-launch")
+    inp = gi.make_inputs(wl, 22, seq_lens=lens_for(wl, "ragged", 8))
+    flags = gsa.GSA_SCORE_SUM_PROBS
+    res = GU.run_gpu(GU.to(inp, gpu), flags=flags)
+    GU.check_gsa(inp, res, flags=flags)
+
+
 @pytest.mark.parametrize("extra", ["selected-gists", "portable"])
 def test_sum_probs_key_combined(gpu, extra):
     wl = SMALL["b2-g7-d128-c16"]
