@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_sparse_gist_amd as gsa
 from long_context_sparse_gist_amd import inputs as gi
 from tests import gpu_util as GU
 
@@ -135,6 +136,24 @@ def test_select_stress(gpu, case):
     if case.startswith("ties"):
         assert np.all(sel[:, :, :top_k] == np.arange(top_k)), "equal keys: the lowest ids win"
     GU.check_gsa(inp, res, top_k=top_k)
+
+
+@pytest.mark.parametrize("case", ["cluster", "few_upfront", "ties_wide", "tie_groups"])
+def test_select_stress_top_p(gpu, case):
+    # top-p after each branch of the select (the second round, the general
+    # select, tied boundary keys): the kept entries are the exact top N of the
+    # GPU's own keys, N a valid cut, and the output the oracle's on that set
+    say(f"[select] {case}, top-p 0.5")
+    wl, inp, top_k = CASES[case]()
+    p = 0.5
+    res = GU.run_gpu(GU.to(inp, gpu), top_k=top_k, flags=gsa.GSA_SELECT_TOP_P, top_p=p)
+    out, sel, sc = res
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            got = sel[b, g][sel[b, g] >= 0]
+            assert np.array_equal(got, exact_topk(sc[b, g, :wl.num_chunks], len(got))), \
+                f"unit ({b},{g}): kept entries are not the top of the GPU's keys"
+    GU.check_gsa_topp(inp, res, p, top_k)
 
 
 def test_select_nan_keys(gpu):
