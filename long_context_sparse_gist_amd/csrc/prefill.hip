@@ -7,20 +7,22 @@
 // into the paged cache.
 //
 // Many queries share the same gist rows, so this is a dense contraction and
-// runs on MFMA.  A workgroup owns 64 columns of one (batch, kv-head) unit --
-// column j is query t = j / G, head j % G of the GQA group -- as 4 blocks of 16
-// (one per wavefront: few enough registers for 4 workgroups per compute unit,
-// whose loads hide each other's latency).  It streams key blocks of 32 rows: first the gists of
-// every chunk up to the last query's, then the slots of the chunks its
-// queries lie in.  Each block's K and V rows go from global memory straight
-// into LDS (global_load_lds, the four wavefronts sharing the loads and the
-// tiles; double-buffered, so block i+1 loads while block i is used); every
-// wavefront reads its K operand from the K tile (rows 16-byte-swizzled so the
-// 16 rows one instruction reads hit different banks) and its V operand
-// transposed from the V tile.  Scores S^T[key][column] = K.Q^T, the mask per
-// (key, column), online softmax per column in the exp2 domain, P (bf16) . V
-// accumulated in fp32, and the output written once at the end: no partials,
-// no workspace.
+// runs on MFMA.  A workgroup owns 128 columns of one (batch, kv-head) unit --
+// column j is query t = j / G, head j % G of the GQA group -- as 8 blocks of 16
+// (one per wavefront: few enough registers for 4 wavefronts per SIMD, two
+// workgroups per compute unit, each key block serving 128 columns).  It
+// streams key blocks of 32 rows: first the gists of every chunk up to the last
+// query's, then the slots of the chunks its queries lie in.  Each block's K
+// and V rows go from global memory straight into LDS (global_load_lds, the
+// wavefronts sharing the loads and the tiles; double-buffered, so block i+1
+// loads while block i is used); every wavefront reads its K operand from the
+// K tile (rows 16-byte-swizzled so the 16 rows one instruction reads hit
+// different banks) and its V operand transposed from the V tile.  Scores
+// S^T[key][column] = K.Q^T, the mask as each column's inclusive key range
+// (compares and selects: a short-circuit test per element compiled to
+// branches that cost more than the MFMAs), online softmax per column in the
+// exp2 domain, P (bf16) . V accumulated in fp32, and the output written once
+// at the end: no partials, no workspace.
 #include "gsa_mfma_core.h"
 
 namespace gsa {
@@ -39,9 +41,10 @@ struct PrefillArgs {
 
 namespace {
 
-constexpr int kPThreads = 256;
+constexpr int kPWaves = 8;                // wavefronts per workgroup
+constexpr int kPThreads = 64 * kPWaves;
 constexpr int kNCB = 1;                   // 16-column blocks per wavefront
-constexpr int kPCols = 4 * kNCB * 16;     // columns per workgroup
+constexpr int kPCols = kPWaves * kNCB * 16;  // columns per workgroup
 constexpr int kPBtLds = 7936;             // block-table entries kept in LDS (64 KB in all at d = 128)
 
 // Wait for this wavefront's outstanding memory operations (global loads into
@@ -67,7 +70,7 @@ __device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, siz
     constexpr int CPR = D / 8;
 #pragma unroll
     for (int qq = 0; qq < CPR / 2; ++qq) {
-        if ((qq & 3) != w) continue;
+        if (qq % kPWaves != w) continue;
         const int f = 64 * qq + lane, r = f / CPR, p = f % CPR;
         const size_t src = (64 * qq) / CPR < 16 ? o0 : o1;  // uniform per qq
         const unsigned lo = __shfl((unsigned)src, r % 16), hi = __shfl((unsigned)(src >> 32), r % 16);
@@ -80,7 +83,7 @@ __device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, siz
 }
 
 template <int D>
-__global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {  // (4 wavefronts per SIMD)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int KK = D / 32, DB = D / 16, CPR = D / 8, TILE = PTiles<D>::TILE;
     unsigned char* ktile = smem;             // 2 buffers
@@ -111,6 +114,7 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
     WaveAttnL<D> wa[kNCB];
     int colm[kNCB], cols[kNCB];
     bool colv[kNCB];
+    int glo[kNCB], ghi[kNCB], slo[kNCB], shi[kNCB];  // keys a column sees: gists [glo, ghi], slots [slo, shi]
 #pragma unroll
     for (int cb = 0; cb < kNCB; ++cb) {
         const int j = jw + (w * kNCB + cb) * 16 + lr;
@@ -118,6 +122,12 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
         const int t = colv[cb] ? j / G : 0, h = j - (j / G) * G;
         cols[cb] = s0 + t;
         colm[cb] = cols[cb] / (C + 1);
+        // the gists of the chunks before the column's chunk, the slots of its
+        // chunk up to its own (an empty range for a column past the end)
+        glo[cb] = colv[cb] ? 0 : 1;
+        ghi[cb] = colv[cb] ? colm[cb] - 1 : 0;
+        slo[cb] = colv[cb] ? colm[cb] * (C + 1) : 1;
+        shi[cb] = colv[cb] ? cols[cb] : 0;
         const __bf16* qp = (const __bf16*)a.q + (((size_t)b * T + t) * a.Hq + (size_t)g * G + h) * D;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -177,7 +187,9 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
         for (int cb = 0; cb < kNCB; ++cb) {
             f32x4_t sc[2];
             wa[cb].scores(kA, sc);
-            // key 16t + 4lg + r against column lr
+            // key 16t + 4lg + r against column lr: inside the column's range
+            // (compares and selects, no branch)
+            const int lo = gist_blk ? glo[cb] : slo[cb], hi = gist_blk ? ghi[cb] : shi[cb];
             bool ok[2][4];
             float bm = -INFINITY;
 #pragma unroll
@@ -185,13 +197,13 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = kbase + 16 * t + 4 * lg + r;
-                    ok[t][r] = colv[cb] && (gist_blk ? key < colm[cb]
-                                                     : key <= cols[cb] && key >= colm[cb] * (C + 1));
-                    if (ok[t][r]) bm = fmaxf(bm, sc[t][r]);
+                    ok[t][r] = (key >= lo) & (key <= hi);
+                    bm = fmaxf(bm, ok[t][r] ? sc[t][r] : -INFINITY);
                 }
             bm = rows4_max(bm);
             const float mold = wa[cb].m, mnew = fmaxf(mold, bm);
-            const float alpha = mnew == -INFINITY ? 1.f : exp2f((mold - mnew) * tl);
+            // (the hardware exp2: exp2(-inf) = 0; arguments of the kept keys are <= 0)
+            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mold - mnew) * tl);
             const float mb = mnew * tl;
             bf16x8_t P;
             float ls = 0.f;
@@ -199,7 +211,8 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const __bf16 pb = (__bf16)(ok[t][r] ? exp2f(sc[t][r] * tl - mb) : 0.f);
+                    const float e = __builtin_amdgcn_exp2f(sc[t][r] * tl - mb);
+                    const __bf16 pb = (__bf16)(ok[t][r] ? e : 0.f);
                     ls += (float)pb;
                     P[4 * t + r] = pb;
                 }
