@@ -49,6 +49,10 @@ __device__ inline float rowmax16(float x) {
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (DPP row shifts, then
 // row broadcasts of lanes 15 and 31).
+// exp2 on the hardware instruction (v_exp_f32: exp2(-inf) = 0, results below
+// 2^-126 flush to 0), for softmax weights that are rounded to bf16 anyway
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline int wave_prefix_incl_dpp(int x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
     x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
@@ -126,7 +130,7 @@ struct WaveAttn {
                 if (16 * t + 4 * lg + r < nvalid) bm = fmaxf(bm, s[t][r]);
         bm = rows4_max(bm);
         const float mnew = fmaxf(m, bm);  // finite: the block has a real token
-        const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on the first block
+        const float alpha = exp2_hw((m - mnew) * tau_log2e);  // 0 on the first block
         const float mb = mnew * tau_log2e;
         bf16x8_t P;
         float ls = 0.f;
@@ -134,7 +138,7 @@ struct WaveAttn {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float pv = (16 * t + 4 * lg + r < nvalid) ? exp2f(s[t][r] * tau_log2e - mb) : 0.f;
+                float pv = (16 * t + 4 * lg + r < nvalid) ? exp2_hw(s[t][r] * tau_log2e - mb) : 0.f;
                 __bf16 pb = (__bf16)pv;
                 ls += (float)pb;
                 P[4 * t + r] = pb;
@@ -374,7 +378,7 @@ struct WaveAttnL {
                 if (16 * t + 4 * lg + r < nvalid) bm = fmaxf(bm, s[t][r]);
         bm = rows4_max(bm);
         const float mnew = fmaxf(m, bm);  // finite: the block has a real token
-        const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on the first block
+        const float alpha = exp2_hw((m - mnew) * tau_log2e);  // 0 on the first block
         const float mb = mnew * tau_log2e;
         bf16x8_t P;
         float ls = 0.f;
@@ -382,7 +386,7 @@ struct WaveAttnL {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float pv = (16 * t + 4 * lg + r < nvalid) ? exp2f(s[t][r] * tau_log2e - mb) : 0.f;
+                float pv = (16 * t + 4 * lg + r < nvalid) ? exp2_hw(s[t][r] * tau_log2e - mb) : 0.f;
                 __bf16 pb = (__bf16)pv;
                 ls += (float)pb;
                 P[4 * t + r] = pb;
@@ -457,7 +461,7 @@ struct WaveAttnL {
         if (nbw <= 0) return;
         bm = rows4_max(bm);
         const float mnew = fmaxf(m, bm);  // finite: a block has a real token
-        const float alpha = exp2f((m - mnew) * tau_log2e);  // 0 on an empty state
+        const float alpha = exp2_hw((m - mnew) * tau_log2e);  // 0 on an empty state
         const float mb = mnew * tau_log2e;
         float ls = 0.f;
 #pragma unroll
@@ -466,7 +470,7 @@ struct WaveAttnL {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pv = (j < nbw && 16 * t + 4 * lg + r < nval[j]) ? exp2f(s[j][t][r] * tau_log2e - mb)
+                    const float pv = (j < nbw && 16 * t + 4 * lg + r < nval[j]) ? exp2_hw(s[j][t][r] * tau_log2e - mb)
                                                                                  : 0.f;
                     const __bf16 pb = (__bf16)pv;
                     ls += (float)pb;
