@@ -293,8 +293,9 @@ gsa_status_t run_attn(const Plan& pl, int kind, int splits, hipStream_t st) {
 
 struct LvPlan {
     gsa::LvArgs A;
-    size_t off_keys, off_cid[2], off_desc[2], off_ncand[2], off_fdesc, off_nfin,
-        off_sel[gsa::kMaxLevels + 1], off_ml, off_acc, total;
+    size_t off_keys, off_cid, off_fdesc, off_nfin, off_sel[gsa::kMaxLevels + 1], off_ml, off_acc,
+        total;
+    bool counters;  // the final attention's arrival counters fit the control block
 };
 
 gsa_status_t check_levels(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* lv, int L) {
@@ -349,16 +350,16 @@ void make_lv_plan(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* 
     A.fcap = (int)(f > 1 ? f : 1);
     auto splits = [](long rows) { return (int)(rows > 0 ? (rows + 127) / 128 : 1); };
     A.S_top = splits(top);
-    A.S_cand = splits(cand_max);
     A.S_fin = splits(A.fcap);
     A.NS = A.S_top + A.S_fin;
-    size_t off = sizeof(unsigned) * kCtlWords;  // the control block (unused here)
-    pl.off_keys = off;  off += align_up(sizeof(float) * units * A.cap);
-    for (int i = 0; i < 2; ++i) {
-        pl.off_cid[i] = off;   off += align_up(sizeof(int32_t) * units * A.cap);
-        pl.off_desc[i] = off;  off += align_up(sizeof(int64_t) * units * A.cap);
-        pl.off_ncand[i] = off; off += align_up(sizeof(int32_t) * units);
-    }
+    pl.counters = (size_t)units <= kCtlWords - kHdrWords;
+    long sel_total = 0;
+    for (int l = 0; l <= L; ++l) sel_total += A.topk[l];
+    A.chain_lds = cand_max <= gsa::kChainCap && sel_total <= gsa::kChainSel;
+    size_t off = sizeof(unsigned) * kCtlWords;  // the control block: per-unit arrival counters
+    // every level's keys and candidate ids in buffers of their own
+    pl.off_keys = off;  off += align_up(sizeof(float) * (L + 1) * units * A.cap);
+    pl.off_cid = off;   off += align_up(sizeof(int32_t) * (L + 1) * units * A.cap);
     pl.off_fdesc = off; off += align_up(sizeof(int64_t) * units * A.fcap);
     pl.off_nfin = off;  off += align_up(sizeof(int32_t) * units);
     for (int l = 0; l <= L; ++l) {
@@ -407,11 +408,8 @@ gsa_status_t mgsa_decode(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_le
     A.a.part_ml = (float2*)(ws + pl.off_ml);
     A.a.part_acc = (float*)(ws + pl.off_acc);
     A.keys = (float*)(ws + pl.off_keys);
-    for (int i = 0; i < 2; ++i) {
-        A.cid[i] = (int32_t*)(ws + pl.off_cid[i]);
-        A.desc[i] = (int64_t*)(ws + pl.off_desc[i]);
-        A.ncand[i] = (int32_t*)(ws + pl.off_ncand[i]);
-    }
+    A.cid = (int32_t*)(ws + pl.off_cid);
+    A.uctr = pl.counters ? (unsigned*)workspace + kHdrWords : nullptr;
     A.fdesc = (int64_t*)(ws + pl.off_fdesc);
     A.nfin = (int32_t*)(ws + pl.off_nfin);
     for (int l = 0; l <= num_levels; ++l) {

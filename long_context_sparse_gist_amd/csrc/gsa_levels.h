@@ -7,6 +7,9 @@ namespace gsa {
 
 constexpr int kMaxLevels = 8;     // meta-gist levels above the gists
 constexpr int kDescShift = 56;    // row descriptor: array id << 56 | element offset
+constexpr int kChainCap = 8192;   // candidate rows the select chain keeps in LDS
+constexpr int kChainSel = 4096;   // kept ids (all levels) the select chain keeps in LDS
+constexpr int kChainBt = 4096;    // block-table entries per sequence the select chain keeps in LDS
 
 struct LvArgs {
     Args a;                       // shapes, q, caches, block table, lengths, partials, out
@@ -20,15 +23,16 @@ struct LvArgs {
     int32_t* sel[kMaxLevels + 1];   // [units][k_l] kept ids, ascending, -1 padded
     int32_t* usel[kMaxLevels + 1];  // the caller's copies, or null
     // lists
-    int cap;                      // rows per unit of the key / candidate buffers
-    float* keys;                  // [units][cap] routing keys of the current list
-    int32_t* cid[2];              // [units][cap] ids of the candidate lists (ping-pong)
-    int64_t* desc[2];             // [units][cap] their row descriptors
-    int32_t* ncand[2];            // [units] their lengths
+    int cap;                      // rows per (level, unit) of the key buffers
+    float* keys;                  // [L+1][units][cap] routing keys of each level's list
+    int32_t* cid;                 // [L+1][units][cap] entry ids of each candidate list (below the top)
+    int chain_lds;                // the select chain keeps its lists in LDS (they fit)
     int fcap;                     // rows per unit of the final list
     int64_t* fdesc;               // [units][fcap]
     int32_t* nfin;                // [units]
-    int S_top, S_cand, S_fin, NS; // splits of the top level, candidate lists, final list; partial slots
+    unsigned* uctr;               // [units] arrival counters of the final attention's
+                                  // workgroups (zero between calls), or null: merge launch
+    int S_top, S_fin, NS;         // splits of the top level and the final list; partial slots
 };
 
 hipError_t launch_levels(const LvArgs& A, hipStream_t st);

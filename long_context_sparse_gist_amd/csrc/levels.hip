@@ -11,12 +11,16 @@
 //   select   the top-k_l candidates (ties to the lower id, NaN last);
 //   attend   the kept entries and the past-the-last-group entries of every
 //            level below the top, the kept chunks' raw tokens and the raw tail.
-// Launches (bf16, MFMA): the top level's attention and keys, then per level a
-// select that writes the next level's candidate list as row descriptors,
-// a keys-only pass over it, ..., the gist-level select writes the final
-// attention list, one attention pass over it, and a merge of the partials.
-// Every list is a per-unit array of row descriptors (array id << 56 | element
-// offset), so one attention kernel serves every level and the final set.
+// Launches (bf16, MFMA): the top level's keys and attention (many workgroups
+// per unit); the select chain, one workgroup per unit, which keeps each
+// level's top-k and scores the next level's candidates itself (MFMA, keys and
+// ids to per-level buffers, so no address is written twice in the kernel),
+// down to the gist level's select, which writes the final attention list; one
+// attention pass over that list, whose last workgroup per unit merges the
+// unit's partials (a separate merge launch when the arrival counters do not
+// fit the control block).  Every list is a per-unit array of row descriptors
+// (array id << 56 | element offset), so one attention kernel serves the top
+// level and the final set.
 #include "gsa_lists.h"
 #include "gsa_levels.h"
 #include "gsa_select.h"
@@ -32,6 +36,29 @@ constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // rows per attention workgroup
 constexpr int kSelThreads = 512;
 constexpr int64_t kOffMask = (1ll << kDescShift) - 1;
+
+// Data handed between workgroups of one launch (the final attention's
+// partials, read by the unit's merging workgroup) goes through device-scope
+// accesses, coherent across the XCDs' L2s without cache-wide fences.
+__device__ inline void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_dev(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float2 ld_dev2(const float2* p) {
+    const uint64_t v = ld_dev((const uint64_t*)p);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ inline void st_dev2(float2* p, float2 v) {
+    st_dev((uint64_t*)p, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32));
+}
 
 __device__ inline float dpp_sum_step(float x, int ctrl) {
     int v = __builtin_bit_cast(int, x), r;
@@ -61,6 +88,14 @@ __device__ inline void level_counts(const LvArgs& A, int b, int (&cnt)[kMaxLevel
     for (int l = 1; l <= kMaxLevels; ++l) cnt[l] = l <= A.L ? cnt[l - 1] / A.fan[l] : 0;
 }
 
+// Entries of the top level of batch row b.
+__device__ inline int top_count(const LvArgs& A, int b) {
+    int n, tail;
+    seq_shape(A.a, b, n, tail);
+    for (int l = 1; l <= A.L; ++l) n /= A.fan[l];
+    return n;
+}
+
 // Descriptor of entry `id` of level l of unit (b, g): level 0 is a gist in the
 // paged cache, a level l >= 1 entry a row of that level's array.
 __device__ inline int64_t entry_desc(const LvArgs& A, int l, int b, int g, int id) {
@@ -69,191 +104,283 @@ __device__ inline int64_t entry_desc(const LvArgs& A, int l, int b, int g, int i
     return ((int64_t)l << kDescShift) | (int64_t)off;
 }
 
-// Attention and / or routing keys over one list per unit.
-//   list < 0   dense: every entry of level -list - 1 (the top level)
-//   list 0, 1  the candidate list in ping-pong buffer `list`
-//   list 2     the final attention list
-// keys: routing keys of the list's rows into A.keys; attn: one partial per
-// split into partial slot slot0 + split (an empty split writes an empty one).
+// q of the group's heads of unit (b, g) as MFMA B operands: lane (lr, lg)
+// holds head lr's elements [32kk + 8lg, 32kk + 8lg + 8); heads past G are 0.
 template <int D>
-__global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int list, int keys, int attn,
-                                                      int slot0) {
+__device__ inline void load_q(const Args& a, int b, int g, int lr, int lg, bf16x8_t (&qB)[D / 32]) {
+    const __bf16* qp = (const __bf16*)a.q + ((size_t)b * a.Hq + (size_t)g * a.G + lr) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        if (lr < a.G) {
+            qB[kk] = *(const bf16x8_t*)(qp + 32 * kk + 8 * lg);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qB[kk][i] = (__bf16)0.0f;
+        }
+    }
+}
+
+// Routing keys of 32 rows (two MFMA tiles of 16) from the lane's K operands:
+// s[t][r] = q_{head lr} . k_{row 16t + 4lg + r}.  Lanes lr < 8 return the key
+// of row 16t + 4lg + r with 4t + r == lr (the row sum over the group's heads,
+// padding heads scoring 0) and set rel to that row; other lanes set rel = -1.
+__device__ inline float tile_keys(const f32x4_t (&s)[2], int lr, int lg, float tau, int& rel) {
+    float kv = 0.f;
+    rel = -1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = row16_sum(s[t][r]) * tau;
+            if (4 * t + r == lr) {
+                kv = x;
+                rel = 16 * t + 4 * lg + r;
+            }
+        }
+    return kv;
+}
+
+// Merge of unit u's partial slots [0, NS) into the output (bf16, rounded to
+// nearest even) by one workgroup of 256 threads (G <= 16 heads): per head the
+// largest maximum M and the normaliser sum_i l_i 2^(m_i - M), then each output
+// element sum_i acc_i 2^(m_i - M) / normaliser.  An empty set gives zeros.
+// sc: LDS for the scale factors 2^(m_i - M) of up to sc_slots slots (past
+// that they are recomputed from the maxima); the loads of each step are
+// issued together, eight slots at a time.
+__device__ void merge_unit_block(const LvArgs& A, int u, float* sc, int sc_slots) {
+    __shared__ float s_M[16], s_inv[16];
+    const Args& a = A.a;
+    const int b = u / a.Hkv, g = u - b * a.Hkv;
+    const int G = a.G, D = a.D, NS = A.NS;
+    const float2* ml = a.part_ml + (size_t)u * NS * G;
+    const float* acc = a.part_acc + (size_t)u * NS * G * D;
+    {
+        const int h = threadIdx.x >> 4, j = threadIdx.x & 15;
+        float m = -INFINITY;
+        if (h < G)
+            for (int i = j; i < NS; i += 16) m = fmaxf(m, ld_dev2(ml + (size_t)i * G + h).x);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        float l = 0.f;
+        if (h < G)
+            for (int i = j; i < NS; i += 16) {
+                const float2 v = ld_dev2(ml + (size_t)i * G + h);
+                const float f = (m != -INFINITY && v.x != -INFINITY) ? exp2f(v.x - m) : 0.f;
+                l += v.y * f;
+                if (i < sc_slots) sc[i * 16 + h] = f;
+            }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) l += __shfl_xor(l, off);
+        if (h < G && j == 0) {
+            s_M[h] = m;
+            s_inv[h] = (m != -INFINITY && l > 0.f) ? 1.f / l : 0.f;
+        }
+    }
+    __syncthreads();
+    __bf16* out = (__bf16*)a.out + ((size_t)b * a.Hq + (size_t)g * G) * D;
+    const int half = D / 2;
+    for (int e = threadIdx.x; e < G * half; e += blockDim.x) {
+        const int hh = e / half, d = 2 * (e - hh * half);
+        const float M = s_M[hh];
+        float ox = 0.f, oy = 0.f;
+        for (int i0 = 0; i0 < NS; i0 += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                v[t] = i0 + t < NS ? ld_dev2((const float2*)(acc + ((size_t)(i0 + t) * G + hh) * D + d))
+                                   : make_float2(0.f, 0.f);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int i = i0 + t;
+                if (i >= NS) break;
+                float f;
+                if (i < sc_slots) {
+                    f = sc[i * 16 + hh];
+                } else {
+                    const float mi = ld_dev2(ml + (size_t)i * G + hh).x;
+                    f = (M != -INFINITY && mi != -INFINITY) ? exp2f(mi - M) : 0.f;
+                }
+                ox += v[t].x * f;
+                oy += v[t].y * f;
+            }
+        }
+        out[hh * D + d] = (__bf16)(ox * s_inv[hh]);
+        out[hh * D + d + 1] = (__bf16)(oy * s_inv[hh]);
+    }
+}
+
+// Attention over one list per unit, one partial per 128-row split into
+// partial slot slot0 + split (an empty split writes an empty partial).
+//   top = 1  every entry of the top level; also its routing keys, into the
+//            top level's key buffer
+//   top = 0  the final attention list; with arrival counters, the unit's
+//            last workgroup to finish merges the unit's partials and clears
+//            its counter
+template <int D>
+__global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slot0) {
     constexpr int KK = D / 32, DB = D / 16, LDW = 32 + 4;
     constexpr int VT = kWaves * D * LDW * 2, RED = kWaves * 16 * D * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem[VT > RED ? VT : RED];
     __shared__ float s_max[kWaves][16], s_sum[kWaves][16];
+    __shared__ int s_last;
     const Args& a = A.a;
     const int u = blockIdx.y, split = blockIdx.x;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
     const int G = a.G;
-    int cnt[kMaxLevels + 1], tail;
-    level_counts(A, b, cnt, tail);
-    int len;
-    if (list < 0) len = cnt[-list - 1];
-    else if (list < 2) len = A.ncand[list][u];
-    else len = A.nfin[u];
+    const int len = top ? top_count(A, b) : A.nfin[u];
     const int p0 = split * kRows;
     const int count = min(kRows, len - p0);
     const size_t pbase = ((size_t)u * A.NS + slot0 + split) * G;
+    const bool dev = !top && A.uctr;  // partials read by this launch's merging workgroup
+    auto put_acc = [&](size_t i, float v) {
+        if (dev) st_dev(a.part_acc + i, v);
+        else a.part_acc[i] = v;
+    };
+    auto put_ml = [&](size_t i, float2 v) {
+        if (dev) st_dev2(a.part_ml + i, v);
+        else a.part_ml[i] = v;
+    };
     if (count <= 0) {
-        if (attn) {
-            for (int e = threadIdx.x; e < G * D; e += blockDim.x) a.part_acc[pbase * D + e] = 0.f;
-            if (threadIdx.x < (unsigned)G) a.part_ml[pbase + threadIdx.x] = make_float2(-INFINITY, 0.f);
+        for (int e = threadIdx.x; e < G * D; e += blockDim.x) put_acc(pbase * D + e, 0.f);
+        if (threadIdx.x < (unsigned)G) put_ml(pbase + threadIdx.x, make_float2(-INFINITY, 0.f));
+    } else {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
+        bf16x8_t qB[KK];
+        load_q<D>(a, b, g, lr, lg, qB);
+        // rows of this lane: half t -> list position p0 + 32*w + 16*t + lr (a
+        // position past the end reads the split's first row)
+        const __bf16* krow[2];
+        const __bf16* vrow[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int rel = 32 * w + 16 * t + lr;
+            const int p = p0 + (rel < count ? rel : 0);
+            const int64_t d = top ? entry_desc(A, A.L, b, g, p) : A.fdesc[(size_t)u * A.fcap + p];
+            const int arr = (int)(d >> kDescShift);
+            const size_t off = (size_t)(d & kOffMask);
+            krow[t] = (const __bf16*)(arr ? A.lk[arr] : a.kc) + off;
+            vrow[t] = (const __bf16*)(arr ? A.lv[arr] : a.vc) + off;
         }
-        return;
-    }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
-
-    bf16x8_t qB[KK];
-    {
-        const __bf16* qp = (const __bf16*)a.q + ((size_t)b * a.Hq + (size_t)g * G + lr) * D;
+        bf16x8_t kA[2][KK], vA[2][KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (lr < G) {
-                qB[kk] = *(const bf16x8_t*)(qp + 32 * kk + 8 * lg);
-            } else {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) qB[kk][i] = (__bf16)0.0f;
-            }
-        }
-    }
-    // rows of this lane: half t -> list position p0 + 32*w + 16*t + lr (a
-    // position past the end reads the split's first row)
-    const __bf16* krow[2];
-    const __bf16* vrow[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int rel = 32 * w + 16 * t + lr;
-        const int p = p0 + (rel < count ? rel : 0);
-        int64_t d;
-        if (list < 0) d = entry_desc(A, -list - 1, b, g, p);
-        else if (list < 2) d = A.desc[list][(size_t)u * A.cap + p];
-        else d = A.fdesc[(size_t)u * A.fcap + p];
-        const int arr = (int)(d >> kDescShift);
-        const size_t off = (size_t)(d & kOffMask);
-        krow[t] = (const __bf16*)(arr ? A.lk[arr] : a.kc) + off;
-        vrow[t] = (const __bf16*)(arr ? A.lv[arr] : a.vc) + off;
-    }
-    bf16x8_t kA[2][KK], vA[2][KK];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(krow[t] + 32 * kk + 8 * lg);
-    if (attn) {
+            for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(krow[t] + 32 * kk + 8 * lg);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) vA[t][kk] = *(const bf16x8_t*)(vrow[t] + 32 * kk + 8 * lg);
-    }
-    // s[t][r] = q_{head lr} . k_{row 32w + 16t + 4lg + r}
-    f32x4_t s[2];
+        // s[t][r] = q_{head lr} . k_{row 32w + 16t + 4lg + r}
+        f32x4_t s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[t][kk], qB[kk], acc, 0, 0, 0);
-        s[t] = acc;
-    }
-    auto rel_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * lg + r; };
-    if (keys) {
-        // lanes lr < 8 keep one key each: row rel_of(t, r) with 4t + r == lr,
-        // the row sum over the group's heads (padding heads score 0)
-        float kv = 0.f;
-        int krel = -1;
+            for (int kk = 0; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[t][kk], qB[kk], acc, 0, 0, 0);
+            s[t] = acc;
+        }
+        auto rel_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * lg + r; };
+        if (top) {
+            int krel;
+            const float kv = tile_keys(s, lr, lg, a.tau, krel);
+            if (krel >= 0 && 32 * w + krel < count)
+                A.keys[((size_t)A.L * a.B * a.Hkv + u) * A.cap + p0 + 32 * w + krel] = kv;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (rel_of(t, r) < count) mx = fmaxf(mx, s[t][r]);
+        mx = rows4_max(mx);
+        if (lg == 0) s_max[w][lr] = mx;
+        __syncthreads();
+        float mh = s_max[0][lr];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) mh = fmaxf(mh, s_max[i][lr]);
+        const float m2 = mh * a.tau_log2e;
+        bf16x8_t P;
+        float lsum = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float x = row16_sum(s[t][r]) * a.tau;
-                if (4 * t + r == lr) {
-                    kv = x;
-                    krel = rel_of(t, r);
-                }
+                const float pv = rel_of(t, r) < count ? exp2f(s[t][r] * a.tau_log2e - m2) : 0.f;
+                const __bf16 pb = (__bf16)pv;
+                lsum += (float)pb;
+                P[4 * t + r] = pb;
             }
-        if (krel >= 0 && krel < count) A.keys[(size_t)u * A.cap + p0 + krel] = kv;
-    }
-    if (!attn) return;  // block-uniform
-
-    float mx = -INFINITY;
+        lsum = rows4_sum(lsum);
+        f32x4_t o[DB];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int db = 0; db < DB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        // V transposed through LDS: V[row 16t + lr][32kk + 8lg + i] -> vt[d][16t + lr]
+        __bf16* vt = (__bf16*)smem + (size_t)w * D * LDW;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (rel_of(t, r) < count) mx = fmaxf(mx, s[t][r]);
-    mx = rows4_max(mx);
-    if (lg == 0) s_max[w][lr] = mx;
-    __syncthreads();
-    float mh = s_max[0][lr];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) mh = fmaxf(mh, s_max[i][lr]);
-    const float m2 = mh * a.tau_log2e;
-    bf16x8_t P;
-    float lsum = 0.f;
+            for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+                for (int i = 0; i < 8; ++i) vt[(32 * kk + 8 * lg + i) * LDW + 16 * t + lr] = vA[t][kk][i];
+        __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pv = rel_of(t, r) < count ? exp2f(s[t][r] * a.tau_log2e - m2) : 0.f;
-            const __bf16 pb = (__bf16)pv;
-            lsum += (float)pb;
-            P[4 * t + r] = pb;
+        for (int db = 0; db < DB; ++db) {
+            const __bf16* col = vt + (16 * db + lr) * LDW;
+            const bf16x4_t lo = *(const bf16x4_t*)(col + 4 * lg);
+            const bf16x4_t hi = *(const bf16x4_t*)(col + 16 + 4 * lg);
+            bf16x8_t vb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vb[i] = lo[i];
+                vb[4 + i] = hi[i];
+            }
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P, vb, o[db], 0, 0, 0);
         }
-    lsum = rows4_sum(lsum);
-    f32x4_t o[DB];
+        __syncthreads();
+        // the wavefronts' sums: o[db][r] is head 4lg + r, column 16db + lr
+        float* red = (float*)smem;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    // V transposed through LDS: V[row 16t + lr][32kk + 8lg + i] -> vt[d][16t + lr]
-    __bf16* vt = (__bf16*)smem + (size_t)w * D * LDW;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * lg + r;
+                if (h < G) red[((size_t)w * 16 + h) * D + 16 * db + lr] = o[db][r];
+            }
+        if (lg == 0) s_sum[w][lr] = lsum;
+        __syncthreads();
+        for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+            const int h = e / D, d = e - h * D;
+            float acc = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vt[(32 * kk + 8 * lg + i) * LDW + 16 * t + lr] = vA[t][kk][i];
-    __syncthreads();
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const __bf16* col = vt + (16 * db + lr) * LDW;
-        const bf16x4_t lo = *(const bf16x4_t*)(col + 4 * lg);
-        const bf16x4_t hi = *(const bf16x4_t*)(col + 16 + 4 * lg);
-        bf16x8_t vb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vb[i] = lo[i];
-            vb[4 + i] = hi[i];
+            for (int i = 0; i < kWaves; ++i) acc += red[((size_t)i * 16 + h) * D + d];
+            put_acc(pbase * D + e, acc);
         }
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P, vb, o[db], 0, 0, 0);
+        if (threadIdx.x < (unsigned)G) {
+            const int h = threadIdx.x;
+            float l = 0.f, mm = s_max[0][h];
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) {
+                l += s_sum[i][h];
+                mm = fmaxf(mm, s_max[i][h]);
+            }
+            put_ml(pbase + h, make_float2(mm * a.tau_log2e, l));
+        }
+    }
+    if (!dev) return;  // grid-uniform
+    // count this workgroup in once its partial's stores have completed; the
+    // unit's last one merges
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev =
+            __hip_atomic_fetch_add(A.uctr + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev + 1 == gridDim.x;
     }
     __syncthreads();
-    // the wavefronts' sums: o[db][r] is head 4lg + r, column 16db + lr
-    float* red = (float*)smem;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * lg + r;
-            if (h < G) red[((size_t)w * 16 + h) * D + 16 * db + lr] = o[db][r];
-        }
-    if (lg == 0) s_sum[w][lr] = lsum;
-    __syncthreads();
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-        const int h = e / D, d = e - h * D;
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) acc += red[((size_t)i * 16 + h) * D + d];
-        a.part_acc[pbase * D + e] = acc;
-    }
-    if (threadIdx.x < (unsigned)G) {
-        const int h = threadIdx.x;
-        float l = 0.f, mm = s_max[0][h];
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            l += s_sum[i][h];
-            mm = fmaxf(mm, s_max[i][h]);
-        }
-        a.part_ml[pbase + h] = make_float2(mm * a.tau_log2e, l);
-    }
+    if (!s_last) return;
+    merge_unit_block(A, u, (float*)smem, (int)(sizeof(smem) / (16 * sizeof(float))));
+    if (threadIdx.x == 0) st_dev(A.uctr + u, 0u);  // zero again for the next call
 }
 
 // Number of ascending entries of sel[0..k) below `bound`.
@@ -267,47 +394,158 @@ __device__ inline int count_below(const int32_t* sel, int k, int bound) {
     return lo;
 }
 
-// Top-k of level l's current list (src < 0: the dense top level; else the
-// candidate list in buffer src), then the next list: level l-1's candidates
-// into buffer src ^ 1 (the top level writes buffer 0), or, at the gists, the
-// final attention list.
-__global__ __launch_bounds__(kSelThreads) void lv_select_kernel(LvArgs A, int l, int src) {
+
+// Top-k of one list by the chain's workgroup: lists of up to 1024 keys by
+// wavefront 0 alone (wave_topk: no barriers), longer ones by the whole block.
+// The result count goes through LDS; on return every thread has it and the
+// selection is written.
+template <typename KeyPtr, typename IdPtr, typename OutPtr>
+__device__ inline int chain_topk(KeyPtr keys, IdPtr ids, int n, int k, OutPtr out,
+                                 SelectSmem<kSelThreads>& sh, int* s_keff) {
+    if (n > 1024) return block_topk<kSelThreads>(keys, ids, n, k, out, false, sh);
+    if (threadIdx.x < 64) {
+        int r;
+        if (n <= 256) r = wave_topk<4>(keys, ids, n, k, out);
+        else if (n <= 512) r = wave_topk<8>(keys, ids, n, k, out);
+        else r = wave_topk<16>(keys, ids, n, k, out);
+        if (threadIdx.x == 0) *s_keff = r;
+    }
+    __syncthreads();
+    return *s_keff;
+}
+
+// The select chain of one unit, one workgroup of 512 threads: from the top
+// level down, the level's top-k (its keys from the top-level pass or from the
+// previous iteration), then the next level's candidates (the children of the
+// kept entries, ascending, then the entries past the level's last complete
+// group): their ids and routing keys (MFMA; each wavefront issues the loads
+// of up to 64 rows at once); at the gists, the final attention list.
+// Segments of the final list: raw rows of the kept chunks, the raw tail,
+// (L >= 1) the kept gists inside complete groups and the gists past the last
+// one, then for each level 1 <= l' < L its kept entries inside complete
+// groups and its entries past the last one.
+// Below the top level the lists live in LDS when every candidate list fits
+// (cap <= kChainCap) and the kept ids of all levels do (A.chain_lds): the
+// chain then touches global memory only for the top level's keys, the
+// candidates' K rows and its outputs.  Otherwise every level has key, id and
+// selection buffers of its own in the workspace (no address is written twice
+// in the kernel).  The unit's block-table row is read into LDS up front when
+// it has at most kChainBt pages.
+template <int D, bool LDS>
+__global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
+    constexpr int KK = D / 32, NW = kSelThreads / 64, U = 4;  // U tiles of 16 rows per wavefront
     __shared__ SelectSmem<kSelThreads> sh;
     __shared__ int seg[2 * kMaxLevels + 8];
+    __shared__ int cnt[kMaxLevels + 2];  // entries per level, then the raw tail
+    __shared__ int kept[kMaxLevels + 1];  // kept entries per level
+    __shared__ int s_keff;
+    __shared__ float s_keys[kChainCap];
+    __shared__ int32_t s_ids[kChainCap];
+    __shared__ int32_t s_sel[kChainSel];
+    __shared__ int32_t s_bt[kChainBt];
     const Args& a = A.a;
     const int u = blockIdx.x, tid = threadIdx.x;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
-    int cnt[kMaxLevels + 1], tail;
-    level_counts(A, b, cnt, tail);
-    const int k = A.topk[l];
-    const int n = src < 0 ? cnt[l] : A.ncand[src][u];
-    const float* keys = A.keys + (size_t)u * A.cap;
-    const int32_t* ids = src < 0 ? nullptr : A.cid[src] + (size_t)u * A.cap;
-    int32_t* sel = A.sel[l] + (size_t)u * k;
-    const int keff = block_topk<kSelThreads>(keys, ids, n, k, sel, false, sh);
-    __syncthreads();  // every thread's entries of sel are written
-    if (A.usel[l])
-        for (int i = tid; i < k; i += kSelThreads) A.usel[l][(size_t)u * k + i] = sel[i];
-    if (l > 0) {
-        // children of the kept entries (ascending), then the entries past the
-        // last complete group of level l
-        const int R = A.fan[l], dst = src < 0 ? 0 : src ^ 1;
-        const int past = cnt[l] * R, ntail = cnt[l - 1] - past;
-        int64_t* desc = A.desc[dst] + (size_t)u * A.cap;
-        int32_t* cid = A.cid[dst] + (size_t)u * A.cap;
-        const int nn = keff * R + ntail;
-        for (int p = tid; p < nn; p += kSelThreads) {
-            const int id = p < keff * R ? sel[p / R] * R + (p - (p / R) * R) : past + (p - keff * R);
-            desc[p] = entry_desc(A, l - 1, b, g, id);
-            cid[p] = id;
-        }
-        if (tid == 0) A.ncand[dst][u] = nn;
-        return;
+    const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const size_t units = (size_t)a.B * a.Hkv;
+    constexpr bool lds = LDS;
+    const bool bt_lds = a.max_pages <= kChainBt;
+    const int32_t* btg = a.bt + (size_t)b * a.max_pages;
+    if (bt_lds)
+        for (int i = tid; i < a.max_pages; i += kSelThreads) s_bt[i] = btg[i];
+    const int32_t* btrow = bt_lds ? s_bt : btg;
+    if (tid == 0) {
+        int c[kMaxLevels + 1], t;
+        level_counts(A, b, c, t);
+#pragma unroll
+        for (int l = 0; l <= kMaxLevels; ++l) cnt[l] = c[l];
+        cnt[kMaxLevels + 1] = t;
     }
-    // the gists: the final list.  Segments: raw rows of the kept chunks, the
-    // raw tail, (L >= 1) the kept gists inside complete groups and the gists
-    // past the last one, then for each level 1 <= l' < L its kept entries
-    // inside complete groups and its entries past the last one.
+    __syncthreads();
+    const int tail = cnt[kMaxLevels + 1];
+    // element offset of logical slot s of this unit (block-table row btrow)
+    auto slot_off = [&](int s) -> size_t {
+        const int lp = s / a.spp, off = s - lp * a.spp;
+        return (((size_t)btrow[lp] * a.Hkv + g) * a.spp + off) * (size_t)a.D;
+    };
+    auto desc_of = [&](int l, int id) -> int64_t {
+        if (l == 0) return (int64_t)slot_off(id * (a.C + 1) + a.C);
+        return entry_desc(A, l, b, g, id);
+    };
+    // kept ids of level l: in LDS at the sum of the lower levels' k
+    auto sel_of = [&](int l) -> int32_t* {
+        if (!lds) return A.sel[l] + (size_t)u * A.topk[l];
+        int o = 0;
+        for (int i = 0; i < l; ++i) o += A.topk[i];
+        return s_sel + o;
+    };
+    bf16x8_t qB[KK];
+    load_q<D>(a, b, g, lr, lg, qB);
+    int n = cnt[A.L], keff = 0;
+    for (int l = A.L; l >= 0; --l) {
+        const int k = A.topk[l];
+        int32_t* sel = sel_of(l);
+        if (l == A.L)
+            keff = chain_topk(A.keys + ((size_t)l * units + u) * A.cap, (const int32_t*)nullptr, n, k,
+                              sel, sh, &s_keff);
+        else if (lds)
+            keff = chain_topk(s_keys, s_ids, n, k, sel, sh, &s_keff);
+        else
+            keff = chain_topk(A.keys + ((size_t)l * units + u) * A.cap,
+                              A.cid + ((size_t)l * units + u) * A.cap, n, k, sel, sh, &s_keff);
+        if (tid == 0) kept[l] = keff;
+        __syncthreads();  // every thread's entries of sel are written
+        if (l == 0) break;
+        const int cl = l - 1, R = A.fan[l];
+        const int nk = keff * R, past = cnt[l] * R;
+        const int nc = nk + (cnt[cl] - past);
+        float* kout = lds ? s_keys : A.keys + ((size_t)cl * units + u) * A.cap;
+        int32_t* iout = lds ? s_ids : A.cid + ((size_t)cl * units + u) * A.cap;
+        for (int p0 = 16 * U * w; p0 < nc; p0 += 16 * U * NW) {
+            int id[U];
+#pragma unroll
+            for (int t = 0; t < U; ++t) {
+                const int rel = 16 * t + lr;
+                const int p = p0 + rel < nc ? p0 + rel : p0;  // past the end: the pass's first row
+                id[t] = p < nk ? sel[p / R] * R + (p - (p / R) * R) : past + (p - nk);
+            }
+            const __bf16* krow[U];
+#pragma unroll
+            for (int t = 0; t < U; ++t) {
+                const int64_t d = desc_of(cl, id[t]);
+                const int arr = (int)(d >> kDescShift);
+                krow[t] = (const __bf16*)(arr ? A.lk[arr] : a.kc) + (size_t)(d & kOffMask);
+            }
+            bf16x8_t kA[U][KK];
+#pragma unroll
+            for (int t = 0; t < U; ++t)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(krow[t] + 32 * kk + 8 * lg);
+#pragma unroll
+            for (int t = 0; t < U; ++t)
+                if (lg == 0 && p0 + 16 * t + lr < nc) iout[p0 + 16 * t + lr] = id[t];
+#pragma unroll
+            for (int h2 = 0; h2 < U / 2; ++h2) {
+                f32x4_t s[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[2 * h2 + t][kk], qB[kk], acc, 0, 0, 0);
+                    s[t] = acc;
+                }
+                int krel;
+                const float kv = tile_keys(s, lr, lg, a.tau, krel);
+                const int q = p0 + 32 * h2 + krel;
+                if (krel >= 0 && q < nc) kout[q] = kv;
+            }
+        }
+        __syncthreads();  // the level's keys and ids are written
+        n = nc;
+    }
+    // the gists: the final list
+    const int32_t* sel = sel_of(0);
     const int C = a.C, n0 = cnt[0];
     if (tid == 0) {
         int at = keff * C + tail;
@@ -319,13 +557,10 @@ __global__ __launch_bounds__(kSelThreads) void lv_select_kernel(LvArgs A, int l,
             seg[2] = past0;
             at += e0 + (n0 - past0);
             for (int lp = 1; lp < A.L; ++lp) {
-                const int kl = min(A.topk[lp], cnt[lp]);
                 // the kept entries of level lp are a prefix of its selection (-1 padded)
-                const int32_t* sl = A.sel[lp] + (size_t)u * A.topk[lp];
+                const int32_t* sl = sel_of(lp);
                 const int past = cnt[lp + 1] * A.fan[lp + 1];
-                int kk = 0;
-                while (kk < kl && sl[kk] >= 0) ++kk;
-                const int e = count_below(sl, kk, past);
+                const int e = count_below(sl, kept[lp], past);
                 seg[2 + 2 * lp] = at;
                 seg[3 + 2 * lp] = e;
                 at += e + (cnt[lp] - past);
@@ -344,14 +579,14 @@ __global__ __launch_bounds__(kSelThreads) void lv_select_kernel(LvArgs A, int l,
         } else {
             slot = n0 * (C + 1) + (p - nraw);
         }
-        fd[p] = (int64_t)slot_offset(a, b, g, slot);
+        fd[p] = (int64_t)slot_off(slot);
     }
     if (A.L >= 1) {
         const int base = nraw + tail, e0 = seg[1], past0 = seg[2];
         for (int p = tid; p < e0 + (n0 - past0); p += kSelThreads)
-            fd[base + p] = entry_desc(A, 0, b, g, p < e0 ? sel[p] : past0 + (p - e0));
+            fd[base + p] = desc_of(0, p < e0 ? sel[p] : past0 + (p - e0));
         for (int lp = 1; lp < A.L; ++lp) {
-            const int32_t* sl = A.sel[lp] + (size_t)u * A.topk[lp];
+            const int32_t* sl = sel_of(lp);
             const int at = seg[2 + 2 * lp], e = seg[3 + 2 * lp];
             const int past = cnt[lp + 1] * A.fan[lp + 1];
             for (int p = tid; p < e + (cnt[lp] - past); p += kSelThreads)
@@ -359,6 +594,12 @@ __global__ __launch_bounds__(kSelThreads) void lv_select_kernel(LvArgs A, int l,
         }
     }
     if (tid == 0) A.nfin[u] = seg[2 * kMaxLevels + 7];
+    // the caller's copies of the kept ids
+    for (int l = 0; l <= A.L; ++l)
+        if (A.usel[l]) {
+            const int32_t* sl = sel_of(l);
+            for (int i = tid; i < A.topk[l]; i += kSelThreads) A.usel[l][(size_t)u * A.topk[l] + i] = sl[i];
+        }
 }
 
 // Max-rescale merge of a unit's partial slots [0, NS) into the output (bf16,
@@ -419,36 +660,27 @@ __global__ __launch_bounds__(256) void lv_merge_kernel(LvArgs A) {
 }
 
 template <int D>
-hipError_t launch_attn_lv(const LvArgs& A, int list, int splits, int keys, int attn, int slot0,
-                          hipStream_t st) {
-    hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(splits, A.a.B * A.a.Hkv), dim3(256), 0, st, A, list,
-                       keys, attn, slot0);
+hipError_t launch_d(const LvArgs& A, hipStream_t st) {
+    const int units = A.a.B * A.a.Hkv;
+    // the top level: keys and attention over all its entries
+    hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A, 1, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (A.chain_lds)
+        hipLaunchKernelGGL((lv_chain_kernel<D, true>), dim3(units), dim3(kSelThreads), 0, st, A);
+    else
+        hipLaunchKernelGGL((lv_chain_kernel<D, false>), dim3(units), dim3(kSelThreads), 0, st, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_fin, units), dim3(256), 0, st, A, 0, A.S_top);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!A.uctr) hipLaunchKernelGGL(lv_merge_kernel, dim3(A.a.G, units), dim3(256), 0, st, A);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_levels(const LvArgs& A, hipStream_t st) {
-    const int units = A.a.B * A.a.Hkv;
-    auto attn = [&](int list, int splits, int keys, int att, int slot0) {
-        return A.a.D == 64 ? launch_attn_lv<64>(A, list, splits, keys, att, slot0, st)
-                           : launch_attn_lv<128>(A, list, splits, keys, att, slot0, st);
-    };
-    hipError_t e;
-    // the top level: keys and attention over all its entries
-    if ((e = attn(-A.L - 1, A.S_top, 1, 1, 0)) != hipSuccess) return e;
-    int src = -1;
-    for (int l = A.L; l >= 0; --l) {
-        hipLaunchKernelGGL(lv_select_kernel, dim3(units), dim3(kSelThreads), 0, st, A, l, src);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (l == 0) break;
-        src = src < 0 ? 0 : src ^ 1;
-        // keys of level l-1's candidates
-        if ((e = attn(src, A.S_cand, 1, 0, 0)) != hipSuccess) return e;
-    }
-    if ((e = attn(2, A.S_fin, 0, 1, A.S_top)) != hipSuccess) return e;
-    hipLaunchKernelGGL(lv_merge_kernel, dim3(A.a.G, units), dim3(256), 0, st, A);
-    return hipGetLastError();
+    return A.a.D == 64 ? launch_d<64>(A, st) : launch_d<128>(A, st);
 }
 
 }  // namespace gsa
