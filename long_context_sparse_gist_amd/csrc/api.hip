@@ -347,9 +347,12 @@ void make_lv_plan(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* 
     long f = (A.topk[0] < c0 ? A.topk[0] : c0) * (C + 1) + (C - 1);
     if (L >= 1) f += A.fan[1] - 1;
     for (int l = 1; l < L; ++l) f += (A.topk[l] < cnt[l] ? A.topk[l] : cnt[l]) + A.fan[l + 1] - 1;
+    // a small top level is scored by the select chain and attended with the final list
+    A.fold_top = top <= gsa::kFoldTop;
+    if (A.fold_top) f += top;
     A.fcap = (int)(f > 1 ? f : 1);
     auto splits = [](long rows) { return (int)(rows > 0 ? (rows + 127) / 128 : 1); };
-    A.S_top = splits(top);
+    A.S_top = A.fold_top ? 0 : splits(top);
     A.S_fin = splits(A.fcap);
     A.NS = A.S_top + A.S_fin;
     pl.counters = (size_t)units <= kCtlWords - kHdrWords;

@@ -9,6 +9,7 @@ constexpr int kMaxLevels = 8;     // meta-gist levels above the gists
 constexpr int kDescShift = 56;    // row descriptor: array id << 56 | element offset
 constexpr int kChainCap = 8192;   // candidate rows the select chain keeps in LDS
 constexpr int kChainSel = 4096;   // kept ids (all levels) the select chain keeps in LDS
+constexpr int kFoldTop = 1024;    // largest top level the select chain scores itself
 constexpr int kChainBt = 4096;    // block-table entries per sequence the select chain keeps in LDS
 
 struct LvArgs {
@@ -27,6 +28,8 @@ struct LvArgs {
     float* keys;                  // [L+1][units][cap] routing keys of each level's list
     int32_t* cid;                 // [L+1][units][cap] entry ids of each candidate list (below the top)
     int chain_lds;                // the select chain keeps its lists in LDS (they fit)
+    int fold_top;                 // the select chain scores the top level and the final list
+                                  // holds its entries (no top-level launch; S_top = 0)
     int fcap;                     // rows per unit of the final list
     int64_t* fdesc;               // [units][fcap]
     int32_t* nfin;                // [units]

@@ -481,33 +481,16 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
     };
     bf16x8_t qB[KK];
     load_q<D>(a, b, g, lr, lg, qB);
-    int n = cnt[A.L], keff = 0;
-    for (int l = A.L; l >= 0; --l) {
-        const int k = A.topk[l];
-        int32_t* sel = sel_of(l);
-        if (l == A.L)
-            keff = chain_topk(A.keys + ((size_t)l * units + u) * A.cap, (const int32_t*)nullptr, n, k,
-                              sel, sh, &s_keff);
-        else if (lds)
-            keff = chain_topk(s_keys, s_ids, n, k, sel, sh, &s_keff);
-        else
-            keff = chain_topk(A.keys + ((size_t)l * units + u) * A.cap,
-                              A.cid + ((size_t)l * units + u) * A.cap, n, k, sel, sh, &s_keff);
-        if (tid == 0) kept[l] = keff;
-        __syncthreads();  // every thread's entries of sel are written
-        if (l == 0) break;
-        const int cl = l - 1, R = A.fan[l];
-        const int nk = keff * R, past = cnt[l] * R;
-        const int nc = nk + (cnt[cl] - past);
-        float* kout = lds ? s_keys : A.keys + ((size_t)cl * units + u) * A.cap;
-        int32_t* iout = lds ? s_ids : A.cid + ((size_t)cl * units + u) * A.cap;
+    // Routing keys (and, with iout, ids) of positions [0, nc) of a list of
+    // level cl entries, position p holding entry id_at(p): every wavefront
+    // issues the loads of up to 16U rows at once, then scores them on MFMA.
+    auto score = [&](int cl, int nc, auto id_at, float* kout, int32_t* iout) {
         for (int p0 = 16 * U * w; p0 < nc; p0 += 16 * U * NW) {
             int id[U];
 #pragma unroll
             for (int t = 0; t < U; ++t) {
                 const int rel = 16 * t + lr;
-                const int p = p0 + rel < nc ? p0 + rel : p0;  // past the end: the pass's first row
-                id[t] = p < nk ? sel[p / R] * R + (p - (p / R) * R) : past + (p - nk);
+                id[t] = id_at(p0 + rel < nc ? p0 + rel : p0);  // past the end: the pass's first row
             }
             const __bf16* krow[U];
 #pragma unroll
@@ -521,9 +504,11 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
             for (int t = 0; t < U; ++t)
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(krow[t] + 32 * kk + 8 * lg);
+            if (iout) {
 #pragma unroll
-            for (int t = 0; t < U; ++t)
-                if (lg == 0 && p0 + 16 * t + lr < nc) iout[p0 + 16 * t + lr] = id[t];
+                for (int t = 0; t < U; ++t)
+                    if (lg == 0 && p0 + 16 * t + lr < nc) iout[p0 + 16 * t + lr] = id[t];
+            }
 #pragma unroll
             for (int h2 = 0; h2 < U / 2; ++h2) {
                 f32x4_t s[2];
@@ -541,7 +526,33 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
                 if (krel >= 0 && q < nc) kout[q] = kv;
             }
         }
-        __syncthreads();  // the level's keys and ids are written
+        __syncthreads();  // the list's keys and ids are written
+    };
+    float* const top_keys = A.keys + ((size_t)A.L * units + u) * A.cap;
+    if (A.fold_top)  // the top level's keys here (its attention is in the final list)
+        score(A.L, cnt[A.L], [](int p) { return p; }, lds ? s_keys : top_keys, (int32_t*)nullptr);
+    int n = cnt[A.L], keff = 0;
+    for (int l = A.L; l >= 0; --l) {
+        const int k = A.topk[l];
+        int32_t* sel = sel_of(l);
+        if (l == A.L && !(lds && A.fold_top))
+            keff = chain_topk(top_keys, (const int32_t*)nullptr, n, k, sel, sh, &s_keff);
+        else if (l == A.L)
+            keff = chain_topk(s_keys, (const int32_t*)nullptr, n, k, sel, sh, &s_keff);
+        else if (lds)
+            keff = chain_topk(s_keys, s_ids, n, k, sel, sh, &s_keff);
+        else
+            keff = chain_topk(A.keys + ((size_t)l * units + u) * A.cap,
+                              A.cid + ((size_t)l * units + u) * A.cap, n, k, sel, sh, &s_keff);
+        if (tid == 0) kept[l] = keff;
+        __syncthreads();  // every thread's entries of sel are written
+        if (l == 0) break;
+        const int cl = l - 1, R = A.fan[l];
+        const int nk = keff * R, past = cnt[l] * R;
+        const int nc = nk + (cnt[cl] - past);
+        score(cl, nc, [&](int p) { return p < nk ? sel[p / R] * R + (p - (p / R) * R) : past + (p - nk); },
+              lds ? s_keys : A.keys + ((size_t)cl * units + u) * A.cap,
+              lds ? s_ids : A.cid + ((size_t)cl * units + u) * A.cap);
         n = nc;
     }
     // the gists: the final list
@@ -566,6 +577,8 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
                 at += e + (cnt[lp] - past);
             }
         }
+        seg[2 * kMaxLevels + 6] = at;  // (folded top level) its entries
+        if (A.fold_top) at += cnt[A.L];
         seg[2 * kMaxLevels + 7] = at;
     }
     __syncthreads();
@@ -592,6 +605,10 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
             for (int p = tid; p < e + (cnt[lp] - past); p += kSelThreads)
                 fd[at + p] = entry_desc(A, lp, b, g, p < e ? sl[p] : past + (p - e));
         }
+    }
+    if (A.fold_top) {
+        const int at = seg[2 * kMaxLevels + 6];
+        for (int p = tid; p < cnt[A.L]; p += kSelThreads) fd[at + p] = desc_of(A.L, p);
     }
     if (tid == 0) A.nfin[u] = seg[2 * kMaxLevels + 7];
     // the caller's copies of the kept ids
@@ -662,10 +679,12 @@ __global__ __launch_bounds__(256) void lv_merge_kernel(LvArgs A) {
 template <int D>
 hipError_t launch_d(const LvArgs& A, hipStream_t st) {
     const int units = A.a.B * A.a.Hkv;
-    // the top level: keys and attention over all its entries
-    hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A, 1, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!A.fold_top) {
+        // the top level: keys and attention over all its entries
+        hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A, 1, 0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (A.chain_lds)
         hipLaunchKernelGGL((lv_chain_kernel<D, true>), dim3(units), dim3(kSelThreads), 0, st, A);
     else
