@@ -145,30 +145,54 @@ __device__ inline float tile_keys(const f32x4_t (&s)[2], int lr, int lg, float t
 // largest maximum M and the normaliser sum_i l_i 2^(m_i - M), then each output
 // element sum_i acc_i 2^(m_i - M) / normaliser.  An empty set gives zeros.
 // sc: LDS for the scale factors 2^(m_i - M) of up to sc_slots slots (past
-// that they are recomputed from the maxima); the loads of each step are
-// issued together, eight slots at a time.
+// that they are recomputed from the maxima).  The loads go out together: each
+// thread's (max, sum) words of up to 32 slots and its first output pair's
+// accumulators of up to 16 slots at the start, the rest eight slots at a time.
 __device__ void merge_unit_block(const LvArgs& A, int u, float* sc, int sc_slots) {
+    constexpr int PF = 16;  // slots of the first output pair loaded up front
     __shared__ float s_M[16], s_inv[16];
     const Args& a = A.a;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
     const int G = a.G, D = a.D, NS = A.NS;
     const float2* ml = a.part_ml + (size_t)u * NS * G;
     const float* acc = a.part_acc + (size_t)u * NS * G * D;
+    const int half = D / 2;
+    const int e0 = threadIdx.x;
+    const bool has0 = e0 < G * half;
+    const int hh0 = has0 ? e0 / half : 0, d0 = 2 * (e0 - hh0 * half);
+    float2 pv[PF];
+#pragma unroll
+    for (int t = 0; t < PF; ++t)
+        pv[t] = has0 && t < NS ? ld_dev2((const float2*)(acc + ((size_t)t * G + hh0) * D + d0))
+                               : make_float2(0.f, 0.f);
     {
         const int h = threadIdx.x >> 4, j = threadIdx.x & 15;
-        float m = -INFINITY;
+        float2 mv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            mv[t] = h < G && j + 16 * t < NS ? ld_dev2(ml + (size_t)(j + 16 * t) * G + h)
+                                             : make_float2(-INFINITY, 0.f);
+        float m = fmaxf(mv[0].x, mv[1].x);
         if (h < G)
-            for (int i = j; i < NS; i += 16) m = fmaxf(m, ld_dev2(ml + (size_t)i * G + h).x);
+            for (int i = j + 32; i < NS; i += 16) m = fmaxf(m, ld_dev2(ml + (size_t)i * G + h).x);
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
         float l = 0.f;
-        if (h < G)
-            for (int i = j; i < NS; i += 16) {
+        if (h < G) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int i = j + 16 * t;
+                const float f = (m != -INFINITY && mv[t].x != -INFINITY) ? exp2f(mv[t].x - m) : 0.f;
+                l += mv[t].y * f;
+                if (i < NS && i < sc_slots) sc[i * 16 + h] = f;
+            }
+            for (int i = j + 32; i < NS; i += 16) {
                 const float2 v = ld_dev2(ml + (size_t)i * G + h);
                 const float f = (m != -INFINITY && v.x != -INFINITY) ? exp2f(v.x - m) : 0.f;
                 l += v.y * f;
                 if (i < sc_slots) sc[i * 16 + h] = f;
             }
+        }
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) l += __shfl_xor(l, off);
         if (h < G && j == 0) {
@@ -178,31 +202,39 @@ __device__ void merge_unit_block(const LvArgs& A, int u, float* sc, int sc_slots
     }
     __syncthreads();
     __bf16* out = (__bf16*)a.out + ((size_t)b * a.Hq + (size_t)g * G) * D;
-    const int half = D / 2;
-    for (int e = threadIdx.x; e < G * half; e += blockDim.x) {
+    auto scale = [&](int i, int hh, float M) -> float {
+        if (i < sc_slots) return sc[i * 16 + hh];
+        const float mi = ld_dev2(ml + (size_t)i * G + hh).x;
+        return (M != -INFINITY && mi != -INFINITY) ? exp2f(mi - M) : 0.f;
+    };
+    for (int e = e0; e < G * half; e += blockDim.x) {
         const int hh = e / half, d = 2 * (e - hh * half);
         const float M = s_M[hh];
         float ox = 0.f, oy = 0.f;
-        for (int i0 = 0; i0 < NS; i0 += 8) {
+        int i0 = 0;
+        if (e == e0) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t)
+                if (t < NS) {
+                    const float f = scale(t, hh, M);
+                    ox += pv[t].x * f;
+                    oy += pv[t].y * f;
+                }
+            i0 = PF;
+        }
+        for (; i0 < NS; i0 += 8) {
             float2 v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 v[t] = i0 + t < NS ? ld_dev2((const float2*)(acc + ((size_t)(i0 + t) * G + hh) * D + d))
                                    : make_float2(0.f, 0.f);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int i = i0 + t;
-                if (i >= NS) break;
-                float f;
-                if (i < sc_slots) {
-                    f = sc[i * 16 + hh];
-                } else {
-                    const float mi = ld_dev2(ml + (size_t)i * G + hh).x;
-                    f = (M != -INFINITY && mi != -INFINITY) ? exp2f(mi - M) : 0.f;
+            for (int t = 0; t < 8; ++t)
+                if (i0 + t < NS) {
+                    const float f = scale(i0 + t, hh, M);
+                    ox += v[t].x * f;
+                    oy += v[t].y * f;
                 }
-                ox += v[t].x * f;
-                oy += v[t].y * f;
-            }
         }
         out[hh * D + d] = (__bf16)(ox * s_inv[hh]);
         out[hh * D + d + 1] = (__bf16)(oy * s_inv[hh]);
