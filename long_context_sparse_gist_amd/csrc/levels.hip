@@ -24,6 +24,7 @@
 #include "gsa_lists.h"
 #include "gsa_levels.h"
 #include "gsa_select.h"
+#include "gsa_wave_select.h"
 
 namespace gsa {
 namespace {
