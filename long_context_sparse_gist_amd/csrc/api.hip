@@ -352,7 +352,8 @@ void make_lv_plan(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* 
     if (A.fold_top) f += top;
     A.fcap = (int)(f > 1 ? f : 1);
     auto splits = [](long rows) { return (int)(rows > 0 ? (rows + 127) / 128 : 1); };
-    A.S_top = A.fold_top ? 0 : splits(top);
+    // the top-level pass: at most kTopSplits workgroups per unit, each looping over its blocks
+    A.S_top = A.fold_top ? 0 : (int)std::min<long>(splits(top), gsa::kTopSplits);
     A.S_fin = splits(A.fcap);
     A.NS = A.S_top + A.S_fin;
     pl.counters = (size_t)units <= kCtlWords - kHdrWords;

@@ -10,6 +10,7 @@ constexpr int kDescShift = 56;    // row descriptor: array id << 56 | element of
 constexpr int kChainCap = 8192;   // candidate rows the select chain keeps in LDS
 constexpr int kChainSel = 4096;   // kept ids (all levels) the select chain keeps in LDS
 constexpr int kFoldTop = 1024;    // largest top level the select chain scores itself
+constexpr int kTopSplits = 64;    // workgroups per unit of the top-level pass
 constexpr int kChainBt = 4096;    // block-table entries per sequence the select chain keeps in LDS
 
 struct LvArgs {

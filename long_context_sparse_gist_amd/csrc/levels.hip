@@ -242,15 +242,12 @@ __device__ void merge_unit_block(const LvArgs& A, int u, float* sc, int sc_slots
     }
 }
 
-// Attention over one list per unit, one partial per 128-row split into
-// partial slot slot0 + split (an empty split writes an empty partial).
-//   top = 1  every entry of the top level; also its routing keys, into the
-//            top level's key buffer
-//   top = 0  the final attention list; with arrival counters, the unit's
-//            last workgroup to finish merges the unit's partials and clears
-//            its counter
+// Attention over the final list of each unit, one partial per 128-row split
+// into partial slot slot0 + split (an empty split writes an empty partial);
+// with arrival counters, the unit's last workgroup to finish merges the
+// unit's partials and clears its counter.
 template <int D>
-__global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slot0) {
+__device__ __forceinline__ void lv_attn_body(const LvArgs& A, int slot0) {
     constexpr int KK = D / 32, DB = D / 16, LDW = 32 + 4;
     constexpr int VT = kWaves * D * LDW * 2, RED = kWaves * 16 * D * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem[VT > RED ? VT : RED];
@@ -260,11 +257,11 @@ __global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slo
     const int u = blockIdx.y, split = blockIdx.x;
     const int b = u / a.Hkv, g = u - b * a.Hkv;
     const int G = a.G;
-    const int len = top ? top_count(A, b) : A.nfin[u];
+    const int len = A.nfin[u];
     const int p0 = split * kRows;
     const int count = min(kRows, len - p0);
     const size_t pbase = ((size_t)u * A.NS + slot0 + split) * G;
-    const bool dev = !top && A.uctr;  // partials read by this launch's merging workgroup
+    const bool dev = A.uctr != nullptr;  // partials read by this launch's merging workgroup
     auto put_acc = [&](size_t i, float v) {
         if (dev) st_dev(a.part_acc + i, v);
         else a.part_acc[i] = v;
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slo
         for (int t = 0; t < 2; ++t) {
             const int rel = 32 * w + 16 * t + lr;
             const int p = p0 + (rel < count ? rel : 0);
-            const int64_t d = top ? entry_desc(A, A.L, b, g, p) : A.fdesc[(size_t)u * A.fcap + p];
+            const int64_t d = A.fdesc[(size_t)u * A.fcap + p];
             const int arr = (int)(d >> kDescShift);
             const size_t off = (size_t)(d & kOffMask);
             krow[t] = (const __bf16*)(arr ? A.lk[arr] : a.kc) + off;
@@ -314,12 +311,6 @@ __global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slo
             s[t] = acc;
         }
         auto rel_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * lg + r; };
-        if (top) {
-            int krel;
-            const float kv = tile_keys(s, lr, lg, a.tau, krel);
-            if (krel >= 0 && 32 * w + krel < count)
-                A.keys[((size_t)A.L * a.B * a.Hkv + u) * A.cap + p0 + 32 * w + krel] = kv;
-        }
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -414,6 +405,174 @@ __global__ __launch_bounds__(256) void lv_attn_kernel(LvArgs A, int top, int slo
     if (!s_last) return;
     merge_unit_block(A, u, (float*)smem, (int)(sizeof(smem) / (16 * sizeof(float))));
     if (threadIdx.x == 0) st_dev(A.uctr + u, 0u);  // zero again for the next call
+}
+
+// The top level's keys and attention: every top-level row (the whole gist
+// list when there is no meta level).  Workgroup `split` of a unit takes the
+// 128-row blocks split, split + S_top, ...; each wavefront keeps a running
+// per-head maximum, normaliser and output over its 32 rows of every block
+// (online softmax, the output rescaled when the maximum moves), and the four
+// wavefronts' states are combined into the workgroup's partial at the end.
+// S_top is capped, so a long top level gives few partials to merge.
+template <int D>
+__global__ __launch_bounds__(256) void lv_top_kernel(LvArgs A) {
+    constexpr int KK = D / 32, DB = D / 16, LDW = 32 + 4;
+    constexpr int VT = kWaves * D * LDW * 2, RED = kWaves * 16 * D * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[VT > RED ? VT : RED];
+    __shared__ float s_max[kWaves][16], s_sum[kWaves][16];
+    const Args& a = A.a;
+    const int u = blockIdx.y, split = blockIdx.x;
+    const int b = u / a.Hkv, g = u - b * a.Hkv;
+    const int G = a.G;
+    const int len = top_count(A, b);
+    const int nblk = (len + kRows - 1) / kRows;
+    const size_t pbase = ((size_t)u * A.NS + split) * G;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
+    float* keys = A.keys + ((size_t)A.L * a.B * a.Hkv + u) * A.cap;
+    bf16x8_t qB[KK];
+    load_q<D>(a, b, g, lr, lg, qB);
+    float m_run = -INFINITY, l_run = 0.f;  // head lr, exp2 domain
+    f32x4_t o[DB];                          // o[db][r]: head 4lg + r, column 16db + lr
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    __bf16* vt = (__bf16*)smem + (size_t)w * D * LDW;
+    for (int blk = split; blk < nblk; blk += gridDim.x) {
+        const int p0 = blk * kRows;
+        const int count = min(kRows, len - p0);
+        const __bf16* krow[2];
+        const __bf16* vrow[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int rel = 32 * w + 16 * t + lr;
+            const int64_t d = entry_desc(A, A.L, b, g, p0 + (rel < count ? rel : 0));
+            const int arr = (int)(d >> kDescShift);
+            const size_t off = (size_t)(d & kOffMask);
+            krow[t] = (const __bf16*)(arr ? A.lk[arr] : a.kc) + off;
+            vrow[t] = (const __bf16*)(arr ? A.lv[arr] : a.vc) + off;
+        }
+        bf16x8_t kA[2][KK], vA[2][KK];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) kA[t][kk] = *(const bf16x8_t*)(krow[t] + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) vA[t][kk] = *(const bf16x8_t*)(vrow[t] + 32 * kk + 8 * lg);
+        f32x4_t s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[t][kk], qB[kk], acc, 0, 0, 0);
+            s[t] = acc;
+        }
+        {
+            int krel;
+            const float kv = tile_keys(s, lr, lg, a.tau, krel);
+            if (krel >= 0 && 32 * w + krel < count) keys[p0 + 32 * w + krel] = kv;
+        }
+        auto rel_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * lg + r; };
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (rel_of(t, r) < count) mx = fmaxf(mx, s[t][r]);
+        mx = rows4_max(mx) * a.tau_log2e;
+        const float m_new = fmaxf(m_run, mx);
+        // the factor that moves this head's state to the new maximum (1 while
+        // the wavefront has seen no row)
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        bf16x8_t P;
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = rel_of(t, r) < count ? exp2f(s[t][r] * a.tau_log2e - m_new) : 0.f;
+                const __bf16 pb = (__bf16)pv;
+                lsum += (float)pb;
+                P[4 * t + r] = pb;
+            }
+        l_run = l_run * alpha + rows4_sum(lsum);
+        m_run = m_new;
+        // the output's rows are heads 4lg + r: their factors from lanes 4lg + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * lg + r);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db][r] *= ar;
+        }
+        // V transposed through this wavefront's LDS tile
+        __syncthreads();  // the previous block's reads of the tile are done
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vt[(32 * kk + 8 * lg + i) * LDW + 16 * t + lr] = vA[t][kk][i];
+        __syncthreads();
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const __bf16* col = vt + (16 * db + lr) * LDW;
+            const bf16x4_t lo = *(const bf16x4_t*)(col + 4 * lg);
+            const bf16x4_t hi = *(const bf16x4_t*)(col + 16 + 4 * lg);
+            bf16x8_t vb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vb[i] = lo[i];
+                vb[4 + i] = hi[i];
+            }
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P, vb, o[db], 0, 0, 0);
+        }
+    }
+    // combine the wavefronts: per head the largest maximum, the others' sums
+    // and outputs rescaled to it
+    __syncthreads();  // the V tiles are free
+    if (lg == 0) {
+        s_max[w][lr] = m_run;
+        s_sum[w][lr] = l_run;
+    }
+    __syncthreads();
+    float* red = (float*)smem;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * lg + r;
+        if (h < G) {
+            float M = s_max[0][h];
+#pragma unroll
+            for (int i = 1; i < kWaves; ++i) M = fmaxf(M, s_max[i][h]);
+            const float f = s_max[w][h] == -INFINITY ? 0.f : exp2f(s_max[w][h] - M);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) red[((size_t)w * 16 + h) * D + 16 * db + lr] = o[db][r] * f;
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int h = e / D, d = e - h * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) acc += red[((size_t)i * 16 + h) * D + d];
+        a.part_acc[pbase * D + e] = acc;
+    }
+    if (threadIdx.x < (unsigned)G) {
+        const int h = threadIdx.x;
+        float M = s_max[0][h];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) M = fmaxf(M, s_max[i][h]);
+        float l = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i)
+            if (s_max[i][h] != -INFINITY) l += s_sum[i][h] * exp2f(s_max[i][h] - M);
+        a.part_ml[pbase + h] = make_float2(M, l);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void lv_attn_final_kernel(LvArgs A, int slot0) {
+    lv_attn_body<D>(A, slot0);
 }
 
 // Number of ascending entries of sel[0..k) below `bound`.
@@ -715,7 +874,7 @@ hipError_t launch_d(const LvArgs& A, hipStream_t st) {
     hipError_t e;
     if (!A.fold_top) {
         // the top level: keys and attention over all its entries
-        hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A, 1, 0);
+        hipLaunchKernelGGL((lv_top_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (A.chain_lds)
@@ -723,7 +882,7 @@ hipError_t launch_d(const LvArgs& A, hipStream_t st) {
     else
         hipLaunchKernelGGL((lv_chain_kernel<D, false>), dim3(units), dim3(kSelThreads), 0, st, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((lv_attn_kernel<D>), dim3(A.S_fin, units), dim3(256), 0, st, A, 0, A.S_top);
+    hipLaunchKernelGGL((lv_attn_final_kernel<D>), dim3(A.S_fin, units), dim3(256), 0, st, A, A.S_top);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (!A.uctr) hipLaunchKernelGGL(lv_merge_kernel, dim3(A.a.G, units), dim3(256), 0, st, A);
     return hipGetLastError();

@@ -106,6 +106,28 @@ def test_levels_hand_worked_bf16(gpu, name):
     assert np.all(o[2:] == 0.0)
 
 
+LONG_TOP = gi.Workload("lv-long-top", gi.BF16, 2, 8, 2, 128, 16, 20000, 24, 16,
+                       plant="align", plant_count=4)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("depth", [0, 1])
+@pytest.mark.parametrize("lens", ["full", "ragged"])
+def test_levels_long_top(gpu, depth, lens):
+    """A top level longer than the top-level pass's workgroups cover one block
+    each (20000 gists, or 10000 meta entries of fanout 2): each workgroup
+    folds several 128-row blocks with its online softmax, and ragged lengths
+    leave some of a unit's workgroups without a block."""
+    wl = LONG_TOP
+    say(f"[levels] long top depth={depth} lens={lens}")
+    inp = gi.make_inputs(wl, 1300 + depth, seq_lens=lens_for(wl, lens, 31 + depth))
+    fanouts, tops = ((), ()) if depth == 0 else ((2,), (40,))
+    g = GU.to(inp, gpu)
+    lv = levels_on(inp, fanouts, tops, 60 + depth, gpu)
+    res = GU.run_gpu_m(g, lv)
+    GU.check_mgsa(inp, [(k.cpu(), v.cpu(), R, t) for k, v, R, t in lv], res)
+
+
 MGSA_1M = gi.Workload("mgsa-1m-c16-r16x16", gi.BF16, 4, 32, 8, 128, 16, 65536, 64, 16,
                       plant="align", plant_count=16)
 
