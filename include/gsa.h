@@ -141,7 +141,8 @@ typedef struct {
 } hgsa_meta_t;
 
 /* Size of the control block at the start of every workspace: an error word
- * and the per-(batch, kv-head) counters of the single-launch path. */
+ * and the per-(batch, kv-head) counters of the single-launch path and of
+ * mgsa_decode's final attention. */
 #define GSA_WORKSPACE_CONTROL_BYTES ((size_t)16384 + (size_t)512 * 25088)
 /* Byte offset (in the control block) of the 32-bit error word.  The
  * single-launch kernel's workgroups hand data to each other through the
@@ -241,7 +242,10 @@ typedef struct {
 #define GSA_MAX_LEVELS 8
 
 /* Bytes of workspace mgsa_decode needs (0 if the shapes are invalid); the
- * same layout rules as gsa_workspace_size (control block first). */
+ * same rules as gsa_workspace_size: 256-byte aligned, the control block first,
+ * zero before the first use and left zero by every call that completes (the
+ * call counts its final attention's workgroups there, one word per
+ * (batch, kv-head)). */
 size_t mgsa_workspace_size(const gsa_params_t* p, const gsa_kv_t* kv, const gsa_level_t* levels,
                            int32_t num_levels);
 
