@@ -113,6 +113,12 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
 
     // this lane's column (lr) of each of the wavefront's column blocks
     WaveAttnL<D> wa[kNCB];
+    // lsum[cb][r]: the sum of column 4lg + r's bf16 weights, accumulated on
+    // MFMA (the weights times a column of ones) and rescaled with the output
+    f32x4_t lsum[kNCB];
+    bf16x8_t ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
     int colm[kNCB], cols[kNCB];
     bool colv[kNCB];
     int glo[kNCB], ghi[kNCB], slo[kNCB], shi[kNCB];  // keys a column sees: gists [glo, ghi], slots [slo, shi]
@@ -143,6 +149,7 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
         for (int db = 0; db < DB; ++db) wa[cb].o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         wa[cb].m = -INFINITY;
         wa[cb].l = 0.f;
+        lsum[cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
 
     // key blocks: the gists of chunks [0, m_hi), then the slots [l0, s_hi]
@@ -183,6 +190,9 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
                 kA[t][kk] = *(const bf16x8_t*)(kt + r * 2 * D + 16 * ((4 * kk + lg) ^ (r % CPR)));
         }
         const bool gist_blk = i < nA;
+        // a gist block before the first query's chunk is visible to every
+        // column: no mask (block-uniform)
+        const bool full = gist_blk && 32 * i + 32 <= m_lo;
         const int kbase = gist_blk ? 32 * i : l0 + 32 * (i - nA);
 #pragma unroll
         for (int cb = 0; cb < kNCB; ++cb) {
@@ -193,14 +203,21 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
             const int lo = gist_blk ? glo[cb] : slo[cb], hi = gist_blk ? ghi[cb] : shi[cb];
             bool ok[2][4];
             float bm = -INFINITY;
+            if (full) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = kbase + 16 * t + 4 * lg + r;
-                    ok[t][r] = (key >= lo) & (key <= hi);
-                    bm = fmaxf(bm, ok[t][r] ? sc[t][r] : -INFINITY);
-                }
+                    for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sc[t][r]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = kbase + 16 * t + 4 * lg + r;
+                        ok[t][r] = (key >= lo) & (key <= hi);
+                        bm = fmaxf(bm, ok[t][r] ? sc[t][r] : -INFINITY);
+                    }
+            }
             bm = rows4_max(bm);
             // the column's reference maximum moves only when the block's
             // exceeds it by more than 2^8 in probability (the weights stay
@@ -212,29 +229,33 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
             if (__ballot(up)) {
                 // (the hardware exp2: exp2(-inf) = 0)
                 const float alpha = up ? __builtin_amdgcn_exp2f((mold - mnew) * tl) : 1.f;
-                wa[cb].l *= alpha;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float ar = __shfl(alpha, 4 * lg + r);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) wa[cb].o[db][r] *= ar;
+                    lsum[cb][r] *= ar;
                 }
             }
             const float mb = mnew * tl;  // (arguments of the kept keys are <= 8)
             bf16x8_t P;
-            float ls = 0.f;
+            if (full) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(sc[t][r] * tl - mb);
-                    const __bf16 pb = (__bf16)(ok[t][r] ? e : 0.f);
-                    ls += (float)pb;
-                    P[4 * t + r] = pb;
-                }
-            wa[cb].l += ls;
+                    for (int r = 0; r < 4; ++r) P[4 * t + r] = (__bf16)__builtin_amdgcn_exp2f(sc[t][r] * tl - mb);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = __builtin_amdgcn_exp2f(sc[t][r] * tl - mb);
+                        P[4 * t + r] = (__bf16)(ok[t][r] ? e : 0.f);
+                    }
+            }
             wa[cb].m = mnew;
             wa[cb].pv(P, vt);
+            lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P, ones, lsum[cb], 0, 0, 0);
         }
         // this block's LDS reads are done and block i+1's tiles have landed
         wait_mem();
@@ -242,10 +263,9 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
     // out[column 4lg + r][16db + lr] = o[db][r] / l(column 4lg + r)
 #pragma unroll
     for (int cb = 0; cb < kNCB; ++cb) {
-        const float lcol = rows4_sum(wa[cb].l);  // lane lr: column lr's sum
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float L = __shfl(lcol, 4 * lg + r);
+            const float L = lsum[cb][r];
             const int j = jw + (w * kNCB + cb) * 16 + 4 * lg + r;
             if (j >= a.ncols) continue;
             const int t = j / G, h = j - t * G;
