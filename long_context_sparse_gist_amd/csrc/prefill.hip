@@ -36,6 +36,7 @@ struct PrefillArgs {
     const int32_t* bt;    // [B][max_pages]
     const int32_t* q_start;  // [B] first query slot
     int B, Hq, Hkv, G, C, T, spp, max_pages, ncols;  // ncols = T * G
+    uint64_t spp_inv;     // ceil(2^32 / spp): slot -> logical page by multiply
     float tau_log2e;
 };
 
@@ -64,7 +65,7 @@ struct PTiles {
 // offsets of the block's rows lane % 16 and 16 + lane % 16.  K: position p of
 // row r holds the row's 16-byte chunk p ^ (r mod CPR); V: the layout
 // WaveAttnL::pv reads.
-template <int D>
+template <int D, bool BTL>
 __device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, size_t o1, unsigned char* kt,
                                             unsigned char* vt, int w, int lane) {
     constexpr int CPR = D / 8;
@@ -82,7 +83,8 @@ __device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, siz
     }
 }
 
-template <int D>
+// BTL: the block-table row is kept in LDS (at most kPBtLds pages).
+template <int D, bool BTL>
 __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) {  // (4 wavefronts per SIMD)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int KK = D / 32, DB = D / 16, CPR = D / 8, TILE = PTiles<D>::TILE;
@@ -100,14 +102,16 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
     const int t_lo = jw / G, t_hi = min(T - 1, (jw + kPCols - 1) / G);
     const int m_lo = (s0 + t_lo) / (C + 1), m_hi = (s0 + t_hi) / (C + 1);
     const int s_hi = s0 + t_hi, l0 = m_lo * (C + 1);
-    const bool bt_lds = a.max_pages <= kPBtLds;
     const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
-    if (bt_lds)
+    if (BTL)
         for (int i = tid; i < a.max_pages; i += kPThreads) btl[i] = btrow[i];
     __syncthreads();
+    // slots number below 2^30, so slot * ceil(2^32 / spp) / 2^32 exceeds
+    // slot / spp by less than 1/4: the quotient is exact or one too large
     auto slot_off = [&](int slot) -> size_t {
-        const int p = slot / a.spp;
-        const int phys = bt_lds ? btl[p] : btrow[p];
+        int p = (int)(((uint64_t)(uint32_t)slot * a.spp_inv) >> 32);
+        p -= p * a.spp > slot;
+        const int phys = BTL ? btl[p] : btrow[p];
         return (((size_t)phys * a.Hkv + g) * a.spp + (slot - p * a.spp)) * (size_t)D;
     };
 
@@ -167,18 +171,21 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
         o0 = slot_off(s[0]);
         o1 = slot_off(s[1]);
     };
-    // every wavefront issues its share of block i's tile loads
-    auto issue = [&](int i, int buf) {
-        size_t o0, o1;
-        rows_of(i, o0, o1);
-        issue_tiles<D>(a, o0, o1, ktile + buf * TILE, vtile + buf * TILE, w, lane);
-    };
     const float tl = a.tau_log2e;
-    if (nblk > 0) issue(0, 0);
+    // every wavefront issues its share of block i's tile loads
+    if (nblk > 0) {
+        size_t o0, o1;
+        rows_of(0, o0, o1);
+        issue_tiles<D, BTL>(a, o0, o1, ktile, vtile, w, lane);
+    }
     wait_mem();
     for (int i = 0; i < nblk; ++i) {
         __syncthreads();  // block i's tiles are in LDS; buffer (i+1)&1 is free
-        if (i + 1 < nblk) issue(i + 1, (i + 1) & 1);
+        if (i + 1 < nblk) {
+            size_t o0, o1;
+            rows_of(i + 1, o0, o1);
+            issue_tiles<D, BTL>(a, o0, o1, ktile + ((i + 1) & 1) * TILE, vtile + ((i + 1) & 1) * TILE, w, lane);
+        }
         const unsigned char* kt = ktile + (i & 1) * TILE;
         const unsigned char* vt = vtile + (i & 1) * TILE;
         bf16x8_t kA[2][KK];
@@ -299,12 +306,21 @@ hipError_t launch_prefill(const void* q, void* out, const void* kc, const void* 
     a.spp = spp;
     a.max_pages = max_pages;
     a.ncols = T * a.G;
+    a.spp_inv = ((1ull << 32) + (uint64_t)spp - 1) / (uint64_t)spp;
     a.tau_log2e = (float)((double)tau * 1.4426950408889634);
     dim3 grid((a.ncols + kPCols - 1) / kPCols, B * Hkv);
-    if (D == 64)
-        hipLaunchKernelGGL((prefill_kernel<64>), grid, dim3(kPThreads), PTiles<64>::bytes(max_pages), st, a);
-    else
-        hipLaunchKernelGGL((prefill_kernel<128>), grid, dim3(kPThreads), PTiles<128>::bytes(max_pages), st, a);
+    const bool btl = max_pages <= kPBtLds;
+    if (D == 64) {
+        if (btl)
+            hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(kPThreads), PTiles<64>::bytes(max_pages), st, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(kPThreads), PTiles<64>::bytes(max_pages), st, a);
+    } else {
+        if (btl)
+            hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(kPThreads), PTiles<128>::bytes(max_pages), st, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(kPThreads), PTiles<128>::bytes(max_pages), st, a);
+    }
     return hipGetLastError();
 }
 

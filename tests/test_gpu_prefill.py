@@ -70,6 +70,23 @@ def test_prefill_every_output(gpu, name, T, kind):
     GU.assert_close(got, ref, wl.dtype, f"{name} T={T} {kind}")
 
 
+LONG_BT = gi.Workload("pf-long-bt", gi.BF16, 1, 2, 1, 64, 4, 8000, 0, 1)
+
+
+@pytest.mark.parametrize("kind", ["mid", "end"])
+def test_prefill_block_table_in_memory(gpu, kind):
+    """A block-table row longer than the kernel keeps in LDS (8000 one-chunk
+    pages): the row is read from memory."""
+    wl = LONG_BT
+    say(f"[prefill] {wl.name} {kind}")
+    inp = gi.make_inputs(wl, 1500)
+    q = queries(wl, 37, 11, gpu)
+    starts = starts_for(wl, 37, kind, 5)
+    got = run(GU.to(inp, gpu), q, starts)
+    ref = PP.run_prefill(inp, q.cpu(), starts)
+    GU.assert_close(got, ref, wl.dtype, f"{wl.name} {kind}")
+
+
 def test_prefill_repeat_is_bitwise(gpu):
     wl = SHAPES["pf-b2-g7-d128-c16"]
     inp = GU.to(gi.make_inputs(wl, 1401), gpu)
