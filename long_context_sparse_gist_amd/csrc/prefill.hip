@@ -60,27 +60,19 @@ struct PTiles {
     }
 };
 
-// Issue this wavefront's share of one key block's tile loads (1 KB per
-// instruction: 64 lanes x 16 bytes into consecutive LDS).  o0 / o1: element
-// offsets of the block's rows lane % 16 and 16 + lane % 16.  K: position p of
-// row r holds the row's 16-byte chunk p ^ (r mod CPR); V: the layout
-// WaveAttnL::pv reads.
+// Issue part w of one key block's tile loads (1 KB per instruction: 64 lanes
+// x 16 bytes into consecutive LDS), for wavefronts w < CPR / 2: lane l loads
+// the 16-byte chunk p = (64w + l) % CPR of row r = (64w + l) / CPR, whose
+// element offset is ro.  K: position p of row r holds the row's chunk
+// p ^ (r mod CPR); V: the layout WaveAttnL::pv reads.
 template <int D, bool BTL>
-__device__ __forceinline__ void issue_tiles(const PrefillArgs& a, size_t o0, size_t o1, unsigned char* kt,
-                                            unsigned char* vt, int w, int lane) {
+__device__ __forceinline__ void issue_part(const PrefillArgs& a, size_t ro, int r, int p, unsigned char* kt,
+                                           unsigned char* vt, int w) {
     constexpr int CPR = D / 8;
-#pragma unroll
-    for (int qq = 0; qq < CPR / 2; ++qq) {
-        if (qq % kPWaves != w) continue;
-        const int f = 64 * qq + lane, r = f / CPR, p = f % CPR;
-        const size_t src = (64 * qq) / CPR < 16 ? o0 : o1;  // uniform per qq
-        const unsigned lo = __shfl((unsigned)src, r % 16), hi = __shfl((unsigned)(src >> 32), r % 16);
-        const size_t ro = ((size_t)hi << 32) | lo;
-        __builtin_amdgcn_global_load_lds((const __bf16*)a.kc + ro + 8 * (p ^ (r % CPR)),
-                                         (lds_void_t*)(kt + 1024 * qq), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __bf16*)a.vc + ro + 8 * (p ^ WaveAttnL<D>::swz(r)),
-                                         (lds_void_t*)(vt + 1024 * qq), 16, 0, 0);
-    }
+    __builtin_amdgcn_global_load_lds((const __bf16*)a.kc + ro + 8 * (p ^ (r % CPR)),
+                                     (lds_void_t*)(kt + 1024 * w), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __bf16*)a.vc + ro + 8 * (p ^ WaveAttnL<D>::swz(r)),
+                                     (lds_void_t*)(vt + 1024 * w), 16, 0, 0);
 }
 
 // BTL: the block-table row is kept in LDS (at most kPBtLds pages).
@@ -159,33 +151,29 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
     // key blocks: the gists of chunks [0, m_hi), then the slots [l0, s_hi]
     const int nA = (m_hi + 31) / 32;
     const int nblk = nA + (s_hi - l0 + 1 + 31) / 32;
-    // element offsets of block i's rows lr and 16 + lr (a row past the end
-    // repeats the last real one: it is masked)
-    auto rows_of = [&](int i, size_t& o0, size_t& o1) {
-        int s[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int k = 32 * i + 16 * hh + lr;
-            s[hh] = i < nA ? min(k, m_hi - 1) * (C + 1) + C : min(l0 + k - 32 * nA, s_hi);
-        }
-        o0 = slot_off(s[0]);
-        o1 = slot_off(s[1]);
+    // Each block's tiles are loaded by wavefronts w < CPR / 2, every lane one
+    // 16-byte chunk of row ir; the row's element offset for block i + 2 is
+    // computed during block i (its block-table read and arithmetic overlap
+    // that block's work) and used when block i + 1 starts.
+    const bool issuer = w < CPR / 2;  // (wave-uniform)
+    const int ir = issuer ? (64 * w + lane) / CPR : 0, ip = (64 * w + lane) % CPR;
+    // element offset of row ir of block i (a row past the end repeats the
+    // last real one: it is masked)
+    auto row_off = [&](int i) -> size_t {
+        const int k = 32 * i + ir;
+        return slot_off(i < nA ? min(k, m_hi - 1) * (C + 1) + C : min(l0 + k - 32 * nA, s_hi));
     };
     const float tl = a.tau_log2e;
-    // every wavefront issues its share of block i's tile loads
-    if (nblk > 0) {
-        size_t o0, o1;
-        rows_of(0, o0, o1);
-        issue_tiles<D, BTL>(a, o0, o1, ktile, vtile, w, lane);
+    size_t nxt = 0;
+    if (issuer) {
+        if (nblk > 0) issue_part<D, BTL>(a, row_off(0), ir, ip, ktile, vtile, w);
+        if (nblk > 1) nxt = row_off(1);
     }
     wait_mem();
     for (int i = 0; i < nblk; ++i) {
         __syncthreads();  // block i's tiles are in LDS; buffer (i+1)&1 is free
-        if (i + 1 < nblk) {
-            size_t o0, o1;
-            rows_of(i + 1, o0, o1);
-            issue_tiles<D, BTL>(a, o0, o1, ktile + ((i + 1) & 1) * TILE, vtile + ((i + 1) & 1) * TILE, w, lane);
-        }
+        if (issuer && i + 1 < nblk)
+            issue_part<D, BTL>(a, nxt, ir, ip, ktile + ((i + 1) & 1) * TILE, vtile + ((i + 1) & 1) * TILE, w);
         const unsigned char* kt = ktile + (i & 1) * TILE;
         const unsigned char* vt = vtile + (i & 1) * TILE;
         bf16x8_t kA[2][KK];
@@ -201,6 +189,7 @@ __global__ __launch_bounds__(kPThreads, 4) void prefill_kernel(PrefillArgs a) { 
         // column: no mask (block-uniform)
         const bool full = gist_blk && 32 * i + 32 <= m_lo;
         const int kbase = gist_blk ? 32 * i : l0 + 32 * (i - nA);
+        if (issuer && i + 2 < nblk) nxt = row_off(i + 2);
 #pragma unroll
         for (int cb = 0; cb < kNCB; ++cb) {
             f32x4_t sc[2];
