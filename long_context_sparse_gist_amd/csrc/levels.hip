@@ -623,7 +623,7 @@ __device__ inline int chain_topk(KeyPtr keys, IdPtr ids, int n, int k, OutPtr ou
 // selection buffers of its own in the workspace (no address is written twice
 // in the kernel).  The unit's block-table row is read into LDS up front when
 // it has at most kChainBt pages.
-template <int D, bool LDS>
+template <int D, bool LDS, bool BTL>
 __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
     constexpr int KK = D / 32, NW = kSelThreads / 64, U = 4;  // U tiles of 16 rows per wavefront
     __shared__ SelectSmem<kSelThreads> sh;
@@ -641,11 +641,9 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
     const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const size_t units = (size_t)a.B * a.Hkv;
     constexpr bool lds = LDS;
-    const bool bt_lds = a.max_pages <= kChainBt;
     const int32_t* btg = a.bt + (size_t)b * a.max_pages;
-    if (bt_lds)
+    if (BTL)
         for (int i = tid; i < a.max_pages; i += kSelThreads) s_bt[i] = btg[i];
-    const int32_t* btrow = bt_lds ? s_bt : btg;
     if (tid == 0) {
         int c[kMaxLevels + 1], t;
         level_counts(A, b, c, t);
@@ -658,7 +656,8 @@ __global__ __launch_bounds__(kSelThreads) void lv_chain_kernel(LvArgs A) {
     // element offset of logical slot s of this unit (block-table row btrow)
     auto slot_off = [&](int s) -> size_t {
         const int lp = s / a.spp, off = s - lp * a.spp;
-        return (((size_t)btrow[lp] * a.Hkv + g) * a.spp + off) * (size_t)a.D;
+        const int phys = BTL ? s_bt[lp] : btg[lp];
+        return (((size_t)phys * a.Hkv + g) * a.spp + off) * (size_t)a.D;
     };
     auto desc_of = [&](int l, int id) -> int64_t {
         if (l == 0) return (int64_t)slot_off(id * (a.C + 1) + a.C);
@@ -877,10 +876,18 @@ hipError_t launch_d(const LvArgs& A, hipStream_t st) {
         hipLaunchKernelGGL((lv_top_kernel<D>), dim3(A.S_top, units), dim3(256), 0, st, A);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (A.chain_lds)
-        hipLaunchKernelGGL((lv_chain_kernel<D, true>), dim3(units), dim3(kSelThreads), 0, st, A);
-    else
-        hipLaunchKernelGGL((lv_chain_kernel<D, false>), dim3(units), dim3(kSelThreads), 0, st, A);
+    const bool btl = A.a.max_pages <= kChainBt;
+    if (A.chain_lds) {
+        if (btl)
+            hipLaunchKernelGGL((lv_chain_kernel<D, true, true>), dim3(units), dim3(kSelThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL((lv_chain_kernel<D, true, false>), dim3(units), dim3(kSelThreads), 0, st, A);
+    } else {
+        if (btl)
+            hipLaunchKernelGGL((lv_chain_kernel<D, false, true>), dim3(units), dim3(kSelThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL((lv_chain_kernel<D, false, false>), dim3(units), dim3(kSelThreads), 0, st, A);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((lv_attn_final_kernel<D>), dim3(A.S_fin, units), dim3(256), 0, st, A, A.S_top);
     if ((e = hipGetLastError()) != hipSuccess) return e;
