@@ -325,7 +325,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has "
-              f"no multi-GPU mode in this build", file=sys.stderr)
+              f"no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
