@@ -106,6 +106,26 @@ def test_levels_hand_worked_bf16(gpu, name):
     assert np.all(o[2:] == 0.0)
 
 
+DEEP = {5: ((2, 2, 2, 2, 2), (40, 20, 10, 6, 4)),
+        8: ((2,) * 8, (30, 16, 8, 6, 4, 3, 2, 2))}
+
+
+@pytest.mark.parametrize("depth", sorted(DEEP))
+@pytest.mark.parametrize("lens", ["full", "edge"])
+def test_levels_deep(gpu, depth, lens):
+    """Five and eight (the most the ABI takes) meta levels of fanout 2 above
+    1100 gists: every level's kept ids and the final list's segments of every
+    level, every unit."""
+    wl = SMALL["lv-b2-g7-d128-c16"]
+    say(f"[levels] deep {depth} lens={lens}")
+    inp = gi.make_inputs(wl, 950 + depth, seq_lens=lens_for(wl, lens, 17 + depth))
+    fanouts, tops = DEEP[depth]
+    g = GU.to(inp, gpu)
+    lv = levels_on(inp, fanouts, tops, 70 + depth, gpu)
+    res = GU.run_gpu_m(g, lv)
+    GU.check_mgsa(inp, [(k.cpu(), v.cpu(), R, t) for k, v, R, t in lv], res)
+
+
 LONG_TOP = gi.Workload("lv-long-top", gi.BF16, 2, 8, 2, 128, 16, 20000, 24, 16,
                        plant="align", plant_count=4)
 
