@@ -148,6 +148,21 @@ def test_levels_long_top(gpu, depth, lens):
     GU.check_mgsa(inp, [(k.cpu(), v.cpu(), R, t) for k, v, R, t in lv], res)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("lens", ["full", "ragged"])
+def test_levels_long_candidates(gpu, lens):
+    """A candidate list longer than one wavefront selects (100 kept entries of
+    fanout 16 above 20000 gists: 1600 candidates), selected by the whole
+    workgroup from the lists the chain keeps in LDS."""
+    wl = LONG_TOP
+    say(f"[levels] long candidate list lens={lens}")
+    inp = gi.make_inputs(wl, 1320, seq_lens=lens_for(wl, lens, 41))
+    g = GU.to(inp, gpu)
+    lv = levels_on(inp, (16,), (100,), 80, gpu)
+    res = GU.run_gpu_m(g, lv)
+    GU.check_mgsa(inp, [(k.cpu(), v.cpu(), R, t) for k, v, R, t in lv], res)
+
+
 MGSA_1M = gi.Workload("mgsa-1m-c16-r16x16", gi.BF16, 4, 32, 8, 128, 16, 65536, 64, 16,
                       plant="align", plant_count=16)
 
