@@ -11,16 +11,21 @@
 //   select   the top-k_l candidates (ties to the lower id, NaN last);
 //   attend   the kept entries and the past-the-last-group entries of every
 //            level below the top, the kept chunks' raw tokens and the raw tail.
-// Launches (bf16, MFMA): the top level's keys and attention (many workgroups
-// per unit); the select chain, one workgroup per unit, which keeps each
-// level's top-k and scores the next level's candidates itself (MFMA, keys and
-// ids to per-level buffers, so no address is written twice in the kernel),
-// down to the gist level's select, which writes the final attention list; one
-// attention pass over that list, whose last workgroup per unit merges the
-// unit's partials (a separate merge launch when the arrival counters do not
-// fit the control block).  Every list is a per-unit array of row descriptors
-// (array id << 56 | element offset), so one attention kernel serves the top
-// level and the final set.
+// Launches (bf16, MFMA):
+//   - a top level longer than kFoldTop entries: its keys and attention
+//     (lv_top_kernel, at most kTopSplits workgroups per unit, each folding its
+//     128-row blocks with an online softmax);
+//   - the select chain (lv_chain_kernel), one workgroup per unit: a short top
+//     level's keys, then per level the top-k and the next level's candidates'
+//     ids and keys (MFMA), down to the gist level's select, which writes the
+//     final attention list (with a short top level's entries in it);
+//   - the final attention (lv_attn_final_kernel), 128 rows of the list per
+//     workgroup, whose last workgroup per unit merges the unit's partials (a
+//     separate merge launch when the arrival counters do not fit the control
+//     block).
+// Every list is a per-unit array of row descriptors (array id << 56 | element
+// offset), so the attention reads rows of any level and of the paged cache
+// alike.
 #include "gsa_lists.h"
 #include "gsa_levels.h"
 #include "gsa_select.h"
