@@ -151,6 +151,28 @@ def test_levels_match_brute_force(fanouts, tops, lens):
             assert np.array_equal(got[got >= 0], s), (b, g, l)
 
 
+SMALL_DEEP = gi.Workload("small-deep", gi.BF16, 2, 6, 2, 64, 4, 600, 5, 8,
+                         plant="align", plant_count=3)
+
+
+@pytest.mark.parametrize("wl", [SMALL_DEEP, SMALL_L], ids=["600-gists", "150-gists-empty-top"])
+@pytest.mark.parametrize("lens", ["full", "ragged"])
+def test_eight_levels_match_brute_force(wl, lens):
+    """Eight meta levels of fanout 2 (the most the library's entry point
+    takes) against the numpy brute force; above 150 gists the eighth level is
+    empty, so every level-7 entry lies past its last complete group."""
+    tops = (6, 5, 4, 3, 3, 2, 2, 1)
+    inp = gi.make_inputs(wl, 81, seq_lens=None if lens == "full" else _ragged(wl, 5))
+    lv = with_levels(inp, (2,) * 8, tops, 15)
+    out, sels, _ = run_levels(inp, lv)
+    ref, rsel = np_mgsa(inp, lv, wl.top_k)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+    for (b, g), kept in rsel.items():
+        for l, s in enumerate(kept):
+            got = sels[l][b, g]
+            assert np.array_equal(got[got >= 0], s), (b, g, l)
+
+
 def test_levels_f32_and_planted_ancestors():
     """fp32 storage; the planted chunks' ancestors are kept at every level and
     the planted chunks themselves selected."""
