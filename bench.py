@@ -500,8 +500,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(wl.name) if single and flags == 0 and not wl.hgsa
-                     else None,
+                     # counters were taken for the default key and set of each single-launch
+                     # workload (flat and two-level), not for the variants
+                     "traffic": measured_traffic(wl.name)
+                     if single and flags == 0 and args.top_p <= 0.0 and hier is None else None,
                      "alg_bytes_per_launch": nbytes, "kernel_hash": kernel_hash(),
                      "copy_peak_gbps": peak_copy, "frac_of_copy_peak": achieved / peak_copy},
     }
